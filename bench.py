@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the LLM.int8() decomposed int8 matmul on one MI355X.
+
+A step is one forward of the whole per-layer path on one batch of synthetic
+input already resident in HBM: outlier-column detection, row-wise
+quantisation with the outlier gather, and the int8 MFMA product with the
+fused dequantise + fp16 outlier epilogue. Weights are converted once at load
+time (timed separately, not part of a step).
+
+Prints ONE JSON line. `value` is the effective throughput 2*s*h*o / t_step
+(TOPS) on the OPT-6.7B-style FFN expansion prefill layer
+(X [2048, 4096], W [4096, 16384], 6 outlier columns in 75% of rows).
+`roofline` is the product kernel against the MI355X dense int8 MFMA peak;
+`decode` reports the weight-streaming GB/s of the 175B-style FFN expansion
+decode layer (X [8, 12288], W [12288, 49152]) against 8 TB/s HBM;
+`cpu_baseline` times the CPU oracle on host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective int8-mixed matmul TOPS (prefill) + weight GB/s (decode), % roofline"
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+FP16_PEAK_TFLOPS = 2500.0    # dense fp16 MFMA
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def run_prefill(i8, torch, w, steps, warmup, dev):
+    from workloads import make_inputs
+    inp = make_inputs(w)
+    X = torch.from_numpy(inp["X"]).to(dev)
+    W = torch.from_numpy(inp["W"]).to(dev)
+    s, h, o = w.s, w.h, w.o
+    torch.cuda.synchronize()
+
+    # load-time conversion (timed on its own)
+    Wq_t, c_w = i8.quantize_colwise_weights(W)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(3):
+        i8.quantize_colwise_weights(W, Wq_t, c_w)
+    e1.record()
+    torch.cuda.synchronize()
+    conv_ms = e0.elapsed_time(e1) / 3
+
+    ws = i8.forward_workspace(s, h, dev)
+    v = i8.forward_workspace_views(ws, s, h)
+    C = torch.empty((s, o), dtype=torch.float16, device=dev)
+
+    def step(ev_a=None, ev_b=None):
+        # exactly the launches of i8mm_forward, split so that the product
+        # kernel can be bracketed by events on the same stream
+        i8.detect_outlier_cols(X, w.alpha, v["mask"], v["idx"], v["n_out"])
+        i8.quantize_rowwise(X, v["mask"], v["idx"], v["n_out"], v["Xq"], v["c_x"], v["X_O"])
+        if ev_a is not None:
+            ev_a.record()
+        i8.int8_mixed_matmul(v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq_t, c_w, W, C)
+        if ev_b is not None:
+            ev_b.record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    gemm_ev = [_events(torch) for _ in range(steps)]
+    t0, t1 = _events(torch)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for k in range(steps):
+        step(*gemm_ev[k])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / steps
+    gemm_ms = sum(a.elapsed_time(b) for a, b in gemm_ev) / steps
+
+    # a plain forward (one C-ABI call per step) timed the same way, for reference
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(steps):
+        i8.forward(X, Wq_t, c_w, W, w.alpha, workspace=ws, C=C)
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / steps
+    n_out = int(v["n_out"].cpu()[0])
+    return dict(step_ms=step_ms, gemm_ms=gemm_ms, fwd_ms=fwd_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out,
+                inputs=inp)
+
+
+def run_decode(i8, torch, w, steps, warmup, dev):
+    from workloads import make_inputs
+    inp = make_inputs(w)
+    X = torch.from_numpy(inp["X"]).to(dev)
+    W = torch.from_numpy(inp["W"]).to(dev)
+    del inp
+    s, h, o = w.s, w.h, w.o
+    Wq_t, c_w = i8.quantize_colwise_weights(W)
+    ws = i8.forward_workspace(s, h, dev)
+    v = i8.forward_workspace_views(ws, s, h)
+    C = torch.empty((s, o), dtype=torch.float16, device=dev)
+    for _ in range(warmup):
+        i8.forward(X, Wq_t, c_w, W, w.alpha, workspace=ws, C=C)
+    torch.cuda.synchronize()
+    gemm_ev = [_events(torch) for _ in range(steps)]
+    t0, t1 = _events(torch)
+    t0.record()
+    for k in range(steps):
+        i8.detect_outlier_cols(X, w.alpha, v["mask"], v["idx"], v["n_out"])
+        i8.quantize_rowwise(X, v["mask"], v["idx"], v["n_out"], v["Xq"], v["c_x"], v["X_O"])
+        gemm_ev[k][0].record()
+        i8.int8_mixed_matmul(v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq_t, c_w, W, C)
+        gemm_ev[k][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    gemm_ms = sum(a.elapsed_time(b) for a, b in gemm_ev) / steps
+    n_out = int(v["n_out"].cpu()[0])
+    weight_bytes = h * o + 2 * n_out * o + 4 * o
+    return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes)
+
+
+def cpu_baseline(w, inputs, budget_s):
+    """Time the CPU oracle (as it stands) on the same workload's inputs.
+
+    The sample is the first R rows of X against all of W, repeated; R and the
+    repetition count are chosen so that the timed work takes about budget_s.
+    """
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()
+                            if d.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing or unreadable
+        blas_threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    X, W = inputs["X"], inputs["W"]
+    Wq_t, c_w = oracle.quantize_colwise_weights(W)      # load time, not timed
+    rows = min(w.s, 256)
+    t = time.perf_counter()
+    oracle.forward(X[:rows], W, w.alpha, Wq_t=Wq_t, c_w=c_w)
+    probe = time.perf_counter() - t
+    per_row = probe / rows
+    rows = int(min(w.s, max(16, budget_s / per_row)))
+    reps = max(1, int(budget_s / (per_row * rows)))
+    t = time.perf_counter()
+    for _ in range(reps):
+        oracle.forward(X[:rows], W, w.alpha, Wq_t=Wq_t, c_w=c_w)
+    el = time.perf_counter() - t
+    tops = 2.0 * rows * w.h * w.o * reps / el / 1e12
+    return {
+        "value": round(tops, 6),
+        "unit": "TOPS",
+        "cores": blas_threads,
+        "kind": "oracle",
+        "sample": (f"oracle.forward on the first {rows} of {w.s} rows of X against the full W "
+                   f"[{w.h}x{w.o}], {reps} rep(s), {el:.1f} s; numpy float64 BLAS with "
+                   f"{blas_threads} thread(s), elementwise steps single-threaded"),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="opt67b_ffn1_prefill")
+    ap.add_argument("--decode-workload", default="b175_ffn1_decode")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic of the product kernel measured with rocprofv3 counters")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(no sharding, no collectives). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import int8_quantized_matmul_amd as i8
+    from workloads import get_config
+
+    dev = torch.device("cuda:0")
+    w = get_config(args.workload)
+    _log(f"[bench] prefill workload {w.name}: s={w.s} h={w.h} o={w.o}")
+    pre = run_prefill(i8, torch, w, args.steps, args.warmup, dev)
+    s, h, o, n_out = w.s, w.h, w.o, pre["n_out"]
+    tops = 2.0 * s * h * o / (pre["step_ms"] * 1e-3) / 1e12
+    alg_ops = 2.0 * s * (h - n_out) * o                  # int8 ops one product launch performs
+    gemm_tops = alg_ops / (pre["gemm_ms"] * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            with open(args.traffic) as f:
+                tr = json.load(f)
+            if tr.get("workload") == w.name and tr.get("kernel_source_sha") == _kernel_sha():
+                traffic = tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "s": s, "h": h, "o": o, "n_outliers": n_out,
+                   "outlier_row_frac": w.row_frac, "alpha": w.alpha, "parallelism": "none"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k_gemm_prefill (int8 MFMA + fused dequant/outlier epilogue)",
+            "achieved": round(gemm_tops, 3),
+            "peak": INT8_PEAK_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+            "traffic": traffic,
+            "algorithmic_ops_per_launch": alg_ops,
+            "avg_launch_ms": round(pre["gemm_ms"], 5),
+        },
+        "pct_int8_peak_effective": round(100 * tops / INT8_PEAK_TOPS, 2),
+        "forward_single_call_ms": round(pre["fwd_ms"], 5),
+        "weight_conversion": {"ms": round(pre["conv_ms"], 4),
+                              "GB_per_s": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1)},
+    }
+    inputs = pre.pop("inputs")
+
+    if not args.no_decode:
+        wd = get_config(args.decode_workload)
+        _log(f"[bench] decode workload {wd.name}: s={wd.s} h={wd.h} o={wd.o}")
+        dec = run_decode(i8, torch, wd, args.steps, args.warmup, dev)
+        gbs = dec["weight_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
+        gbs_gemm = dec["weight_bytes"] / (dec["gemm_ms"] * 1e-3) / 1e9
+        out["decode"] = {
+            "workload": wd.name, "s": wd.s, "h": wd.h, "o": wd.o, "n_outliers": dec["n_out"],
+            "ms_per_step": round(dec["step_ms"], 5),
+            "weight_GB_per_s": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "product_kernel_ms": round(dec["gemm_ms"], 5),
+            "product_kernel_weight_GB_per_s": round(gbs_gemm, 1),
+        }
+
+    if not args.no_cpu_baseline:
+        _log("[bench] timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _kernel_sha():
+    import hashlib
+    hsh = hashlib.sha256()
+    src = os.path.join(ROOT, "int8_quantized_matmul_amd", "csrc", "gemm_kernels.hip")
+    with open(src, "rb") as f:
+        hsh.update(f.read())
+    return hsh.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

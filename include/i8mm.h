@@ -1,0 +1,214 @@
+/*
+ * i8mm.h - C ABI of the LLM.int8() mixed-precision decomposed int8 matmul
+ *          for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, for a transformer linear layer C = X W with
+ * X fp16 [s, h] and W fp16 [h, o]:
+ *   1. the outlier feature columns O = { j : max_i |X_ij| >= alpha };
+ *   2. row-wise absmax int8 quantisation of X over the columns not in O;
+ *   3. (once, at load time) column-wise absmax int8 quantisation of W;
+ *   4. C = fp16( C_i32 / (c_x (x) c_w) + X[:, O] W[O, :] ), where C_i32 is the
+ *      exact int8 x int8 -> int32 product over the columns not in O.
+ *
+ * Page tags used in the citations below:
+ *   [DIGEST] "LLM.int8(): 8-bit Matrix Multiplication for Transformers at
+ *            Scale" (paper-graph-ui.vercel.app digest of arXiv 2208.07339)
+ *   [TM]     transformer-math LLM.int8() tutorial (aicassindra.com)
+ *   [PY]     "LLM.int8() 完全拆解：系统离群值的涌现与混合精度分解"
+ *            (pinghaoyang.com.cn)
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     owned by the caller; the library never frees or retains them.
+ *   - fp16 values are passed as their IEEE binary16 bit patterns (uint16_t).
+ *   - All matrices are row-major and dense (leading dimension = row length),
+ *     except X_O, whose row stride is the explicit argument ldo.
+ *   - Every pointer must be 16-byte aligned.
+ *   - Shape limits: s >= 1; h and o multiples of 64; h <= 133120 (so an
+ *     int32 accumulator cannot overflow: h * 127^2 < 2^31).
+ *   - Work is enqueued on `stream` (NULL = the default stream); calls return
+ *     without synchronising. Arguments are validated on the host before any
+ *     work is enqueued: an invalid call enqueues nothing. Faults of the
+ *     device work itself surface at the caller's next synchronisation.
+ *   - The library allocates no device memory and holds no per-call state;
+ *     concurrent calls on different streams are safe if their output buffers
+ *     do not overlap.
+ *   - Scales are fp32: c = fl32(127 / m) (IEEE division, round to nearest
+ *     even), c = 1 when m == 0. Quantisation is v = fl32(x * c) rounded half
+ *     away from zero, in [-127, 127].
+ */
+#ifndef I8MM_H
+#define I8MM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    I8MM_OK = 0,
+    I8MM_EINVAL = -1,   /* bad pointer, shape, alignment or argument value */
+    I8MM_EDEVICE = -2,  /* no HIP device, or the current device is not gfx950 */
+    I8MM_ELAUNCH = -3   /* a kernel launch was rejected by the runtime */
+} i8mm_status;
+
+/* Largest h accepted (int32 accumulator bound, rounded down to 64). */
+#define I8MM_MAX_H 133120
+
+/*
+ * Load-time weight conversion: W fp16 [h, o] -> Wq_t int8 [o, h] and c_w fp32 [o].
+ *
+ * [DIGEST] "The Full LLM.int8() Algorithm", Step 4, second and third
+ * bullets (c_w_j = 127 / max_i |W_ij|, W_i8 = round(W (.) c_w)), and "Why
+ * vector-wise rather than row-wise" (the column constants are computed once
+ * at load time); [PY] "第一件武器：向量级量化" (one scale per column of W).
+ * The max runs over all h rows of W, so the conversion does not depend on
+ * the per-forward outlier set.
+ *
+ * Wq_t is W_i8 TRANSPOSED: row j of Wq_t holds column j of W_i8, so the
+ * reduction dimension h is contiguous for both operands of the product.
+ * W: [h, o] fp16 (read). Wq_t: [o, h] int8 (written). c_w: [o] fp32 (written).
+ */
+i8mm_status i8mm_quantize_colwise_weights(const uint16_t* W, int64_t h, int64_t o,
+                                          int8_t* Wq_t, float* c_w, hipStream_t stream);
+
+/*
+ * Outlier-column detection: O = { j in [0, h) : max_i |X_ij| >= alpha }.
+ *
+ * [DIGEST] "The Full LLM.int8() Algorithm", Step 1; [DIGEST]
+ * "Mixed-Precision Decomposition", formal definition of O and "The outlier
+ * detection threshold" (alpha = 6.0); [PY] "第二件武器：混合精度分解".
+ * The comparison is done in fp32 on the exactly widened fp16 value.
+ *
+ * X: [s, h] fp16 (read).
+ * mask: [ceil(h/32)] uint32 (written): bit (j % 32) of word j / 32 is set iff j in O.
+ * idx: [h] int32 (written): the members of O in ascending order in idx[0 .. |O|);
+ *      entries from |O| on are unspecified.
+ * n_out: [1] int32 (written): |O|. Stays on the device (no host round trip).
+ * alpha: finite or +inf, >= 0 (alpha = +inf gives O = {}, pure vector-wise
+ *        int8; alpha = 0 puts every column in O).
+ */
+i8mm_status i8mm_detect_outlier_cols(const uint16_t* X, int64_t s, int64_t h, float alpha,
+                                     uint32_t* mask, int32_t* idx, int32_t* n_out,
+                                     hipStream_t stream);
+
+/*
+ * Row-wise absmax quantisation of the non-outlier columns, plus the gather
+ * of the outlier columns.
+ *
+ * [DIGEST] "The Full LLM.int8() Algorithm", Step 2 (split X into X^O and
+ * X^{not O}) and Step 4, first and third bullets (c_x_i = 127 / max over the
+ * non-outlier columns of row i; X_i8 = round(c_x (.) X^{not O}));
+ * [TM] "Absmax INT8 quantization from first principles" and "Vector-wise:
+ * a scale per row and per column".
+ *
+ * X: [s, h] fp16 (read). mask, idx, n_out: as written by
+ * i8mm_detect_outlier_cols (read on the device).
+ * Xq: [s, h] int8 (written): quantised X with the columns in O set to 0.
+ * c_x: [s] fp32 (written).
+ * X_O: [s, ldo] fp16 (written): X_O[i, k] = X[i, idx[k]] for k < |O|, and 0
+ *      for |O| <= k < round_up(|O|, 32); later entries are not touched.
+ * ldo: row stride of X_O in elements; must be >= round_up(h, 32) (|O| is
+ *      only known on the device, so room for |O| = h is required) and a
+ *      multiple of 8.
+ */
+i8mm_status i8mm_quantize_rowwise(const uint16_t* X, int64_t s, int64_t h,
+                                  const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
+                                  int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
+                                  hipStream_t stream);
+
+/*
+ * The decomposed product: C = fp16( C_i32 / (c_x (x) c_w) + X_O W[idx, :] ).
+ *
+ * [DIGEST] "Mixed-Precision Decomposition", formal definition (sum of the
+ * fp16 outlier outer products and S times the int8 product); [DIGEST] "The
+ * Full LLM.int8() Algorithm", Steps 3-5; [PY] "第二件武器：混合精度分解"
+ * (decomposition equation); [TM] "The mixed-precision decomposition".
+ *
+ * C_i32 = Xq Wq_t^T is exact (int8 MFMA, int32 accumulate). The dequantised
+ * value and the fp16 outlier product (fp16 MFMA, fp32 accumulate) are summed
+ * in fp32 and rounded once to fp16 (round to nearest even). S is never
+ * materialised. n_out is read on the device; only rows idx[0 .. n_out) of W
+ * are read.
+ *
+ * Xq: [s, h] int8; c_x: [s] fp32; X_O: [s, ldo] fp16 (ldo as above);
+ * idx, n_out: as from i8mm_detect_outlier_cols; Wq_t: [o, h] int8;
+ * c_w: [o] fp32; W: [h, o] fp16 (the original weights);
+ * C: [s, o] fp16 (written).
+ */
+i8mm_status i8mm_int8_mixed_matmul(const int8_t* Xq, const float* c_x,
+                                   const uint16_t* X_O, int64_t ldo,
+                                   const int32_t* idx, const int32_t* n_out,
+                                   const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                                   int64_t s, int64_t h, int64_t o, uint16_t* C,
+                                   hipStream_t stream);
+
+/*
+ * The 16-bit outlier product alone: C_O fp32 [s, o] = X_O W[idx, :].
+ *
+ * [DIGEST] "The Full LLM.int8() Algorithm", Step 3 (C^O = X^O_f16 W^O_f16);
+ * [PY] "第二件武器：混合精度分解" (an s x |O| by |O| x o skinny product).
+ * fp16 MFMA with fp32 accumulation; the same device routine that the fused
+ * epilogue of i8mm_int8_mixed_matmul uses. Arguments as above.
+ */
+i8mm_status i8mm_outlier_matmul(const uint16_t* X_O, int64_t ldo,
+                                const int32_t* idx, const int32_t* n_out,
+                                const uint16_t* W, int64_t s, int64_t h, int64_t o,
+                                float* C_O, hipStream_t stream);
+
+/*
+ * The int8 product alone: C_i32 int32 [s, o] = Xq Wq_t^T, exact.
+ *
+ * [DIGEST] "The Full LLM.int8() Algorithm", Step 4, fourth bullet (Int8
+ * matrix multiplication producing an Int32 accumulator). Runs the same
+ * main loop as i8mm_int8_mixed_matmul with a plain int32 store.
+ */
+i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq_t,
+                               int64_t s, int64_t h, int64_t o, int32_t* C_i32,
+                               hipStream_t stream);
+
+/*
+ * Bytes of device workspace that i8mm_forward needs for (s, h): mask, idx,
+ * n_out, Xq, c_x and X_O (ldo = round_up(h, 32)), each 256-byte aligned.
+ * Returns 0 for invalid shapes.
+ */
+size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h);
+
+/*
+ * The whole per-forward path for one linear layer ([DIGEST] "The Full
+ * LLM.int8() Algorithm", Steps 1-5): detect, quantise rows and gather,
+ * decomposed product. Weights must already be converted by
+ * i8mm_quantize_colwise_weights.
+ *
+ * workspace: caller-owned device buffer of i8mm_forward_workspace_bytes(s, h)
+ * bytes, 256-byte aligned; on return (after synchronisation) it holds the
+ * intermediates at the offsets given by i8mm_forward_workspace_layout.
+ * X: [s, h] fp16; Wq_t: [o, h] int8; c_w: [o] fp32; W: [h, o] fp16;
+ * C: [s, o] fp16 (written).
+ */
+i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                         const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                         void* workspace, uint16_t* C, hipStream_t stream);
+
+/*
+ * Byte offsets of the intermediates inside the forward workspace, in the
+ * order mask, idx, n_out, Xq, c_x, X_O (6 entries written to offsets[]),
+ * and the X_O row stride (elements) in *ldo. Returns I8MM_EINVAL for bad
+ * shapes or null pointers. Host-only; touches no device.
+ */
+i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[6], int64_t* ldo);
+
+/* Library version string (static storage). */
+const char* i8mm_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* i8mm_status_string(i8mm_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I8MM_H */

@@ -1,0 +1,244 @@
+"""LLM.int8() mixed-precision decomposed int8 matmul for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of libi8mm.so (include/i8mm.h). Each
+function checks tensor placement, dtype and shape, allocates outputs with
+torch on the tensors' device, and passes raw device pointers plus torch's
+current HIP stream to the library. Every step of the computation runs in the
+library's HIP kernels; there is no CPU or PyTorch fallback: without the
+built library the first call raises ImportError.
+
+Page tags: [DIGEST] "LLM.int8(): 8-bit Matrix Multiplication for Transformers
+at Scale" (paper-graph-ui digest), "The Full LLM.int8() Algorithm".
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _native
+
+__all__ = [
+    "quantize_colwise_weights",
+    "detect_outlier_cols",
+    "quantize_rowwise",
+    "int8_mixed_matmul",
+    "outlier_matmul",
+    "int8_gemm_i32",
+    "forward",
+    "forward_workspace",
+    "forward_workspace_views",
+    "x_o_stride",
+    "version",
+    "library_path",
+    "I8MMError",
+]
+
+
+class _LazyLib:
+    """Loads libi8mm.so on first use, so that the build module can be imported
+    before the library exists. Any call without the library raises ImportError."""
+
+    def __getattr__(self, name):
+        return getattr(_native.load(), name)
+
+
+_lib = _LazyLib()
+
+
+class I8MMError(RuntimeError):
+    """A libi8mm entry point returned an error status."""
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = _lib.i8mm_status_string(status).decode()
+        raise I8MMError(f"{what}: {msg} (status {status})")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+def x_o_stride(h: int) -> int:
+    """Row stride (elements) of the gathered outlier columns X_O: room for |O| = h."""
+    return (h + 31) // 32 * 32
+
+
+def version() -> str:
+    return _lib.i8mm_version().decode()
+
+
+def library_path() -> str:
+    return _native.loaded_path()
+
+
+def quantize_colwise_weights(W: torch.Tensor, Wq_t: Optional[torch.Tensor] = None,
+                             c_w: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Load-time conversion: W fp16 [h, o] -> (Wq_t int8 [o, h], c_w fp32 [o])."""
+    h, o = W.shape
+    if Wq_t is None:
+        Wq_t = torch.empty((o, h), dtype=torch.int8, device=W.device)
+    if c_w is None:
+        c_w = torch.empty((o,), dtype=torch.float32, device=W.device)
+    st = _lib.i8mm_quantize_colwise_weights(
+        _dev(W, "W", torch.float16), h, o, _dev(Wq_t, "Wq_t", torch.int8, (o, h)),
+        _dev(c_w, "c_w", torch.float32, (o,)), _stream(W))
+    _check(st, "quantize_colwise_weights")
+    return Wq_t, c_w
+
+
+def detect_outlier_cols(X: torch.Tensor, alpha: float = 6.0, mask: Optional[torch.Tensor] = None,
+                        idx: Optional[torch.Tensor] = None, n_out: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """O = {j : max_i |X_ij| >= alpha} as (mask int32 view of uint32 [ceil(h/32)],
+    idx int32 [h] (first |O| valid, ascending), n_out int32 [1]) on the device."""
+    s, h = X.shape
+    nw = (h + 31) // 32
+    dev = X.device
+    if mask is None:
+        mask = torch.empty((nw,), dtype=torch.int32, device=dev)
+    if idx is None:
+        idx = torch.empty((h,), dtype=torch.int32, device=dev)
+    if n_out is None:
+        n_out = torch.empty((1,), dtype=torch.int32, device=dev)
+    st = _lib.i8mm_detect_outlier_cols(
+        _dev(X, "X", torch.float16), s, h, float(alpha), _dev(mask, "mask", torch.int32, (nw,)),
+        _dev(idx, "idx", torch.int32, (h,)), _dev(n_out, "n_out", torch.int32, (1,)), _stream(X))
+    _check(st, "detect_outlier_cols")
+    return mask, idx, n_out
+
+
+def quantize_rowwise(X: torch.Tensor, mask: torch.Tensor, idx: torch.Tensor, n_out: torch.Tensor,
+                     Xq: Optional[torch.Tensor] = None, c_x: Optional[torch.Tensor] = None,
+                     X_O: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Row-wise absmax int8 over the non-outlier columns: (Xq int8 [s, h] with
+    O columns 0, c_x fp32 [s], X_O fp16 [s, x_o_stride(h)] gathered outliers)."""
+    s, h = X.shape
+    dev = X.device
+    ldo = x_o_stride(h) if X_O is None else X_O.shape[1]
+    if Xq is None:
+        Xq = torch.empty((s, h), dtype=torch.int8, device=dev)
+    if c_x is None:
+        c_x = torch.empty((s,), dtype=torch.float32, device=dev)
+    if X_O is None:
+        X_O = torch.empty((s, ldo), dtype=torch.float16, device=dev)
+    st = _lib.i8mm_quantize_rowwise(
+        _dev(X, "X", torch.float16), s, h, _dev(mask, "mask", torch.int32),
+        _dev(idx, "idx", torch.int32), _dev(n_out, "n_out", torch.int32, (1,)),
+        _dev(Xq, "Xq", torch.int8, (s, h)), _dev(c_x, "c_x", torch.float32, (s,)),
+        _dev(X_O, "X_O", torch.float16, (s, ldo)), ldo, _stream(X))
+    _check(st, "quantize_rowwise")
+    return Xq, c_x, X_O
+
+
+def int8_mixed_matmul(Xq: torch.Tensor, c_x: torch.Tensor, X_O: torch.Tensor, idx: torch.Tensor,
+                      n_out: torch.Tensor, Wq_t: torch.Tensor, c_w: torch.Tensor, W: torch.Tensor,
+                      C: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C fp16 [s, o] = fp16(C_i32 / (c_x ⊗ c_w) + X_O W[idx, :])."""
+    s, h = Xq.shape
+    o = Wq_t.shape[0]
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.float16, device=Xq.device)
+    st = _lib.i8mm_int8_mixed_matmul(
+        _dev(Xq, "Xq", torch.int8), _dev(c_x, "c_x", torch.float32, (s,)),
+        _dev(X_O, "X_O", torch.float16), X_O.shape[1], _dev(idx, "idx", torch.int32),
+        _dev(n_out, "n_out", torch.int32, (1,)), _dev(Wq_t, "Wq_t", torch.int8, (o, h)),
+        _dev(c_w, "c_w", torch.float32, (o,)), _dev(W, "W", torch.float16, (h, o)),
+        s, h, o, _dev(C, "C", torch.float16, (s, o)), _stream(Xq))
+    _check(st, "int8_mixed_matmul")
+    return C
+
+
+def outlier_matmul(X_O: torch.Tensor, idx: torch.Tensor, n_out: torch.Tensor, W: torch.Tensor,
+                   C_O: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C_O fp32 [s, o] = X_O W[idx, :] (the fp16 outlier product alone)."""
+    s, ldo = X_O.shape
+    h, o = W.shape
+    if C_O is None:
+        C_O = torch.empty((s, o), dtype=torch.float32, device=X_O.device)
+    st = _lib.i8mm_outlier_matmul(
+        _dev(X_O, "X_O", torch.float16), ldo, _dev(idx, "idx", torch.int32),
+        _dev(n_out, "n_out", torch.int32, (1,)), _dev(W, "W", torch.float16), s, h, o,
+        _dev(C_O, "C_O", torch.float32, (s, o)), _stream(X_O))
+    _check(st, "outlier_matmul")
+    return C_O
+
+
+def int8_gemm_i32(Xq: torch.Tensor, Wq_t: torch.Tensor, C: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C_i32 int32 [s, o] = Xq Wq_t^T exactly (same main loop as the mixed product)."""
+    s, h = Xq.shape
+    o = Wq_t.shape[0]
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.int32, device=Xq.device)
+    st = _lib.i8mm_int8_gemm_i32(
+        _dev(Xq, "Xq", torch.int8), _dev(Wq_t, "Wq_t", torch.int8, (o, h)), s, h, o,
+        _dev(C, "C", torch.int32, (s, o)), _stream(Xq))
+    _check(st, "int8_gemm_i32")
+    return C
+
+
+def forward_workspace(s: int, h: int, device) -> torch.Tensor:
+    """A device workspace (uint8) for forward()."""
+    n = _lib.i8mm_forward_workspace_bytes(s, h)
+    if n == 0:
+        raise I8MMError(f"invalid shape for the forward workspace: s={s}, h={h}")
+    return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def forward_workspace_views(workspace: torch.Tensor, s: int, h: int) -> Dict[str, torch.Tensor]:
+    """Typed views of the intermediates that forward() leaves in its workspace."""
+    offs = (ctypes.c_size_t * 6)()
+    ldo = ctypes.c_int64()
+    _check(_lib.i8mm_forward_workspace_layout(s, h, offs, ctypes.byref(ldo)), "forward_workspace_layout")
+    nw = (h + 31) // 32
+    l = ldo.value
+
+    def view(i, nbytes, dtype, shape):
+        return workspace[offs[i]:offs[i] + nbytes].view(dtype).view(shape)
+
+    return {
+        "mask": view(0, 4 * nw, torch.int32, (nw,)),
+        "idx": view(1, 4 * h, torch.int32, (h,)),
+        "n_out": view(2, 4, torch.int32, (1,)),
+        "Xq": view(3, s * h, torch.int8, (s, h)),
+        "c_x": view(4, 4 * s, torch.float32, (s,)),
+        "X_O": view(5, 2 * s * l, torch.float16, (s, l)),
+    }
+
+
+def forward(X: torch.Tensor, Wq_t: torch.Tensor, c_w: torch.Tensor, W: torch.Tensor,
+            alpha: float = 6.0, workspace: Optional[torch.Tensor] = None,
+            C: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole per-forward path: detect -> quantise rows -> decomposed product."""
+    s, h = X.shape
+    o = Wq_t.shape[0]
+    if workspace is None:
+        workspace = forward_workspace(s, h, X.device)
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.float16, device=X.device)
+    need = _lib.i8mm_forward_workspace_bytes(s, h)
+    if workspace.numel() < need or workspace.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
+    st = _lib.i8mm_forward(
+        _dev(X, "X", torch.float16), s, h, o, float(alpha), _dev(Wq_t, "Wq_t", torch.int8, (o, h)),
+        _dev(c_w, "c_w", torch.float32, (o,)), _dev(W, "W", torch.float16, (h, o)),
+        _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
+    _check(st, "forward")
+    return C

@@ -1,0 +1,207 @@
+// C-ABI layer of libi8mm: host-side validation, the device check and the
+// launch sequence of each entry point declared in include/i8mm.h.
+//
+// Page tags: [DIGEST] "LLM.int8(): 8-bit Matrix Multiplication for
+// Transformers at Scale" (paper-graph-ui digest), "The Full LLM.int8()
+// Algorithm" (Steps 1-5, composed by i8mm_forward).
+
+#include "../../include/i8mm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+bool valid_shape_sh(int64_t s, int64_t h) {
+    return s >= 1 && h >= 64 && h % 64 == 0 && h <= I8MM_MAX_H && s <= (int64_t(1) << 31) - 1;
+}
+
+bool valid_o(int64_t o) { return o >= 64 && o % 64 == 0 && o <= (int64_t(1) << 31) - 64; }
+
+i8mm_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return I8MM_EDEVICE;
+    }
+    if (dev < kMaxDevices) {
+        const int cached = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (cached == 1) return I8MM_OK;
+        if (cached == 2) return I8MM_EDEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return I8MM_EDEVICE;
+    }
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? I8MM_OK : I8MM_EDEVICE;
+}
+
+i8mm_status launched(hipError_t e) { return e == hipSuccess ? I8MM_OK : I8MM_ELAUNCH; }
+
+// Workspace of i8mm_forward: mask, idx, n_out, Xq, c_x, X_O, each 256-byte aligned.
+void forward_layout(int64_t s, int64_t h, size_t off[6], int64_t* ldo, size_t* total) {
+    const int64_t nw = (h + 31) / 32;
+    const int64_t l = round_up(h, 32);
+    size_t cur = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = cur;
+        cur += static_cast<size_t>(round_up(static_cast<int64_t>(bytes), 256));
+        return at;
+    };
+    off[0] = take(4 * nw);
+    off[1] = take(4 * h);
+    off[2] = take(4);
+    off[3] = take(static_cast<size_t>(s) * h);
+    off[4] = take(4 * s);
+    off[5] = take(2 * static_cast<size_t>(s) * l);
+    *ldo = l;
+    *total = cur;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* i8mm_version(void) { return "i8mm 0.1.0 (gfx950)"; }
+
+const char* i8mm_status_string(i8mm_status st) {
+    switch (st) {
+        case I8MM_OK: return "ok";
+        case I8MM_EINVAL: return "invalid argument";
+        case I8MM_EDEVICE: return "no gfx950 device";
+        case I8MM_ELAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+i8mm_status i8mm_quantize_colwise_weights(const uint16_t* W, int64_t h, int64_t o,
+                                          int8_t* Wq_t, float* c_w, hipStream_t stream) {
+    if (!W || !Wq_t || !c_w) return I8MM_EINVAL;
+    if (!valid_shape_sh(1, h) || !valid_o(o)) return I8MM_EINVAL;
+    if (!aligned16(W) || !aligned16(Wq_t) || !aligned16(c_w)) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_quantize_cols(W, h, o, Wq_t, c_w, stream));
+}
+
+i8mm_status i8mm_detect_outlier_cols(const uint16_t* X, int64_t s, int64_t h, float alpha,
+                                     uint32_t* mask, int32_t* idx, int32_t* n_out,
+                                     hipStream_t stream) {
+    if (!X || !mask || !idx || !n_out) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h)) return I8MM_EINVAL;
+    if (std::isnan(alpha) || alpha < 0.0f) return I8MM_EINVAL;
+    if (!aligned16(X) || !aligned16(mask) || !aligned16(idx) || !aligned16(n_out)) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_detect(X, s, h, alpha, mask, idx, n_out, stream));
+}
+
+i8mm_status i8mm_quantize_rowwise(const uint16_t* X, int64_t s, int64_t h,
+                                  const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
+                                  int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
+                                  hipStream_t stream) {
+    if (!X || !mask || !idx || !n_out || !Xq || !c_x || !X_O) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h)) return I8MM_EINVAL;
+    if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
+    if (!aligned16(X) || !aligned16(mask) || !aligned16(idx) || !aligned16(n_out) || !aligned16(Xq) ||
+        !aligned16(c_x) || !aligned16(X_O))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_quantize_rows(X, s, h, mask, idx, n_out, Xq, c_x, X_O, ldo, stream));
+}
+
+i8mm_status i8mm_int8_mixed_matmul(const int8_t* Xq, const float* c_x, const uint16_t* X_O, int64_t ldo,
+                                   const int32_t* idx, const int32_t* n_out,
+                                   const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                                   int64_t s, int64_t h, int64_t o, uint16_t* C, hipStream_t stream) {
+    if (!Xq || !c_x || !X_O || !idx || !n_out || !Wq_t || !c_w || !W || !C) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h) || !valid_o(o)) return I8MM_EINVAL;
+    if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
+    if (!aligned16(Xq) || !aligned16(c_x) || !aligned16(X_O) || !aligned16(idx) || !aligned16(n_out) ||
+        !aligned16(Wq_t) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W,
+                                           s, h, o, C, stream));
+}
+
+i8mm_status i8mm_outlier_matmul(const uint16_t* X_O, int64_t ldo, const int32_t* idx, const int32_t* n_out,
+                                const uint16_t* W, int64_t s, int64_t h, int64_t o, float* C_O,
+                                hipStream_t stream) {
+    if (!X_O || !idx || !n_out || !W || !C_O) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h) || !valid_o(o)) return I8MM_EINVAL;
+    if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
+    if (!aligned16(X_O) || !aligned16(idx) || !aligned16(n_out) || !aligned16(W) || !aligned16(C_O))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_outlier_matmul(X_O, ldo, idx, n_out, W, s, o, C_O, stream));
+}
+
+i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq_t, int64_t s, int64_t h, int64_t o,
+                               int32_t* C_i32, hipStream_t stream) {
+    if (!Xq || !Wq_t || !C_i32) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h) || !valid_o(o)) return I8MM_EINVAL;
+    if (!aligned16(Xq) || !aligned16(Wq_t) || !aligned16(C_i32)) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::Int32, Xq, nullptr, nullptr, 0, nullptr, nullptr, Wq_t,
+                                           nullptr, nullptr, s, h, o, C_i32, stream));
+}
+
+size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h) {
+    if (!valid_shape_sh(s, h)) return 0;
+    size_t off[6], total;
+    int64_t ldo;
+    forward_layout(s, h, off, &ldo, &total);
+    return total;
+}
+
+i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[6], int64_t* ldo) {
+    if (!offsets || !ldo || !valid_shape_sh(s, h)) return I8MM_EINVAL;
+    size_t total;
+    forward_layout(s, h, offsets, ldo, &total);
+    return I8MM_OK;
+}
+
+i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                         const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                         void* workspace, uint16_t* C, hipStream_t stream) {
+    if (!X || !Wq_t || !c_w || !W || !workspace || !C) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h) || !valid_o(o)) return I8MM_EINVAL;
+    if (std::isnan(alpha) || alpha < 0.0f) return I8MM_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
+    if (!aligned16(X) || !aligned16(Wq_t) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    size_t off[6], total;
+    int64_t ldo;
+    forward_layout(s, h, off, &ldo, &total);
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* mask = reinterpret_cast<uint32_t*>(ws + off[0]);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + off[1]);
+    int32_t* n_out = reinterpret_cast<int32_t*>(ws + off[2]);
+    int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[3]);
+    float* c_x = reinterpret_cast<float*>(ws + off[4]);
+    uint16_t* X_O = reinterpret_cast<uint16_t*>(ws + off[5]);
+    hipError_t e = i8mm::launch_detect(X, s, h, alpha, mask, idx, n_out, stream);
+    if (e != hipSuccess) return I8MM_ELAUNCH;
+    e = i8mm::launch_quantize_rows(X, s, h, mask, idx, n_out, Xq, c_x, X_O, ldo, stream);
+    if (e != hipSuccess) return I8MM_ELAUNCH;
+    e = i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W, s, h, o, C,
+                               stream);
+    return launched(e);
+}
+
+}  // extern "C"

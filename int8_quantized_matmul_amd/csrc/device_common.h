@@ -1,0 +1,55 @@
+// Device-side types and helpers shared by the gfx950 kernels of libi8mm.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8mm {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+    // v_cvt_f16_f32 rounds to nearest even in the default mode.
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// fl32(127 / m) with an IEEE correctly rounded division; 1 when m == 0.
+__device__ __forceinline__ float absmax_scale(float m) {
+    return m > 0.0f ? __fdiv_rn(127.0f, m) : 1.0f;
+}
+
+// One fp32 multiply, then round half away from zero, clamped to [-127, 127].
+__device__ __forceinline__ int quantize_one(float x, float c) {
+    float v = __fmul_rn(x, c);
+    float r = roundf(v);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return static_cast<int>(r);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int t = __shfl_up(v, off, kWave);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+}  // namespace i8mm

@@ -1,0 +1,36 @@
+// Host-side launchers of the gfx950 kernels. Arguments are validated by the
+// C-ABI layer (api.cpp) before any of these is called; each launcher only
+// picks a grid and enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace i8mm {
+
+hipError_t launch_detect(const uint16_t* X, int64_t s, int64_t h, float alpha,
+                         uint32_t* mask, int32_t* idx, int32_t* n_out, hipStream_t stream);
+
+hipError_t launch_quantize_rows(const uint16_t* X, int64_t s, int64_t h,
+                                const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
+                                int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
+                                hipStream_t stream);
+
+hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
+                                int8_t* Wq_t, float* c_w, hipStream_t stream);
+
+// mode: product variant of the shared int8 main loop.
+enum class GemmOut { Mixed = 0, Int32 = 1 };
+
+hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
+                            const uint16_t* X_O, int64_t ldo,
+                            const int32_t* idx, const int32_t* n_out,
+                            const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                            int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream);
+
+hipError_t launch_outlier_matmul(const uint16_t* X_O, int64_t ldo,
+                                 const int32_t* idx, const int32_t* n_out,
+                                 const uint16_t* W, int64_t s, int64_t o,
+                                 float* C_O, hipStream_t stream);
+
+}  // namespace i8mm

@@ -1,0 +1,101 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments on the host before touching any device (runs without a GPU)."""
+
+import ctypes
+import os
+
+import pytest
+
+from int8_quantized_matmul_amd import _native
+
+
+def _lib():
+    if not os.path.exists(_native.LIB_PATH):
+        from int8_quantized_matmul_amd.build import build
+        build()
+    return _native.load()
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    names = _native.header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(_native._SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings():
+    lib = _lib()
+    assert b"gfx950" in lib.i8mm_version()
+    assert lib.i8mm_status_string(0) == b"ok"
+    assert lib.i8mm_status_string(-1) == b"invalid argument"
+    assert lib.i8mm_status_string(-2) == b"no gfx950 device"
+
+
+P = ctypes.c_void_p(1 << 20)          # a 16-byte aligned non-null stand-in (never dereferenced)
+MIS = ctypes.c_void_p((1 << 20) + 4)  # misaligned
+
+
+@pytest.mark.parametrize("args", [
+    (None, 64, 64, P, P, None),       # null W
+    (P, 63, 64, P, P, None),          # h not a multiple of 64
+    (P, 64, 96, P, P, None),          # o not a multiple of 64
+    (P, 133184, 64, P, P, None),      # h above the int32 bound
+    (MIS, 64, 64, P, P, None),        # misaligned
+])
+def test_quantize_colwise_weights_rejects(args):
+    assert _lib().i8mm_quantize_colwise_weights(*args) == -1
+
+
+@pytest.mark.parametrize("s,h,alpha", [(0, 64, 6.0), (4, 0, 6.0), (4, 100, 6.0), (4, 64, float("nan")),
+                                       (4, 64, -1.0)])
+def test_detect_rejects(s, h, alpha):
+    assert _lib().i8mm_detect_outlier_cols(P, s, h, alpha, P, P, P, None) == -1
+
+
+def test_quantize_rowwise_rejects_small_ldo():
+    lib = _lib()
+    assert lib.i8mm_quantize_rowwise(P, 4, 128, P, P, P, P, P, P, 96, None) == -1   # ldo < h
+    assert lib.i8mm_quantize_rowwise(P, 4, 128, P, P, P, P, P, P, 132, None) == -1  # ldo % 8
+    assert lib.i8mm_quantize_rowwise(P, 4, 128, P, P, None, P, P, P, 128, None) == -1
+
+
+def test_mixed_matmul_and_gemm_reject():
+    lib = _lib()
+    assert lib.i8mm_int8_mixed_matmul(P, P, P, 64, P, P, P, P, P, 4, 64, 64, None, None) == -1
+    assert lib.i8mm_int8_mixed_matmul(P, P, P, 32, P, P, P, P, P, 4, 64, 64, P, None) == -1
+    assert lib.i8mm_int8_gemm_i32(P, P, 4, 64, 65, P, None) == -1
+    assert lib.i8mm_outlier_matmul(P, 64, P, P, P, 4, 64, 64, MIS, None) == -1
+
+
+def test_forward_rejects_unaligned_workspace():
+    lib = _lib()
+    ws = ctypes.c_void_p((1 << 20) + 16)
+    assert lib.i8mm_forward(P, 4, 64, 64, 6.0, P, P, P, ws, P, None) == -1
+
+
+def test_forward_workspace_layout():
+    lib = _lib()
+    for s, h in [(1, 64), (16, 256), (2048, 4096), (4096, 12288), (3, 133120)]:
+        total = lib.i8mm_forward_workspace_bytes(s, h)
+        offs = (ctypes.c_size_t * 6)()
+        ldo = ctypes.c_int64()
+        assert lib.i8mm_forward_workspace_layout(s, h, offs, ctypes.byref(ldo)) == 0
+        assert ldo.value == (h + 31) // 32 * 32
+        sizes = [4 * ((h + 31) // 32), 4 * h, 4, s * h, 4 * s, 2 * s * ldo.value]
+        for i in range(6):
+            assert offs[i] % 256 == 0
+            end = offs[i] + sizes[i]
+            assert end <= (offs[i + 1] if i < 5 else total)
+    assert lib.i8mm_forward_workspace_bytes(0, 64) == 0
+    assert lib.i8mm_forward_workspace_bytes(4, 96) == 0
+
+
+def test_valid_call_without_gpu_reports_no_device():
+    """With valid arguments the call reaches the device check; on a machine
+    with no GPU that is I8MM_EDEVICE (nothing is enqueued)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert _lib().i8mm_int8_gemm_i32(P, P, 1, 64, 64, P, None) == -2

@@ -1,0 +1,165 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle on seeded
+inputs small enough for the oracle to finish in seconds, spanning several
+tiles and ragged tails of both main loops (s <= 16 weight streaming, s > 16
+LDS-tiled), plus the method's degenerate cases.
+
+Bars: bit-exact for the outlier set, int8 codes, fp32 scales, gathered
+outlier columns and int32 accumulators; max |C - C_ref| <= 2e-3 ||C_ref||_inf
+for the fp16 output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import int8_quantized_matmul_amd as i8
+import oracle
+from gpu_util import DEV, H, T, check_C, check_detect, check_rows, round_up, say
+from workloads import get_config, make_inputs, random_case
+
+pytestmark = pytest.mark.gpu
+
+# (seed, s, h, o, n_outliers, row_frac): ragged s, o tails vs the 256 tiles,
+# h % 128 == 64 K tails, decode (s <= 16) and prefill main loops.
+SHAPES = [
+    (0, 1, 64, 64, 0, 0.0),
+    (1, 5, 192, 128, 2, 1.0),
+    (2, 16, 256, 512, 2, 0.3),
+    (3, 17, 192, 320, 3, 0.5),
+    (4, 64, 512, 1024, 7, 0.75),
+    (5, 300, 640, 576, 5, 0.06),
+    (6, 513, 384, 768, 40, 0.28),
+    (7, 8, 1024, 1024, 64, 1.0),
+    (8, 257, 1152, 832, 1, 1.0),
+]
+
+
+def _run_all(X, W, alpha):
+    Xd, Wd = T(X), T(W)
+    say(f"  launch: detect/quantize/gemm s={X.shape[0]} h={X.shape[1]} o={W.shape[1]} alpha={alpha}")
+    mask, idx, n_out = i8.detect_outlier_cols(Xd, alpha)
+    Xq, c_x, X_O = i8.quantize_rowwise(Xd, mask, idx, n_out)
+    Wq_t, c_w = i8.quantize_colwise_weights(Wd)
+    C = i8.int8_mixed_matmul(Xq, c_x, X_O, idx, n_out, Wq_t, c_w, Wd)
+    Ci = i8.int8_gemm_i32(Xq, Wq_t)
+    CO = i8.outlier_matmul(X_O, idx, n_out, Wd)
+    torch.cuda.synchronize()
+    return dict(mask=mask, idx=idx, n_out=n_out, Xq=Xq, c_x=c_x, X_O=X_O, Wq_t=Wq_t, c_w=c_w, C=C, Ci=Ci, CO=CO)
+
+
+def _check_all(X, W, alpha, g):
+    idx_r = check_detect(X, alpha, g["mask"], g["idx"], g["n_out"])
+    Xq_r, cx_r, XO_r = check_rows(X, idx_r, g["Xq"], g["c_x"], g["X_O"])
+    Wq_r, cw_r = oracle.quantize_colwise_weights(W)
+    assert np.array_equal(H(g["Wq_t"]), Wq_r), "Wq_t differs"
+    assert np.array_equal(H(g["c_w"]).view(np.uint32), cw_r.view(np.uint32)), "c_w differs"
+    Ci_r = oracle.int8_matmul_i32(Xq_r, Wq_r)
+    assert np.array_equal(H(g["Ci"]), Ci_r), "C_i32 differs"
+    CO_r = oracle.outlier_matmul(XO_r, W, idx_r)
+    CO = H(g["CO"]).astype(np.float64)
+    scale = np.abs(XO_r.astype(np.float64)) @ np.abs(W[idx_r].astype(np.float64)) if idx_r.size else 0.0
+    assert (np.abs(CO - CO_r) <= 1e-5 * scale + 1e-30).all(), "outlier product differs"
+    C_r = oracle.int8_mixed_matmul(Xq_r, cx_r, XO_r, idx_r, Wq_r, cw_r, W)
+    return check_C(g["C"], C_r)
+
+
+@pytest.mark.parametrize("seed,s,h,o,nout,frac", SHAPES, ids=[f"s{c[1]}h{c[2]}o{c[3]}n{c[4]}" for c in SHAPES])
+def test_all_entry_points_match_oracle(seed, s, h, o, nout, frac):
+    inp = random_case(seed, s, h, o, nout, row_frac=frac)
+    X, W = inp["X"], inp["W"]
+    if nout:
+        X[0, int(inp["planted"][0])] = np.float16(6.0)   # an element exactly at alpha
+    g = _run_all(X, W, 6.0)
+    rel = _check_all(X, W, 6.0, g)
+    say(f"  max rel err {rel:.2e}")
+
+
+def test_tiny_config():
+    w = get_config("tiny")
+    inp = make_inputs(w)
+    g = _run_all(inp["X"], inp["W"], w.alpha)
+    assert int(H(g["n_out"])[0]) == 2
+    _check_all(inp["X"], inp["W"], w.alpha, g)
+
+
+@pytest.mark.parametrize("s", [12, 40])
+def test_alpha_zero_every_column_is_outlier(s):
+    """alpha = 0: O = all columns, Xq == 0, C == fp16(X W) from the fp16 MFMA path."""
+    inp = random_case(30 + s, s, 128, 192, 0)
+    X, W = inp["X"], inp["W"]
+    g = _run_all(X, W, 0.0)
+    assert int(H(g["n_out"])[0]) == 128
+    assert not H(g["Xq"]).any()
+    _check_all(X, W, 0.0, g)
+    ref = (X.astype(np.float64) @ W.astype(np.float64)).astype(np.float16)
+    check_C(g["C"], ref)
+
+
+@pytest.mark.parametrize("s", [4, 33])
+def test_alpha_inf_is_pure_vectorwise(s):
+    inp = random_case(40 + s, s, 256, 256, 3)
+    g = _run_all(inp["X"], inp["W"], float("inf"))
+    assert int(H(g["n_out"])[0]) == 0
+    _check_all(inp["X"], inp["W"], float("inf"), g)
+
+
+@pytest.mark.parametrize("s", [3, 20])
+def test_zero_rows_and_zero_input(s):
+    inp = random_case(50 + s, s, 128, 128, 1, row_frac=0.5)
+    X = inp["X"]
+    X[1, :] = 0                      # an all-zero row
+    X[2, :] = 0
+    X[2, int(inp["planted"][0])] = 9.0   # a row whose only non-zero is an outlier
+    g = _run_all(X, inp["W"], 6.0)
+    _check_all(X, inp["W"], 6.0, g)
+    Z = np.zeros_like(X)
+    g = _run_all(Z, inp["W"], 6.0)
+    assert not H(g["C"]).view(np.uint16).any()
+    assert (H(g["c_x"]) == 1.0).all()
+
+
+@pytest.mark.parametrize("s", [2, 17])
+def test_max_h_int32_accumulator_bound(s):
+    """h = 133120 (largest accepted): all codes 127 give C_i32 = h * 127^2,
+    just below 2^31, exactly (C = h / 4 stays finite in fp16)."""
+    h, o = 133120, 64
+    X = np.ones((s, h), np.float16)
+    W = np.full((h, o), 0.25, np.float16)
+    Xd, Wd = T(X), T(W)
+    say(f"  launch: max-h s={s}")
+    mask, idx, n_out = i8.detect_outlier_cols(Xd, 6.0)
+    Xq, c_x, X_O = i8.quantize_rowwise(Xd, mask, idx, n_out)
+    Wq_t, c_w = i8.quantize_colwise_weights(Wd)
+    Ci = i8.int8_gemm_i32(Xq, Wq_t)
+    C = i8.int8_mixed_matmul(Xq, c_x, X_O, idx, n_out, Wq_t, c_w, Wd)
+    torch.cuda.synchronize()
+    assert int(H(n_out)[0]) == 0
+    assert (H(Ci) == h * 127 * 127).all()
+    assert h * 127 * 127 < 2 ** 31
+    check_C(C, (X.astype(np.float64) @ W.astype(np.float64)).astype(np.float16))
+
+
+def test_forward_matches_separate_calls_and_is_deterministic():
+    inp = random_case(60, 70, 768, 640, 6, row_frac=0.75)
+    X, W = inp["X"], inp["W"]
+    Xd, Wd = T(X), T(W)
+    Wq_t, c_w = i8.quantize_colwise_weights(Wd)
+    ws = i8.forward_workspace(70, 768, DEV)
+    C1 = i8.forward(Xd, Wq_t, c_w, Wd, 6.0, workspace=ws)
+    v = {k: t.clone() for k, t in i8.forward_workspace_views(ws, 70, 768).items()}
+    C2 = i8.forward(Xd, Wq_t, c_w, Wd, 6.0, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+    g = _run_all(X, W, 6.0)
+    assert torch.equal(g["C"], C1)
+    n = int(H(v["n_out"])[0])
+    assert torch.equal(v["idx"][:n], g["idx"][:n]) and torch.equal(v["mask"], g["mask"])
+    assert torch.equal(v["Xq"], g["Xq"]) and torch.equal(v["c_x"], g["c_x"])
+
+
+def test_bad_arguments_raise():
+    X = torch.zeros((4, 96), dtype=torch.float16, device=DEV)
+    with pytest.raises(i8.I8MMError):
+        i8.detect_outlier_cols(X)
+    with pytest.raises(ValueError):
+        i8.detect_outlier_cols(torch.zeros((4, 64), dtype=torch.float32, device=DEV))
