@@ -189,6 +189,9 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic of the product kernel measured with rocprofv3 counters")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this many MiB (5 times) and exit; its "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -201,6 +204,15 @@ def main(argv=None):
     from workloads import get_config
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.bitwise_not(src, out=dst)   # elementwise: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+        return 0
     w = get_config(args.workload)
     _log(f"[bench] prefill workload {w.name}: s={w.s} h={w.h} o={w.o}")
     pre = run_prefill(i8, torch, w, args.steps, args.warmup, dev)

@@ -25,7 +25,9 @@
  *     except X_O, whose row stride is the explicit argument ldo.
  *   - Every pointer must be 16-byte aligned.
  *   - Shape limits: s >= 1; h and o multiples of 64; h <= 133120 (so an
- *     int32 accumulator cannot overflow: h * 127^2 < 2^31).
+ *     int32 accumulator cannot overflow: h * 127^2 < 2^31); for the fused
+ *     product (i8mm_int8_mixed_matmul, i8mm_forward) also h * o < 2^31
+ *     (W is addressed with 32-bit byte offsets).
  *   - Work is enqueued on `stream` (NULL = the default stream); calls return
  *     without synchronising. Arguments are validated on the host before any
  *     work is enqueued: an invalid call enqueues nothing. Faults of the

@@ -30,6 +30,9 @@ bool valid_shape_sh(int64_t s, int64_t h) {
 
 bool valid_o(int64_t o) { return o >= 64 && o % 64 == 0 && o <= (int64_t(1) << 31) - 64; }
 
+// The fused product addresses W and X_O through 32-bit buffer offsets.
+bool valid_w_extent(int64_t h, int64_t o) { return h * o < (int64_t(1) << 31); }
+
 i8mm_status check_device() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
@@ -128,7 +131,7 @@ i8mm_status i8mm_int8_mixed_matmul(const int8_t* Xq, const float* c_x, const uin
                                    const int8_t* Wq_t, const float* c_w, const uint16_t* W,
                                    int64_t s, int64_t h, int64_t o, uint16_t* C, hipStream_t stream) {
     if (!Xq || !c_x || !X_O || !idx || !n_out || !Wq_t || !c_w || !W || !C) return I8MM_EINVAL;
-    if (!valid_shape_sh(s, h) || !valid_o(o)) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
     if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
     if (!aligned16(Xq) || !aligned16(c_x) || !aligned16(X_O) || !aligned16(idx) || !aligned16(n_out) ||
         !aligned16(Wq_t) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
@@ -179,7 +182,7 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
                          const int8_t* Wq_t, const float* c_w, const uint16_t* W,
                          void* workspace, uint16_t* C, hipStream_t stream) {
     if (!X || !Wq_t || !c_w || !W || !workspace || !C) return I8MM_EINVAL;
-    if (!valid_shape_sh(s, h) || !valid_o(o)) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
     if (std::isnan(alpha) || alpha < 0.0f) return I8MM_EINVAL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
     if (!aligned16(X) || !aligned16(Wq_t) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))

@@ -17,10 +17,10 @@
 //  * k_gemm_prefill: 256x256 output tile per 256-thread block, K step 128,
 //    LDS double buffering with a register-staged global prefetch,
 //    v_mfma_i32_32x32x32_i8, 2x2 waves of 128x128.
-//  * k_gemm_decode (s <= 16): weight streaming. One wavefront per 16*NT
-//    output columns reads its rows of Wq_t straight from HBM into the MFMA
-//    operand registers (v_mfma_i32_16x16x64_i8, rows of X beyond s are
-//    zero), several K steps in flight.
+//  * k_gemm_decode (s <= 16): weight streaming. Four wavefronts per 16*NT
+//    output columns split K and read their rows of Wq_t straight from HBM
+//    into the MFMA operand registers (v_mfma_i32_16x16x64_i8, rows of X
+//    beyond s read as zero), two register batches in flight.
 // The fused epilogue converts the int32 accumulator to fp32, multiplies by
 // 1/c_x_i * 1/c_w_j (S is never materialised), then accumulates the fp16
 // outlier product on top with fp16 MFMA (fp32 accumulate) and rounds once
@@ -45,6 +45,83 @@ constexpr int kStage = kStageA + kStageB;
 // different 16-byte bank groups.
 __device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ (row & 7)); }
 
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zero, which pads ragged tiles without branches. Word 3 selects the
+// 32-bit data format that raw loads on gfx9-family parts expect.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a per-lane offset past every buffer
+
+// Block -> output tile. Blocks are dealt to the 8 XCDs round robin
+// (block b runs on XCD b % 8); each XCD is given one contiguous run of the
+// s-fastest tile order so that the tiles sharing rows of Wq_t and Xq meet
+// in the same 4 MiB L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t nb) {
+    const int64_t q = nb / 8, r = nb % 8, x = b % 8, i = b / 8;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One 16-deep slice (outlier columns 16 kb .. 16 kb + 15) of the fp16
+// outlier product's operands for a 256 x 256 tile, staged in LDS by
+// direct-to-LDS buffer loads (lane i of a load writes 16 bytes at
+// base + 16 i): the first kSlice halves hold W[idx[k], o0 .. o0 + 255] as
+// [16][256], the next kSlice hold X_O[s0 .. s0 + 255, k] as [256][16].
+// Entries past |O|, past o or past s are written as zeros by the range
+// check. Every wavefront issues two 1 KiB loads of each operand.
+constexpr int kSlice = 256 * 16;
+
+__device__ __forceinline__ void stage_outlier_slice(int kb, int n, int wid, int lane, int64_t o0, int64_t s0,
+                                                    int64_t s, int64_t o, int64_t ldo,
+                                                    const int32_t* __restrict__ idx,
+                                                    __amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rX,
+                                                    uint16_t* dst) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int j = wid + 4 * q;                 // wave-uniform, 0..7
+        const int k0 = kb * 16 + 2 * j;            // rows k0 (lanes 0-31) and k0 + 1 (lanes 32-63)
+        const int id0 = idx[k0], id1 = idx[k0 + 1];
+        const int k = k0 + (lane >> 5);
+        const int64_t col = o0 + (lane & 31) * 8;
+        const bool okW = k < n && col < o;
+        const uint32_t vW = okW ? static_cast<uint32_t>(((lane >> 5) ? id1 : id0) * o * 2 + (lane & 31) * 16)
+                                : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, LDS_PTR(dst + j * 512), 16, vW, 0, 0, 0);
+        const int r = 32 * j + (lane >> 1);
+        const uint32_t vX = s0 + r < s ? static_cast<uint32_t>(r * ldo * 2 + (kb * 16 + (lane & 1) * 8) * 2)
+                                       : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, LDS_PTR(dst + kSlice + j * 512), 16, vX, 0, 0, 0);
+    }
+}
+
+// f += X_O[., slice] W[slice, .] for the 32 x 32 block (sb, ob) of a
+// wave's 128 x 128 output, operands from a staged slice
+// (v_mfma_f32_32x32x16_f16; the lane holds k = 8 (lane / 32) + e of the
+// slice for its column / row).
+__device__ __forceinline__ v16f apply_outlier_slice(const uint16_t* sl, int wo, int ws, int sb, int ob, int r32,
+                                                    int khalf, v16f f) {
+    const v8h xb = *reinterpret_cast<const v8h*>(sl + kSlice + (ws * 128 + sb * 32 + r32) * 16 + 8 * khalf);
+    v8h wa;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        wa[e] = __builtin_bit_cast(_Float16, sl[(8 * khalf + e) * 256 + wo * 128 + ob * 32 + r32]);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb, f, 0, 0, 0);
+}
+
+// LDS staging of the fp16 output: each wavefront owns 32 rows x 128
+// columns, rows padded to 136 halves (272 bytes) against bank conflicts.
+constexpr int kOutRow = 136;
+constexpr int kOutWave = 32 * kOutRow;          // halves per wavefront
+constexpr int kMaxOnceSlices = 5;               // extra slices staged at once
+
 template <GemmOut MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq_t,
@@ -58,26 +135,37 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int wo = wid & 1, ws = wid >> 1;
     const int64_t n_ts = (s + kTS - 1) / kTS;
-    const int64_t ts_i = static_cast<int64_t>(blockIdx.x) % n_ts;
-    const int64_t to_i = static_cast<int64_t>(blockIdx.x) / n_ts;
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t ts_i = tile % n_ts, to_i = tile / n_ts;
     const int64_t o0 = to_i * kTO, s0 = ts_i * kTS;
 
+    // Tile-relative buffer resources: rows past o (or s) read as zero.
+    const int64_t o_rows = o - o0 < kTO ? o - o0 : kTO;
+    const int64_t s_rows = s - s0 < kTS ? s - s0 : kTS;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq_t + o0 * h, static_cast<uint32_t>(o_rows * h));
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(Xq + s0 * h, static_cast<uint32_t>(s_rows * h));
+
     // Global -> register staging: thread t moves chunk (t & 7) of rows
-    // (t >> 3) + 32 p, p = 0..7, of both tiles.
+    // (t >> 3) + 32 p, p = 0..7, of both tiles. The row offset travels in
+    // the per-lane offset, which the range check covers, so rows past the
+    // tile read as zero; only the uniform K offset goes in the scalar offset.
     const int st_c = t & 7, st_r = t >> 3;
+    uint32_t voff[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) voff[p] = static_cast<uint32_t>((st_r + 32 * p) * h + st_c * 16);
     v4i ra[8], rb[8];
     const int64_t KT = (h + kTK - 1) / kTK;
-    const v4i zero4 = {0, 0, 0, 0};
 
     auto gload = [&](int64_t kt) {
-        const int64_t k = kt * kTK + st_c * 16;
-        const bool kin = k < h;
+        const uint32_t k = static_cast<uint32_t>(kt * kTK);
+        // chunks past h (a half stage when h % 128 == 64, or the prefetch
+        // past the last stage) read as zero
+        const bool kin = k + st_c * 16 < h;
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            const int64_t row = st_r + 32 * p;
-            const int64_t orow = o0 + row, srow = s0 + row;
-            ra[p] = (kin && orow < o) ? *reinterpret_cast<const v4i*>(Wq_t + orow * h + k) : zero4;
-            rb[p] = (kin && srow < s) ? *reinterpret_cast<const v4i*>(Xq + srow * h + k) : zero4;
+            const uint32_t v = kin ? voff[p] : kOutOfRange;
+            ra[p] = buf_load16(rA, v, k);
+            rb[p] = buf_load16(rB, v, k);
         }
     };
     auto lstore = [&](int buf) {
@@ -91,6 +179,23 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         }
     };
 
+    const int r32 = lane & 31, khalf = lane >> 5;
+
+    // The first slice of the outlier operands goes to its own LDS region
+    // now; the loads complete under the main loop and hold no registers.
+    __shared__ __attribute__((aligned(16))) uint16_t olds[2 * kSlice];
+    int n_o = 0;
+    const bool mixed = MODE == GemmOut::Mixed;
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(mixed ? W + o0 : nullptr, mixed ? static_cast<uint32_t>((h * o - o0) * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rX = make_rsrc(mixed ? X_O + s0 * ldo : nullptr,
+                                                mixed ? static_cast<uint32_t>(s_rows * ldo * 2) : 0u);
+    if constexpr (MODE == GemmOut::Mixed) {
+        n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
+        if (n_o > 0)
+            stage_outlier_slice(0, n_o, __builtin_amdgcn_readfirstlane(wid), lane, o0, s0, s, o, ldo, idx, rW, rX,
+                                olds);
+    }
+
     v16i acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -102,26 +207,69 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     gload(0);
     lstore(0);
     __syncthreads();
-    const int r32 = lane & 31, khalf = lane >> 5;
+    // LDS slots of this lane's fragments (chunk added per sub-step)
+    int rowA[4], rowB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        rowA[i] = wo * 128 + i * 32 + r32;
+        rowB[i] = ws * 128 + i * 32 + r32;
+    }
+    v4i fa[2][4], fb[2][4];
+    auto frags = [&](const v4i* A, const v4i* B, int kk, v4i* a, v4i* b) {
+        const int c = kk * 2 + khalf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = A[swz(rowA[i], c)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = B[swz(rowB[i], c)];
+    };
+    auto mma = [&](const v4i* a, const v4i* b) {
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb)
+                acc[ob][sb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ob], b[sb], acc[ob][sb], 0, 0, 0);
+    };
+
+    // One basic block per K stage. The prefetch of stage kt + 1 is issued
+    // unconditionally: past the last stage every offset is >= h and the
+    // range-checked loads return zeros that land in the idle buffer.
     for (int64_t kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) gload(kt + 1);
+        gload(kt + 1);
         const v4i* A = lds + (kt & 1) * kStage;
         const v4i* B = A + kStageA;
+        frags(A, B, 0, fa[0], fb[0]);
+        frags(A, B, 1, fa[1], fb[1]);
+        mma(fa[0], fb[0]);
+        frags(A, B, 2, fa[0], fb[0]);
+        mma(fa[1], fb[1]);
+        frags(A, B, 3, fa[1], fb[1]);
+        mma(fa[0], fb[0]);
+        // The other buffer was last read before the previous barrier.
+        lstore((kt + 1) & 1);
+        mma(fa[1], fb[1]);
+        // Issue order: the fragments of sub-steps 0 and 1, then each group of
+        // 16 MFMAs carries one kind of memory traffic: the global prefetch,
+        // the fragments of sub-step 2, of sub-step 3, and the LDS stores.
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // DS read
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int c = kk * 2 + khalf;
-            v4i a[4], b[4];
-#pragma unroll
-            for (int ob = 0; ob < 4; ++ob) a[ob] = A[swz(wo * 128 + ob * 32 + r32, c)];
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) b[sb] = B[swz(ws * 128 + sb * 32 + r32, c)];
-#pragma unroll
-            for (int ob = 0; ob < 4; ++ob)
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-                    acc[ob][sb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ob], b[sb], acc[ob][sb], 0, 0, 0);
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
         }
-        if (kt + 1 < KT) lstore((kt + 1) & 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // DS write
+        }
         __syncthreads();
     }
 
@@ -146,110 +294,151 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             }
     } else {
         uint16_t* C = static_cast<uint16_t*>(Cout);
-        float inv_x[4];
+        // Slices past the first go to the main-loop buffers, free now: all
+        // at once when they fit (|O| <= 96), else in rounds per row block.
+        // The output staging area follows them.
+        const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+        uint16_t* big = reinterpret_cast<uint16_t*>(lds);
+        uint16_t* out_st = big + kMaxOnceSlices * 2 * kSlice + wid * kOutWave;
+        const int nsl = (n_o + 15) / 16;
+        const bool once = nsl <= 1 + kMaxOnceSlices;
+        if (once && nsl > 1) {
+            for (int q = 1; q < nsl; ++q)
+                stage_outlier_slice(q, n_o, wid_u, lane, o0, s0, s, o, ldo, idx, rW, rX, big + (q - 1) * 2 * kSlice);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        // 1 / c_w of the wave's 128 columns, kept in its LDS area (reciprocals to 1 ulp).
+        float* invw = reinterpret_cast<float*>(big + kMaxOnceSlices * 2 * kSlice + 4 * kOutWave) + wid * 128;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t col = o0 + wo * 128 + lane + 64 * i;
+            invw[lane + 64 * i] = __builtin_amdgcn_rcpf(col < o ? c_w[col] : 1.0f);
+        }
+        // One 32-row block at a time: a lane then holds 4-column runs of one
+        // row across all 128 columns of the wave.
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             const int64_t srow = s0 + ws * 128 + sb * 32 + r32;
-            inv_x[sb] = 1.0f / (srow < s ? c_x[srow] : 1.0f);
-        }
-        const int n = n_out[0];
-        // One 32-column block at a time, so that only 64 fp32 values are
-        // live next to the remaining int32 accumulators.
+            const float inv_x = __builtin_amdgcn_rcpf(srow < s ? c_x[srow] : 1.0f);
+            if (!once) __syncthreads();   // the previous row block's rounds are done
 #pragma unroll
-        for (int ob = 0; ob < 4; ++ob) {
-            // Dequantise: f = C_i32 * (1/c_x) * (1/c_w).
-            v16f f[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t ocol = o0 + wo * 128 + ob * 32 + 8 * g + 4 * khalf;
-                v4f cw = ocol < o ? *reinterpret_cast<const v4f*>(c_w + ocol) : v4f{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float inv_w = 1.0f / cw[e];
-#pragma unroll
-                    for (int sb = 0; sb < 4; ++sb)
-                        f[sb][4 * g + e] = static_cast<float>(acc[ob][sb][4 * g + e]) * (inv_x[sb] * inv_w);
-                }
-            }
-            // Outlier product X_O W[idx, :] with v_mfma_f32_32x32x16_f16. The A
-            // operand holds W[idx[k], ocol] for ocol = lane % 32 of the block
-            // and k = 16 kb + 8 (lane / 32) + e; the B operand holds the same
-            // k range of X_O row srow (zero-padded past |O|).
-            const int64_t ocol_a = o0 + wo * 128 + ob * 32 + r32;
-            for (int kb = 0; kb * 16 < n; ++kb) {
-                const int kbase = kb * 16 + 8 * khalf;
-                v8h wa;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int k = kbase + e;
-                    uint16_t bits = (k < n && ocol_a < o) ? W[static_cast<int64_t>(idx[k]) * o + ocol_a]
-                                                          : static_cast<uint16_t>(0);
-                    wa[e] = __builtin_bit_cast(_Float16, bits);
-                }
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) {
-                    const int64_t srow = s0 + ws * 128 + sb * 32 + r32;
-                    v8h xb;
-                    if (srow < s) {
-                        xb = *reinterpret_cast<const v8h*>(X_O + srow * ldo + kbase);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) xb[e] = static_cast<_Float16>(0.0f);
-                    }
-                    f[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb, f[sb], 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                const int64_t srow = s0 + ws * 128 + sb * 32 + r32;
+            for (int ob = 0; ob < 4; ++ob) {
+                // Dequantise: f = C_i32 * (1/c_x) * (1/c_w).
+                v16f f;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int64_t ocol = o0 + wo * 128 + ob * 32 + 8 * g + 4 * khalf;
-                    if (srow < s && ocol < o) {
-                        const uint32_t lo = float_to_half_bits(f[sb][4 * g]) |
-                                            (static_cast<uint32_t>(float_to_half_bits(f[sb][4 * g + 1])) << 16);
-                        const uint32_t hi = float_to_half_bits(f[sb][4 * g + 2]) |
-                                            (static_cast<uint32_t>(float_to_half_bits(f[sb][4 * g + 3])) << 16);
-                        *reinterpret_cast<uint2*>(C + srow * o + ocol) = make_uint2(lo, hi);
+                    const v4f iw = *reinterpret_cast<const v4f*>(invw + ob * 32 + 8 * g + 4 * khalf);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        f[4 * g + e] = static_cast<float>(acc[ob][sb][4 * g + e]) * (inv_x * iw[e]);
+                }
+                // Outlier product X_O W[idx, :] on top (fp32 accumulate).
+                if (n_o > 0) f = apply_outlier_slice(olds, wo, ws, sb, ob, r32, khalf, f);
+                if (once) {
+                    for (int q = 1; q < nsl; ++q)
+                        f = apply_outlier_slice(big + (q - 1) * 2 * kSlice, wo, ws, sb, ob, r32, khalf, f);
+                } else {
+                    for (int rb = 1; rb < nsl; rb += kMaxOnceSlices) {
+                        const int re = rb + kMaxOnceSlices < nsl ? rb + kMaxOnceSlices : nsl;
+                        __syncthreads();
+                        for (int q = rb; q < re; ++q)
+                            stage_outlier_slice(q, n_o, wid_u, lane, o0, s0, s, o, ldo, idx, rW, rX,
+                                                big + (q - rb) * 2 * kSlice);
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        __syncthreads();
+                        for (int q = rb; q < re; ++q)
+                            f = apply_outlier_slice(big + (q - rb) * 2 * kSlice, wo, ws, sb, ob, r32, khalf, f);
                     }
                 }
+                // Round once to fp16 and stage in this wavefront's LDS area
+                // (LDS operations of one wavefront execute in order, so its
+                // own reads below see these writes).
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t lo = float_to_half_bits(f[4 * g]) |
+                                        (static_cast<uint32_t>(float_to_half_bits(f[4 * g + 1])) << 16);
+                    const uint32_t hi = float_to_half_bits(f[4 * g + 2]) |
+                                        (static_cast<uint32_t>(float_to_half_bits(f[4 * g + 3])) << 16);
+                    *reinterpret_cast<uint2*>(out_st + r32 * kOutRow + ob * 32 + 8 * g + 4 * khalf) =
+                        make_uint2(lo, hi);
+                }
+            }
+            // Write the 32 x 128 block as full 256-byte rows: 16 lanes per
+            // row, 4 rows per store instruction.
+            const int64_t gcol = o0 + wo * 128 + (lane & 15) * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 4 * i + (lane >> 4);
+                const v4i v = *reinterpret_cast<const v4i*>(out_st + row * kOutRow + (lane & 15) * 8);
+                const int64_t grow = s0 + ws * 128 + sb * 32 + row;
+                if (grow < s && gcol < o) *reinterpret_cast<v4i*>(C + grow * o + gcol) = v;
             }
         }
     }
 }
 
 // ------------------------------------------------------------------ decode
-// 16x16 fp16 outlier accumulation shared by the decode epilogue and the
-// standalone outlier product: f (16x16 fp32 tile, lane layout of
-// v_mfma_f32_16x16x32_f16: register r <-> D[o = 4 (lane / 16) + r][s = lane % 16])
-// += X_O[s, k] W[idx[k], o] over k < n.
-__device__ __forceinline__ v4f outlier_tile_16x16(v4f f, int lane, int64_t ocol, int64_t srow, int64_t s,
+// Operands of one 32-deep slice (outlier columns 32 kb .. 32 kb + 31) of the
+// fp16 outlier product for one 16 x 16 output tile, in the lane layout of
+// v_mfma_f32_16x16x32_f16: wa holds W[idx[k], ocol], xb holds X_O[srow, k],
+// k = 32 kb + 8 (lane / 16) + e, ocol = ocol0 + lane % 16, srow = srow0 +
+// lane % 16. Indices come through scalar loads; columns past |O|, rows past
+// s and columns past o read as zero. Shared by the decode epilogue and the
+// standalone outlier product (register layout: register r of the result
+// holds D[o = 4 (lane / 16) + r][s = lane % 16]).
+__device__ __forceinline__ void outlier_operands_16(int kb, int n, int lane, int64_t ocol0, int64_t srow0,
+                                                    int64_t s, int64_t o, const uint16_t* __restrict__ X_O,
+                                                    int64_t ldo, const int32_t* __restrict__ idx,
+                                                    const uint16_t* __restrict__ W, v8h& wa, v8h& xb) {
+    int id[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) id[j] = idx[kb * 32 + j];     // uniform address: scalar loads
+    const int g = lane >> 4;
+    const int kbase = kb * 32 + 8 * g;
+    const int64_t ocol = ocol0 + (lane & 15);
+    const bool col_ok = ocol < o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bool ok = col_ok && kbase + e < n;
+        const int sel = g == 0 ? id[e] : g == 1 ? id[8 + e] : g == 2 ? id[16 + e] : id[24 + e];
+        const int row = ok ? sel : 0;
+        const uint16_t bits = W[static_cast<int64_t>(row) * o + (col_ok ? ocol : 0)];
+        wa[e] = __builtin_bit_cast(_Float16, ok ? bits : static_cast<uint16_t>(0));
+    }
+    const int64_t srow = srow0 + (lane & 15);
+    const bool rok = srow < s;
+    const v8h v = *reinterpret_cast<const v8h*>(X_O + (rok ? srow : 0) * ldo + kbase);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xb[e] = rok ? v[e] : static_cast<_Float16>(0.0f);
+}
+
+// f += X_O W[idx, :] over all outlier columns for one 16 x 16 tile; the
+// first slice's operands may be passed in already loaded.
+__device__ __forceinline__ v4f outlier_tile_16x16(v4f f, int lane, int64_t ocol0, int64_t srow0, int64_t s,
                                                    int64_t o, const uint16_t* __restrict__ X_O, int64_t ldo,
                                                    const int32_t* __restrict__ idx, int n,
-                                                   const uint16_t* __restrict__ W) {
-    const int g = lane >> 4;
+                                                   const uint16_t* __restrict__ W, const v8h* first) {
     for (int kb = 0; kb * 32 < n; ++kb) {
-        const int kbase = kb * 32 + 8 * g;
         v8h wa, xb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int k = kbase + e;
-            uint16_t bits = (k < n && ocol < o) ? W[static_cast<int64_t>(idx[k]) * o + ocol] : static_cast<uint16_t>(0);
-            wa[e] = __builtin_bit_cast(_Float16, bits);
-        }
-        if (srow < s) {
-            xb = *reinterpret_cast<const v8h*>(X_O + srow * ldo + kbase);
+        if (kb == 0 && first != nullptr) {
+            wa = first[0];
+            xb = first[1];
         } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xb[e] = static_cast<_Float16>(0.0f);
+            outlier_operands_16(kb, n, lane, ocol0, srow0, s, o, X_O, ldo, idx, W, wa, xb);
         }
         f = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, xb, f, 0, 0, 0);
     }
     return f;
 }
 
-constexpr int kDecodeUnroll = 8;
+constexpr int kDecodeU = 4;        // K steps of 64 per register batch
+constexpr int kDecodeSplit = 4;    // wavefronts of a block splitting K
 
+// Decode: block = 4 wavefronts on the same 16*NT output columns, each
+// streaming one quarter of K from HBM with two register batches in flight
+// (range-checked loads: steps past a wave's range read as zero), then an
+// exact int32 reduction of the four partial tiles through LDS.
 template <GemmOut MODE, int NT>
 __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq_t,
                                                      int64_t s, int64_t h, int64_t o,
@@ -258,81 +447,92 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
                                                      const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ n_out,
                                                      const uint16_t* __restrict__ W, void* __restrict__ Cout) {
+    __shared__ v4i red[kDecodeSplit][NT][64];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    const int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + wid;
-    const int64_t obase = gw * 16 * NT;
-    if (obase >= o) return;   // whole wavefront; no block-level synchronisation below
-
+    const int64_t obase = static_cast<int64_t>(blockIdx.x) * 16 * NT;
     const int r16 = lane & 15, g = lane >> 4;
-    const int8_t* wp[NT];
+
+    // Wq_t rows obase .. obase + 16 NT - 1 (always inside o: 16 NT divides 64).
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq_t + obase * h, static_cast<uint32_t>(16 * NT * h));
+    // Xq rows 0 .. s - 1; lanes of rows >= s fall past the range and read zero.
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(Xq, static_cast<uint32_t>(s * h));
+    uint32_t vA[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        int64_t orow = obase + nt * 16 + r16;
-        if (orow >= o) orow = o - 1;   // never used for output; keeps loads in bounds
-        wp[nt] = Wq_t + orow * h + g * 16;
+    for (int nt = 0; nt < NT; ++nt) vA[nt] = static_cast<uint32_t>((nt * 16 + r16) * h + g * 16);
+    const uint32_t vB = static_cast<uint32_t>(r16 * h + g * 16);
+
+    // Wavefronts that finish an output tile fetch the first slice of its
+    // outlier operands now, so the loads complete under the K loop.
+    int n_o = 0;
+    v8h pre[2];
+    if constexpr (MODE == GemmOut::Mixed) {
+        n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
+        if (wid < NT && n_o > 0)
+            outlier_operands_16(0, n_o, lane, obase + wid * 16, 0, s, o, X_O, ldo, idx, W, pre[0], pre[1]);
     }
-    const bool xvalid = r16 < s;
-    const int8_t* xp = Xq + (xvalid ? r16 : 0) * h + g * 16;
-    const v4i zero4 = {0, 0, 0, 0};
+
+    const int64_t nsteps = h / 64;
+    const int64_t per = ((nsteps + kDecodeSplit - 1) / kDecodeSplit + kDecodeU - 1) / kDecodeU * kDecodeU;
+    const int64_t st0 = wid * per < nsteps ? wid * per : nsteps;
+    const int64_t st1 = st0 + per < nsteps ? st0 + per : nsteps;
 
     v4i acc[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = zero4;
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
+    v4i a0[kDecodeU][NT], b0[kDecodeU], a1[kDecodeU][NT], b1[kDecodeU];
 
-    const int64_t nsteps = h / 64;
-    int64_t st = 0;
-    for (; st + kDecodeUnroll <= nsteps; st += kDecodeUnroll) {
-        v4i a[kDecodeUnroll][NT], b[kDecodeUnroll];
+    auto load = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU], int64_t stb) {
 #pragma unroll
-        for (int u = 0; u < kDecodeUnroll; ++u) {
-            const int64_t k = (st + u) * 64;
+        for (int u = 0; u < kDecodeU; ++u) {
+            const bool ok = stb + u < st1;
+            const uint32_t k = ok ? static_cast<uint32_t>((stb + u) * 64) : 0u;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                a[u][nt] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp[nt] + k));
-            b[u] = xvalid ? *reinterpret_cast<const v4i*>(xp + k) : zero4;
+            for (int nt = 0; nt < NT; ++nt) a[u][nt] = buf_load16(rA, ok ? vA[nt] : kOutOfRange, k);
+            b[u] = buf_load16(rB, ok ? vB : kOutOfRange, k);
         }
+    };
+    auto mma = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU]) {
 #pragma unroll
-        for (int u = 0; u < kDecodeUnroll; ++u)
+        for (int u = 0; u < kDecodeU; ++u)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][nt], b[u], acc[nt], 0, 0, 0);
+    };
+
+    load(a0, b0, st0);
+    for (int64_t stb = st0; stb < st1; stb += 2 * kDecodeU) {
+        load(a1, b1, stb + kDecodeU);
+        mma(a0, b0);
+        load(a0, b0, stb + 2 * kDecodeU);
+        mma(a1, b1);
     }
-    for (; st < nsteps; ++st) {
-        const int64_t k = st * 64;
-        v4i b = xvalid ? *reinterpret_cast<const v4i*>(xp + k) : zero4;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            v4i a = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp[nt] + k));
-            acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[nt], 0, 0, 0);
-        }
-    }
+    for (int nt = 0; nt < NT; ++nt) red[wid][nt][lane] = acc[nt];
+    __syncthreads();
+    if (wid >= NT) return;
+    const int nt = wid;
+    v4i sum = red[0][nt][lane];
+#pragma unroll
+    for (int w = 1; w < kDecodeSplit; ++w) sum += red[w][nt][lane];
 
     // Lane layout of a 16x16 accumulator: register r holds D[o = 4 g + r][s = r16].
     const int64_t srow = r16;
+    const int64_t ocol = obase + nt * 16 + 4 * g;
     if constexpr (MODE == GemmOut::Int32) {
         int32_t* C = static_cast<int32_t*>(Cout);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int64_t ocol = obase + nt * 16 + 4 * g;
-            if (srow < s && ocol < o) *reinterpret_cast<v4i*>(C + srow * o + ocol) = acc[nt];
-        }
+        if (srow < s) *reinterpret_cast<v4i*>(C + srow * o + ocol) = sum;
     } else {
         uint16_t* C = static_cast<uint16_t*>(Cout);
-        const float inv_x = 1.0f / (srow < s ? c_x[srow] : 1.0f);
-        const int n = n_out[0];
+        const float inv_x = __builtin_amdgcn_rcpf(srow < s ? c_x[srow] : 1.0f);
+        const v4f cw = *reinterpret_cast<const v4f*>(c_w + ocol);
+        v4f f;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int64_t ocol = obase + nt * 16 + 4 * g;
-            v4f cw = ocol < o ? *reinterpret_cast<const v4f*>(c_w + ocol) : v4f{1.f, 1.f, 1.f, 1.f};
-            v4f f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(acc[nt][e]) * (inv_x * (1.0f / cw[e]));
-            f = outlier_tile_16x16(f, lane, obase + nt * 16 + r16, srow, s, o, X_O, ldo, idx, n, W);
-            if (srow < s && ocol < o) {
-                const uint32_t lo = float_to_half_bits(f[0]) | (static_cast<uint32_t>(float_to_half_bits(f[1])) << 16);
-                const uint32_t hi = float_to_half_bits(f[2]) | (static_cast<uint32_t>(float_to_half_bits(f[3])) << 16);
-                *reinterpret_cast<uint2*>(C + srow * o + ocol) = make_uint2(lo, hi);
-            }
+        for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+        f = outlier_tile_16x16(f, lane, obase + nt * 16, 0, s, o, X_O, ldo, idx, n_o, W, pre);
+        if (srow < s) {
+            const uint32_t lo = float_to_half_bits(f[0]) | (static_cast<uint32_t>(float_to_half_bits(f[1])) << 16);
+            const uint32_t hi = float_to_half_bits(f[2]) | (static_cast<uint32_t>(float_to_half_bits(f[3])) << 16);
+            *reinterpret_cast<uint2*>(C + srow * o + ocol) = make_uint2(lo, hi);
         }
     }
 }
@@ -353,7 +553,7 @@ __global__ __launch_bounds__(256) void k_outlier_only(const uint16_t* __restrict
     const int r16 = lane & 15, g = lane >> 4;
     const int64_t srow = ts_i * 16 + r16;
     v4f f = {0.f, 0.f, 0.f, 0.f};
-    f = outlier_tile_16x16(f, lane, to_i * 16 + r16, srow, s, o, X_O, ldo, idx, n_out[0], W);
+    f = outlier_tile_16x16(f, lane, to_i * 16, ts_i * 16, s, o, X_O, ldo, idx, n_out[0], W, nullptr);
     const int64_t ocol = to_i * 16 + 4 * g;
     if (srow < s) *reinterpret_cast<v4f*>(C_O + srow * o + ocol) = f;
 }
@@ -364,8 +564,7 @@ hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, 
                        const uint16_t* W, int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream) {
     if (s <= 16) {
         constexpr int NT = 2;
-        const int64_t waves = (o + 16 * NT - 1) / (16 * NT);
-        hipLaunchKernelGGL((k_gemm_decode<MODE, NT>), dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0,
+        hipLaunchKernelGGL((k_gemm_decode<MODE, NT>), dim3(static_cast<unsigned>(o / (16 * NT))), dim3(256), 0,
                            stream, Xq, Wq_t, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C);
     } else {
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
