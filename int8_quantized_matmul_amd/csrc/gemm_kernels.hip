@@ -157,13 +157,14 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     const int64_t KT = (h + kTK - 1) / kTK;
 
     auto gload = [&](int64_t kt) {
-        const uint32_t k = static_cast<uint32_t>(kt * kTK);
+        const uint32_t k = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kt * kTK));
         // chunks past h (a half stage when h % 128 == 64, or the prefetch
-        // past the last stage) read as zero
-        const bool kin = k + st_c * 16 < h;
+        // past the last stage) read as zero: their offset gets the top bit
+        // (row offsets stay below 2^31), computed without a branch
+        const uint32_t oob = (k + st_c * 16 < static_cast<uint32_t>(h)) ? 0u : kOutOfRange;
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            const uint32_t v = kin ? voff[p] : kOutOfRange;
+            const uint32_t v = voff[p] | oob;
             ra[p] = buf_load16(rA, v, k);
             rb[p] = buf_load16(rB, v, k);
         }
@@ -206,6 +207,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 
     gload(0);
     lstore(0);
+    gload(1);
     __syncthreads();
     // LDS slots of this lane's fragments (chunk added per sub-step)
     int rowA[4], rowB[4];
@@ -230,47 +232,59 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                 acc[ob][sb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ob], b[sb], acc[ob][sb], 0, 0, 0);
     };
 
-    // One basic block per K stage. The prefetch of stage kt + 1 is issued
-    // unconditionally: past the last stage every offset is >= h and the
-    // range-checked loads return zeros that land in the idle buffer.
+    frags(lds, lds + kStageA, 0, fa[0], fb[0]);
+    // Software pipeline across the stage barrier: the fragments of the
+    // last sub-step are read before the barrier and multiplied after it,
+    // covering the latency of the next stage's first LDS reads. The global
+    // prefetch runs two stages ahead of its LDS store. Past the last stage
+    // every offset is >= h and the range-checked loads return zeros that
+    // land in the idle buffer.
     for (int64_t kt = 0; kt < KT; ++kt) {
-        gload(kt + 1);
         const v4i* A = lds + (kt & 1) * kStage;
         const v4i* B = A + kStageA;
-        frags(A, B, 0, fa[0], fb[0]);
         frags(A, B, 1, fa[1], fb[1]);
         mma(fa[0], fb[0]);
         frags(A, B, 2, fa[0], fb[0]);
         mma(fa[1], fb[1]);
         frags(A, B, 3, fa[1], fb[1]);
-        mma(fa[0], fb[0]);
         // The other buffer was last read before the previous barrier.
         lstore((kt + 1) & 1);
-        mma(fa[1], fb[1]);
-        // Issue order: the fragments of sub-steps 0 and 1, then each group of
-        // 16 MFMAs carries one kind of memory traffic: the global prefetch,
-        // the fragments of sub-step 2, of sub-step 3, and the LDS stores.
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // DS read
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // VMEM read
-        }
+        mma(fa[0], fb[0]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 8; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // DS write
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // DS write
         }
         __syncthreads();
+        const v4i* A2 = lds + ((kt + 1) & 1) * kStage;
+        frags(A2, A2 + kStageA, 0, fa[0], fb[0]);
+        gload(kt + 2);
+        mma(fa[1], fb[1]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
     }
 
     // Lane layout of a 32x32 accumulator: register r holds
