@@ -44,6 +44,20 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+def product_kernel_ms(i8, torch, n, launch):
+    """Average duration of the product kernel: n back-to-back launches on the
+    launch stream between one pair of HIP events (its inputs are the step's
+    intermediates, already in place)."""
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(n):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def run_prefill(i8, torch, w, steps, warmup, dev):
     from workloads import make_inputs
     inp = make_inputs(w)
@@ -67,43 +81,27 @@ def run_prefill(i8, torch, w, steps, warmup, dev):
     v = i8.forward_workspace_views(ws, s, h)
     C = torch.empty((s, o), dtype=torch.float16, device=dev)
 
-    def step(ev_a=None, ev_b=None):
-        # exactly the launches of i8mm_forward, split so that the product
-        # kernel can be bracketed by events on the same stream
-        i8.detect_outlier_cols(X, w.alpha, v["mask"], v["idx"], v["n_out"])
-        i8.quantize_rowwise(X, v["mask"], v["idx"], v["n_out"], v["Xq"], v["c_x"], v["X_O"])
-        if ev_a is not None:
-            ev_a.record()
-        i8.int8_mixed_matmul(v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq_t, c_w, W, C)
-        if ev_b is not None:
-            ev_b.record()
+    def step():
+        # one forward: detect -> quantise rows -> decomposed product (one C-ABI call)
+        i8.forward(X, Wq_t, c_w, W, w.alpha, workspace=ws, C=C)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    gemm_ev = [_events(torch) for _ in range(steps)]
     t0, t1 = _events(torch)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
-    for k in range(steps):
-        step(*gemm_ev[k])
+    for _ in range(steps):
+        step()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_ms = t0.elapsed_time(t1) / steps
-    gemm_ms = sum(a.elapsed_time(b) for a, b in gemm_ev) / steps
+    gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
+        v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq_t, c_w, W, C))
 
-    # a plain forward (one C-ABI call per step) timed the same way, for reference
-    e0, e1 = _events(torch)
-    e0.record()
-    for _ in range(steps):
-        i8.forward(X, Wq_t, c_w, W, w.alpha, workspace=ws, C=C)
-    e1.record()
-    torch.cuda.synchronize()
-    fwd_ms = e0.elapsed_time(e1) / steps
     n_out = int(v["n_out"].cpu()[0])
-    return dict(step_ms=step_ms, gemm_ms=gemm_ms, fwd_ms=fwd_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out,
+    return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out,
                 inputs=inp)
 
 
@@ -121,19 +119,15 @@ def run_decode(i8, torch, w, steps, warmup, dev):
     for _ in range(warmup):
         i8.forward(X, Wq_t, c_w, W, w.alpha, workspace=ws, C=C)
     torch.cuda.synchronize()
-    gemm_ev = [_events(torch) for _ in range(steps)]
     t0, t1 = _events(torch)
     t0.record()
-    for k in range(steps):
-        i8.detect_outlier_cols(X, w.alpha, v["mask"], v["idx"], v["n_out"])
-        i8.quantize_rowwise(X, v["mask"], v["idx"], v["n_out"], v["Xq"], v["c_x"], v["X_O"])
-        gemm_ev[k][0].record()
-        i8.int8_mixed_matmul(v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq_t, c_w, W, C)
-        gemm_ev[k][1].record()
+    for _ in range(steps):
+        i8.forward(X, Wq_t, c_w, W, w.alpha, workspace=ws, C=C)
     t1.record()
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
-    gemm_ms = sum(a.elapsed_time(b) for a, b in gemm_ev) / steps
+    gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
+        v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq_t, c_w, W, C))
     n_out = int(v["n_out"].cpu()[0])
     weight_bytes = h * o + 2 * n_out * o + 4 * o
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes)
@@ -258,7 +252,6 @@ def main(argv=None):
             "avg_launch_ms": round(pre["gemm_ms"], 5),
         },
         "pct_int8_peak_effective": round(100 * tops / INT8_PEAK_TOPS, 2),
-        "forward_single_call_ms": round(pre["fwd_ms"], 5),
         "weight_conversion": {"ms": round(pre["conv_ms"], 4),
                               "GB_per_s": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1)},
     }
