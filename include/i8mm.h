@@ -172,21 +172,28 @@ i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq_t,
                                int64_t s, int64_t h, int64_t o, int32_t* C_i32,
                                hipStream_t stream);
 
+/* Bytes at the start of the forward workspace that hold the mask accumulator. */
+#define I8MM_FORWARD_ACC_BYTES 16640
+
 /*
- * Bytes of device workspace that i8mm_forward needs for (s, h): mask, idx,
- * n_out, Xq, c_x and X_O (ldo = round_up(h, 32)), each 256-byte aligned.
- * Returns 0 for invalid shapes.
+ * Bytes of device workspace that i8mm_forward needs for (s, h): the mask
+ * accumulator, mask, idx, n_out, Xq, c_x and X_O (ldo = round_up(h, 32)),
+ * each 256-byte aligned. Returns 0 for invalid shapes.
  */
 size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h);
 
 /*
  * The whole per-forward path for one linear layer ([DIGEST] "The Full
  * LLM.int8() Algorithm", Steps 1-5): detect, quantise rows and gather,
- * decomposed product. Weights must already be converted by
- * i8mm_quantize_colwise_weights.
+ * decomposed product, in two or three kernel launches. Weights must already
+ * be converted by i8mm_quantize_colwise_weights.
  *
  * workspace: caller-owned device buffer of i8mm_forward_workspace_bytes(s, h)
- * bytes, 256-byte aligned; on return (after synchronisation) it holds the
+ * bytes, 256-byte aligned. Its first I8MM_FORWARD_ACC_BYTES bytes (the
+ * detection's mask accumulator) must be ZERO before the first call, e.g. by
+ * allocating it zero-filled; every i8mm_forward returns them to zero, so a
+ * workspace may be reused for any shape whose size fits. Calls that share a
+ * workspace must not overlap. After completion the workspace holds the
  * intermediates at the offsets given by i8mm_forward_workspace_layout.
  * X: [s, h] fp16; Wq_t: [o, h] int8; c_w: [o] fp32; W: [h, o] fp16;
  * C: [s, o] fp16 (written).
@@ -196,12 +203,12 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
                          void* workspace, uint16_t* C, hipStream_t stream);
 
 /*
- * Byte offsets of the intermediates inside the forward workspace, in the
- * order mask, idx, n_out, Xq, c_x, X_O (6 entries written to offsets[]),
- * and the X_O row stride (elements) in *ldo. Returns I8MM_EINVAL for bad
- * shapes or null pointers. Host-only; touches no device.
+ * Byte offsets inside the forward workspace, in the order accumulator, mask,
+ * idx, n_out, Xq, c_x, X_O (7 entries written to offsets[]), and the X_O row
+ * stride (elements) in *ldo. Returns I8MM_EINVAL for bad shapes or null
+ * pointers. Host-only; touches no device.
  */
-i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[6], int64_t* ldo);
+i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[7], int64_t* ldo);
 
 /* Library version string (static storage). */
 const char* i8mm_version(void);

@@ -195,16 +195,17 @@ def int8_gemm_i32(Xq: torch.Tensor, Wq_t: torch.Tensor, C: Optional[torch.Tensor
 
 
 def forward_workspace(s: int, h: int, device) -> torch.Tensor:
-    """A device workspace (uint8) for forward()."""
+    """A zero-filled device workspace (uint8) for forward(). Its leading mask
+    accumulator must start at zero; forward() leaves it zero again."""
     n = _lib.i8mm_forward_workspace_bytes(s, h)
     if n == 0:
         raise I8MMError(f"invalid shape for the forward workspace: s={s}, h={h}")
-    return torch.empty((n,), dtype=torch.uint8, device=device)
+    return torch.zeros((n,), dtype=torch.uint8, device=device)
 
 
 def forward_workspace_views(workspace: torch.Tensor, s: int, h: int) -> Dict[str, torch.Tensor]:
     """Typed views of the intermediates that forward() leaves in its workspace."""
-    offs = (ctypes.c_size_t * 6)()
+    offs = (ctypes.c_size_t * 7)()
     ldo = ctypes.c_int64()
     _check(_lib.i8mm_forward_workspace_layout(s, h, offs, ctypes.byref(ldo)), "forward_workspace_layout")
     nw = (h + 31) // 32
@@ -214,12 +215,13 @@ def forward_workspace_views(workspace: torch.Tensor, s: int, h: int) -> Dict[str
         return workspace[offs[i]:offs[i] + nbytes].view(dtype).view(shape)
 
     return {
-        "mask": view(0, 4 * nw, torch.int32, (nw,)),
-        "idx": view(1, 4 * h, torch.int32, (h,)),
-        "n_out": view(2, 4, torch.int32, (1,)),
-        "Xq": view(3, s * h, torch.int8, (s, h)),
-        "c_x": view(4, 4 * s, torch.float32, (s,)),
-        "X_O": view(5, 2 * s * l, torch.float16, (s, l)),
+        "acc": view(0, 4 * nw, torch.int32, (nw,)),
+        "mask": view(1, 4 * nw, torch.int32, (nw,)),
+        "idx": view(2, 4 * h, torch.int32, (h,)),
+        "n_out": view(3, 4, torch.int32, (1,)),
+        "Xq": view(4, s * h, torch.int8, (s, h)),
+        "c_x": view(5, 4 * s, torch.float32, (s,)),
+        "X_O": view(6, 2 * s * l, torch.float16, (s, l)),
     }
 
 

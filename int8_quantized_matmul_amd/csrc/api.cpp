@@ -56,8 +56,11 @@ i8mm_status check_device() {
 
 i8mm_status launched(hipError_t e) { return e == hipSuccess ? I8MM_OK : I8MM_ELAUNCH; }
 
-// Workspace of i8mm_forward: mask, idx, n_out, Xq, c_x, X_O, each 256-byte aligned.
-void forward_layout(int64_t s, int64_t h, size_t off[6], int64_t* ldo, size_t* total) {
+// Workspace of i8mm_forward: the mask accumulator (fixed size, so that its
+// place does not depend on the shape), then mask, idx, n_out, Xq, c_x, X_O;
+// each 256-byte aligned.
+constexpr size_t kAccBytes = I8MM_FORWARD_ACC_BYTES;
+void forward_layout(int64_t s, int64_t h, size_t off[7], int64_t* ldo, size_t* total) {
     const int64_t nw = (h + 31) / 32;
     const int64_t l = round_up(h, 32);
     size_t cur = 0;
@@ -66,12 +69,13 @@ void forward_layout(int64_t s, int64_t h, size_t off[6], int64_t* ldo, size_t* t
         cur += static_cast<size_t>(round_up(static_cast<int64_t>(bytes), 256));
         return at;
     };
-    off[0] = take(4 * nw);
-    off[1] = take(4 * h);
-    off[2] = take(4);
-    off[3] = take(static_cast<size_t>(s) * h);
-    off[4] = take(4 * s);
-    off[5] = take(2 * static_cast<size_t>(s) * l);
+    off[0] = take(kAccBytes);
+    off[1] = take(4 * nw);
+    off[2] = take(4 * h);
+    off[3] = take(4);
+    off[4] = take(static_cast<size_t>(s) * h);
+    off[5] = take(4 * s);
+    off[6] = take(2 * static_cast<size_t>(s) * l);
     *ldo = l;
     *total = cur;
 }
@@ -165,13 +169,13 @@ i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq_t, int64_t s, 
 
 size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h) {
     if (!valid_shape_sh(s, h)) return 0;
-    size_t off[6], total;
+    size_t off[7], total;
     int64_t ldo;
     forward_layout(s, h, off, &ldo, &total);
     return total;
 }
 
-i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[6], int64_t* ldo) {
+i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[7], int64_t* ldo) {
     if (!offsets || !ldo || !valid_shape_sh(s, h)) return I8MM_EINVAL;
     size_t total;
     forward_layout(s, h, offsets, ldo, &total);
@@ -188,22 +192,23 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
     if (!aligned16(X) || !aligned16(Wq_t) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
         return I8MM_EINVAL;
     if (i8mm_status d = check_device()) return d;
-    size_t off[6], total;
+    size_t off[7], total;
     int64_t ldo;
     forward_layout(s, h, off, &ldo, &total);
     char* ws = static_cast<char*>(workspace);
-    uint32_t* mask = reinterpret_cast<uint32_t*>(ws + off[0]);
-    int32_t* idx = reinterpret_cast<int32_t*>(ws + off[1]);
-    int32_t* n_out = reinterpret_cast<int32_t*>(ws + off[2]);
-    int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[3]);
-    float* c_x = reinterpret_cast<float*>(ws + off[4]);
-    uint16_t* X_O = reinterpret_cast<uint16_t*>(ws + off[5]);
-    hipError_t e = i8mm::launch_detect(X, s, h, alpha, mask, idx, n_out, stream);
-    if (e != hipSuccess) return I8MM_ELAUNCH;
-    e = i8mm::launch_quantize_rows(X, s, h, mask, idx, n_out, Xq, c_x, X_O, ldo, stream);
+    uint32_t* acc = reinterpret_cast<uint32_t*>(ws + off[0]);
+    uint32_t* mask = reinterpret_cast<uint32_t*>(ws + off[1]);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + off[2]);
+    int32_t* n_out = reinterpret_cast<int32_t*>(ws + off[3]);
+    int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[4]);
+    float* c_x = reinterpret_cast<float*>(ws + off[5]);
+    uint16_t* X_O = reinterpret_cast<uint16_t*>(ws + off[6]);
+    bool acc_used = false;
+    hipError_t e = i8mm::launch_forward_prologue(X, s, h, alpha, acc, mask, idx, n_out, Xq, c_x, X_O, ldo, stream,
+                                                 &acc_used);
     if (e != hipSuccess) return I8MM_ELAUNCH;
     e = i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W, s, h, o, C,
-                               stream);
+                               stream, acc_used ? acc : nullptr, acc_used ? static_cast<int>((h + 31) / 32) : 0);
     return launched(e);
 }
 

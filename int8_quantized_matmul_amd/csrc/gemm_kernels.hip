@@ -129,8 +129,11 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     const float* __restrict__ c_x, const float* __restrict__ c_w,
                     const uint16_t* __restrict__ X_O, int64_t ldo,
                     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out,
-                    const uint16_t* __restrict__ W, void* __restrict__ Cout) {
+                    const uint16_t* __restrict__ W, void* __restrict__ Cout,
+                    uint32_t* __restrict__ clear, int clear_words) {
     __shared__ v4i lds[2 * kStage];
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
 
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int wo = wid & 1, ws = wid >> 1;
@@ -446,22 +449,24 @@ __device__ __forceinline__ v4f outlier_tile_16x16(v4f f, int lane, int64_t ocol0
     return f;
 }
 
-constexpr int kDecodeU = 4;        // K steps of 64 per register batch
-constexpr int kDecodeSplit = 4;    // wavefronts of a block splitting K
 
-// Decode: block = 4 wavefronts on the same 16*NT output columns, each
-// streaming one quarter of K from HBM with two register batches in flight
-// (range-checked loads: steps past a wave's range read as zero), then an
-// exact int32 reduction of the four partial tiles through LDS.
-template <GemmOut MODE, int NT>
+// Decode: block = kDecodeSplit (4) wavefronts on the same 16*NT output
+// columns, each streaming its share of K from HBM with two register batches
+// of kDecodeU K steps in flight (range-checked loads: steps past a wave's
+// range read as zero), then an exact int32 reduction of the partial tiles
+// through LDS.
+template <GemmOut MODE, int NT, int kDecodeU = 4, int kDecodeSplit = 4>
 __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq_t,
                                                      int64_t s, int64_t h, int64_t o,
                                                      const float* __restrict__ c_x, const float* __restrict__ c_w,
                                                      const uint16_t* __restrict__ X_O, int64_t ldo,
                                                      const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ n_out,
-                                                     const uint16_t* __restrict__ W, void* __restrict__ Cout) {
+                                                     const uint16_t* __restrict__ W, void* __restrict__ Cout,
+                                                     uint32_t* __restrict__ clear, int clear_words) {
     __shared__ v4i red[kDecodeSplit][NT][64];
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int64_t obase = static_cast<int64_t>(blockIdx.x) * 16 * NT;
     const int r16 = lane & 15, g = lane >> 4;
@@ -575,15 +580,16 @@ __global__ __launch_bounds__(256) void k_outlier_only(const uint16_t* __restrict
 template <GemmOut MODE>
 hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, int64_t ldo,
                        const int32_t* idx, const int32_t* n_out, const int8_t* Wq_t, const float* c_w,
-                       const uint16_t* W, int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream) {
+                       const uint16_t* W, int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
+                       uint32_t* clear, int clear_words) {
     if (s <= 16) {
         constexpr int NT = 2;
         hipLaunchKernelGGL((k_gemm_decode<MODE, NT>), dim3(static_cast<unsigned>(o / (16 * NT))), dim3(256), 0,
-                           stream, Xq, Wq_t, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C);
+                           stream, Xq, Wq_t, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C, clear, clear_words);
     } else {
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
         hipLaunchKernelGGL((k_gemm_prefill<MODE>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
-                           Xq, Wq_t, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C);
+                           Xq, Wq_t, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C, clear, clear_words);
     }
     return hipGetLastError();
 }
@@ -594,10 +600,13 @@ hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                             const uint16_t* X_O, int64_t ldo,
                             const int32_t* idx, const int32_t* n_out,
                             const int8_t* Wq_t, const float* c_w, const uint16_t* W,
-                            int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream) {
+                            int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
+                            uint32_t* clear, int clear_words) {
     if (mode == GemmOut::Int32)
-        return launch_mode<GemmOut::Int32>(Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W, s, h, o, C, stream);
-    return launch_mode<GemmOut::Mixed>(Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W, s, h, o, C, stream);
+        return launch_mode<GemmOut::Int32>(Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W, s, h, o, C, stream,
+                                           clear, clear_words);
+    return launch_mode<GemmOut::Mixed>(Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W, s, h, o, C, stream,
+                                       clear, clear_words);
 }
 
 hipError_t launch_outlier_matmul(const uint16_t* X_O, int64_t ldo, const int32_t* idx, const int32_t* n_out,

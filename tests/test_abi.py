@@ -81,15 +81,17 @@ def test_forward_workspace_layout():
     lib = _lib()
     for s, h in [(1, 64), (16, 256), (2048, 4096), (4096, 12288), (3, 133120)]:
         total = lib.i8mm_forward_workspace_bytes(s, h)
-        offs = (ctypes.c_size_t * 6)()
+        offs = (ctypes.c_size_t * 7)()
         ldo = ctypes.c_int64()
         assert lib.i8mm_forward_workspace_layout(s, h, offs, ctypes.byref(ldo)) == 0
         assert ldo.value == (h + 31) // 32 * 32
-        sizes = [4 * ((h + 31) // 32), 4 * h, 4, s * h, 4 * s, 2 * s * ldo.value]
-        for i in range(6):
+        assert offs[0] == 0   # the accumulator sits first, whatever the shape
+        sizes = [16640, 4 * ((h + 31) // 32), 4 * h, 4, s * h, 4 * s, 2 * s * ldo.value]
+        assert 16640 >= 4 * (133120 // 32)
+        for i in range(7):
             assert offs[i] % 256 == 0
             end = offs[i] + sizes[i]
-            assert end <= (offs[i + 1] if i < 5 else total)
+            assert end <= (offs[i + 1] if i < 6 else total)
     assert lib.i8mm_forward_workspace_bytes(0, 64) == 0
     assert lib.i8mm_forward_workspace_bytes(4, 96) == 0
 

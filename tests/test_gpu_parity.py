@@ -157,6 +157,57 @@ def test_forward_matches_separate_calls_and_is_deterministic():
     assert torch.equal(v["Xq"], g["Xq"]) and torch.equal(v["c_x"], g["c_x"])
 
 
+# Forward paths: s * ceil(h / 8192) <= 16 (h <= 16384) runs the single-block
+# fused prologue, other inputs the accumulator path (detect -> quantise with ranks
+# -> product); (70, 768) once overran the small path's 16-row tables.
+FWD = [(70, 768, 640, 6, 6.0), (16, 8192, 256, 7, 6.0), (17, 8192, 256, 7, 6.0), (300, 640, 576, 5, 6.0),
+       (8, 16384, 128, 9, 6.0), (9, 12288, 128, 9, 6.0),
+       (40, 128, 192, 0, 0.0), (1100, 128, 192, 0, 0.0), (513, 384, 768, 40, 6.0), (2, 64, 64, 0, 6.0)]
+
+
+@pytest.mark.parametrize("s,h,o,nout,alpha", FWD, ids=[f"s{c[0]}h{c[1]}n{c[3]}a{c[4]}" for c in FWD])
+def test_forward_paths_match_separate_calls(s, h, o, nout, alpha):
+    inp = random_case(70 + s, s, h, o, nout, row_frac=0.5)
+    X, W = inp["X"], inp["W"]
+    Xd, Wd = T(X), T(W)
+    Wq_t, c_w = i8.quantize_colwise_weights(Wd)
+    ws = i8.forward_workspace(s, h, DEV)
+    say(f"  launch: forward s={s} h={h} o={o} alpha={alpha}")
+    C1 = i8.forward(Xd, Wq_t, c_w, Wd, alpha, workspace=ws)
+    torch.cuda.synchronize()
+    v = {k: t.clone() for k, t in i8.forward_workspace_views(ws, s, h).items()}
+    assert not v["acc"].any(), "mask accumulator not returned to zero"
+    g = _run_all(X, W, alpha)
+    n = int(H(g["n_out"])[0])
+    assert int(H(v["n_out"])[0]) == n
+    assert torch.equal(v["mask"], g["mask"]) and torch.equal(v["idx"][:n], g["idx"][:n])
+    assert torch.equal(v["Xq"], g["Xq"]) and torch.equal(v["c_x"], g["c_x"])
+    npad = round_up(n, 32)
+    assert torch.equal(v["X_O"][:, :npad], g["X_O"][:, :npad])
+    assert torch.equal(C1, g["C"])
+    _check_all(X, W, alpha, dict(g, mask=v["mask"], idx=v["idx"], n_out=v["n_out"], Xq=v["Xq"], c_x=v["c_x"],
+                                 X_O=v["X_O"], C=C1))
+    C2 = i8.forward(Xd, Wq_t, c_w, Wd, alpha, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+
+
+def test_forward_workspace_reuse_across_shapes():
+    """One workspace, shapes alternating between the two prologue paths."""
+    big = i8.forward_workspace(1100, 640, DEV)
+    for (s, h, o, nout) in [(1100, 640, 256, 5), (8, 640, 256, 3), (600, 640, 320, 9), (8, 640, 256, 3)]:
+        inp = random_case(90 + s + nout, s, h, o, nout, row_frac=0.5)
+        X, W = inp["X"], inp["W"]
+        Xd, Wd = T(X), T(W)
+        Wq_t, c_w = i8.quantize_colwise_weights(Wd)
+        say(f"  launch: forward reuse s={s} h={h}")
+        C = i8.forward(Xd, Wq_t, c_w, Wd, 6.0, workspace=big)
+        torch.cuda.synchronize()
+        ref = _run_all(X, W, 6.0)
+        assert torch.equal(C, ref["C"])
+        assert not i8.forward_workspace_views(big, s, h)["acc"].any()
+
+
 def test_bad_arguments_raise():
     X = torch.zeros((4, 96), dtype=torch.float16, device=DEV)
     with pytest.raises(i8.I8MMError):
