@@ -67,12 +67,12 @@ def run_prefill(i8, torch, w, steps, warmup, dev):
     torch.cuda.synchronize()
 
     # load-time conversion (timed on its own)
-    Wq_t, c_w = i8.quantize_colwise_weights(W)
+    Wq, c_w = i8.quantize_colwise_weights(W)
     torch.cuda.synchronize()
     e0, e1 = _events(torch)
     e0.record()
     for _ in range(3):
-        i8.quantize_colwise_weights(W, Wq_t, c_w)
+        i8.quantize_colwise_weights(W, Wq, c_w)
     e1.record()
     torch.cuda.synchronize()
     conv_ms = e0.elapsed_time(e1) / 3
@@ -83,7 +83,7 @@ def run_prefill(i8, torch, w, steps, warmup, dev):
 
     def step():
         # one forward: detect -> quantise rows -> decomposed product (one C-ABI call)
-        i8.forward(X, Wq_t, c_w, W, w.alpha, workspace=ws, C=C)
+        i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C)
 
     for _ in range(warmup):
         step()
@@ -98,7 +98,7 @@ def run_prefill(i8, torch, w, steps, warmup, dev):
     wall = time.perf_counter() - wall0
     step_ms = t0.elapsed_time(t1) / steps
     gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
-        v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq_t, c_w, W, C))
+        v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
 
     n_out = int(v["n_out"].cpu()[0])
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out,
@@ -112,22 +112,22 @@ def run_decode(i8, torch, w, steps, warmup, dev):
     W = torch.from_numpy(inp["W"]).to(dev)
     del inp
     s, h, o = w.s, w.h, w.o
-    Wq_t, c_w = i8.quantize_colwise_weights(W)
+    Wq, c_w = i8.quantize_colwise_weights(W)
     ws = i8.forward_workspace(s, h, dev)
     v = i8.forward_workspace_views(ws, s, h)
     C = torch.empty((s, o), dtype=torch.float16, device=dev)
     for _ in range(warmup):
-        i8.forward(X, Wq_t, c_w, W, w.alpha, workspace=ws, C=C)
+        i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C)
     torch.cuda.synchronize()
     t0, t1 = _events(torch)
     t0.record()
     for _ in range(steps):
-        i8.forward(X, Wq_t, c_w, W, w.alpha, workspace=ws, C=C)
+        i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C)
     t1.record()
     torch.cuda.synchronize()
     step_ms = t0.elapsed_time(t1) / steps
     gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
-        v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq_t, c_w, W, C))
+        v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
     n_out = int(v["n_out"].cpu()[0])
     weight_bytes = h * o + 2 * n_out * o + 4 * o
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes)

@@ -25,9 +25,14 @@
  *     except X_O, whose row stride is the explicit argument ldo.
  *   - Every pointer must be 16-byte aligned.
  *   - Shape limits: s >= 1; h and o multiples of 64; h <= 133120 (so an
- *     int32 accumulator cannot overflow: h * 127^2 < 2^31); for the fused
- *     product (i8mm_int8_mixed_matmul, i8mm_forward) also h * o < 2^31
- *     (W is addressed with 32-bit byte offsets).
+ *     int32 accumulator cannot overflow: h * 127^2 < 2^31); for the
+ *     products (i8mm_int8_mixed_matmul, i8mm_int8_gemm_i32, i8mm_forward)
+ *     also h * o < 2^31 (Wq and W are addressed with 32-bit byte offsets).
+ *   - Quantised weights use the PANEL layout Wq [h / 64][o][64]: the code
+ *     W_i8[k, j] is the byte at offset (k / 64) * o * 64 + j * 64 + k % 64.
+ *     Panel p holds rows 64 p .. 64 p + 63 of W_i8 with each column's 64
+ *     codes contiguous, so 16 columns of one panel (the A operand of one
+ *     int8 matrix-core instruction) are one contiguous KiB.
  *   - Work is enqueued on `stream` (NULL = the default stream); calls return
  *     without synchronising. Arguments are validated on the host before any
  *     work is enqueued: an invalid call enqueues nothing. Faults of the
@@ -38,6 +43,9 @@
  *   - Scales are fp32: c = fl32(127 / m) (IEEE division, round to nearest
  *     even), c = 1 when m == 0. Quantisation is v = fl32(x * c) rounded half
  *     away from zero, in [-127, 127].
+ *   - X may hold +-inf (always an outlier: |x| >= alpha for every accepted
+ *     alpha); a NaN is never an outlier, and a NaN among a row's
+ *     non-outlier values leaves that row's scale and codes unspecified.
  */
 #ifndef I8MM_H
 #define I8MM_H
@@ -61,7 +69,7 @@ typedef enum {
 #define I8MM_MAX_H 133120
 
 /*
- * Load-time weight conversion: W fp16 [h, o] -> Wq_t int8 [o, h] and c_w fp32 [o].
+ * Load-time weight conversion: W fp16 [h, o] -> Wq int8 (panel layout) and c_w fp32 [o].
  *
  * [DIGEST] "The Full LLM.int8() Algorithm", Step 4, second and third
  * bullets (c_w_j = 127 / max_i |W_ij|, W_i8 = round(W (.) c_w)), and "Why
@@ -70,12 +78,11 @@ typedef enum {
  * The max runs over all h rows of W, so the conversion does not depend on
  * the per-forward outlier set.
  *
- * Wq_t is W_i8 TRANSPOSED: row j of Wq_t holds column j of W_i8, so the
- * reduction dimension h is contiguous for both operands of the product.
- * W: [h, o] fp16 (read). Wq_t: [o, h] int8 (written). c_w: [o] fp32 (written).
+ * W: [h, o] fp16 (read). Wq: h * o bytes (written), W_i8 in the panel
+ * layout described above. c_w: [o] fp32 (written).
  */
 i8mm_status i8mm_quantize_colwise_weights(const uint16_t* W, int64_t h, int64_t o,
-                                          int8_t* Wq_t, float* c_w, hipStream_t stream);
+                                          int8_t* Wq, float* c_w, hipStream_t stream);
 
 /*
  * Outlier-column detection: O = { j in [0, h) : max_i |X_ij| >= alpha }.
@@ -107,8 +114,11 @@ i8mm_status i8mm_detect_outlier_cols(const uint16_t* X, int64_t s, int64_t h, fl
  * [TM] "Absmax INT8 quantization from first principles" and "Vector-wise:
  * a scale per row and per column".
  *
- * X: [s, h] fp16 (read). mask, idx, n_out: as written by
- * i8mm_detect_outlier_cols (read on the device).
+ * X: [s, h] fp16 (read). mask: as written by i8mm_detect_outlier_cols (read
+ * on the device); it alone defines O: the column of rank k in O (its k-th
+ * member in ascending order) goes to X_O[:, k]. idx and n_out must be the
+ * matching outputs of the same detection call; they are validated like the
+ * other pointers but not read.
  * Xq: [s, h] int8 (written): quantised X with the columns in O set to 0.
  * c_x: [s] fp32 (written).
  * X_O: [s, ldo] fp16 (written): X_O[i, k] = X[i, idx[k]] for k < |O|, and 0
@@ -130,21 +140,21 @@ i8mm_status i8mm_quantize_rowwise(const uint16_t* X, int64_t s, int64_t h,
  * Full LLM.int8() Algorithm", Steps 3-5; [PY] "第二件武器：混合精度分解"
  * (decomposition equation); [TM] "The mixed-precision decomposition".
  *
- * C_i32 = Xq Wq_t^T is exact (int8 MFMA, int32 accumulate). The dequantised
+ * C_i32 = Xq W_i8 is exact (int8 MFMA, int32 accumulate). The dequantised
  * value and the fp16 outlier product (fp16 MFMA, fp32 accumulate) are summed
  * in fp32 and rounded once to fp16 (round to nearest even). S is never
  * materialised. n_out is read on the device; only rows idx[0 .. n_out) of W
  * are read.
  *
  * Xq: [s, h] int8; c_x: [s] fp32; X_O: [s, ldo] fp16 (ldo as above);
- * idx, n_out: as from i8mm_detect_outlier_cols; Wq_t: [o, h] int8;
+ * idx, n_out: as from i8mm_detect_outlier_cols; Wq: panel layout (above);
  * c_w: [o] fp32; W: [h, o] fp16 (the original weights);
  * C: [s, o] fp16 (written).
  */
 i8mm_status i8mm_int8_mixed_matmul(const int8_t* Xq, const float* c_x,
                                    const uint16_t* X_O, int64_t ldo,
                                    const int32_t* idx, const int32_t* n_out,
-                                   const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                                   const int8_t* Wq, const float* c_w, const uint16_t* W,
                                    int64_t s, int64_t h, int64_t o, uint16_t* C,
                                    hipStream_t stream);
 
@@ -162,17 +172,20 @@ i8mm_status i8mm_outlier_matmul(const uint16_t* X_O, int64_t ldo,
                                 float* C_O, hipStream_t stream);
 
 /*
- * The int8 product alone: C_i32 int32 [s, o] = Xq Wq_t^T, exact.
+ * The int8 product alone: C_i32 int32 [s, o] = Xq W_i8, exact (Wq in the
+ * panel layout).
  *
  * [DIGEST] "The Full LLM.int8() Algorithm", Step 4, fourth bullet (Int8
  * matrix multiplication producing an Int32 accumulator). Runs the same
  * main loop as i8mm_int8_mixed_matmul with a plain int32 store.
  */
-i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq_t,
+i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq,
                                int64_t s, int64_t h, int64_t o, int32_t* C_i32,
                                hipStream_t stream);
 
-/* Bytes at the start of the forward workspace that hold the mask accumulator. */
+/* Bytes at the start of the forward workspace that hold the cross-block
+ * accumulator of the detection (the outlier mask being ORed together, or,
+ * for inputs of at most 64 rows, the per-row maxima). */
 #define I8MM_FORWARD_ACC_BYTES 16640
 
 /*
@@ -185,21 +198,21 @@ size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h);
 /*
  * The whole per-forward path for one linear layer ([DIGEST] "The Full
  * LLM.int8() Algorithm", Steps 1-5): detect, quantise rows and gather,
- * decomposed product, in two or three kernel launches. Weights must already
+ * decomposed product, in three kernel launches. Weights must already
  * be converted by i8mm_quantize_colwise_weights.
  *
  * workspace: caller-owned device buffer of i8mm_forward_workspace_bytes(s, h)
  * bytes, 256-byte aligned. Its first I8MM_FORWARD_ACC_BYTES bytes (the
- * detection's mask accumulator) must be ZERO before the first call, e.g. by
+ * detection's accumulator) must be ZERO before the first call, e.g. by
  * allocating it zero-filled; every i8mm_forward returns them to zero, so a
  * workspace may be reused for any shape whose size fits. Calls that share a
  * workspace must not overlap. After completion the workspace holds the
  * intermediates at the offsets given by i8mm_forward_workspace_layout.
- * X: [s, h] fp16; Wq_t: [o, h] int8; c_w: [o] fp32; W: [h, o] fp16;
+ * X: [s, h] fp16; Wq: panel layout (above); c_w: [o] fp32; W: [h, o] fp16;
  * C: [s, o] fp16 (written).
  */
 i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
-                         const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                         const int8_t* Wq, const float* c_w, const uint16_t* W,
                          void* workspace, uint16_t* C, hipStream_t stream);
 
 /*

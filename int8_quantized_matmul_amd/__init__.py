@@ -31,6 +31,8 @@ __all__ = [
     "forward_workspace",
     "forward_workspace_views",
     "x_o_stride",
+    "weight_panels_shape",
+    "panels_to_rows",
     "version",
     "library_path",
     "I8MMError",
@@ -46,6 +48,9 @@ class _LazyLib:
 
 
 _lib = _LazyLib()
+
+# Bytes of the forward workspace's leading accumulator (I8MM_FORWARD_ACC_BYTES).
+ACC_BYTES = _native.header_define("I8MM_FORWARD_ACC_BYTES")
 
 
 class I8MMError(RuntimeError):
@@ -81,6 +86,22 @@ def x_o_stride(h: int) -> int:
     return (h + 31) // 32 * 32
 
 
+def weight_panels_shape(h: int, o: int) -> Tuple[int, int, int]:
+    """Shape of the quantised weights in the library's panel layout: the code
+    W_i8[k, j] sits at Wq[k // 64, j, k % 64] (h / 64 panels of 64 reduction
+    rows, each column's 64 codes contiguous)."""
+    if h % 64 != 0:
+        raise ValueError(f"h must be a multiple of 64 (got {h})")
+    return (h // 64, o, 64)
+
+
+def panels_to_rows(Wq: torch.Tensor) -> torch.Tensor:
+    """The codes of a panel-layout Wq as W_i8 transposed, [o, h] (a copy, for
+    inspection and tests; the products read the panel layout directly)."""
+    p, o, _ = Wq.shape
+    return Wq.permute(1, 0, 2).reshape(o, p * 64)
+
+
 def version() -> str:
     return _lib.i8mm_version().decode()
 
@@ -89,19 +110,21 @@ def library_path() -> str:
     return _native.loaded_path()
 
 
-def quantize_colwise_weights(W: torch.Tensor, Wq_t: Optional[torch.Tensor] = None,
+def quantize_colwise_weights(W: torch.Tensor, Wq: Optional[torch.Tensor] = None,
                              c_w: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Load-time conversion: W fp16 [h, o] -> (Wq_t int8 [o, h], c_w fp32 [o])."""
+    """Load-time conversion: W fp16 [h, o] -> (Wq int8 [h/64, o, 64] panel
+    layout, c_w fp32 [o])."""
     h, o = W.shape
-    if Wq_t is None:
-        Wq_t = torch.empty((o, h), dtype=torch.int8, device=W.device)
+    shape = weight_panels_shape(h, o)
+    if Wq is None:
+        Wq = torch.empty(shape, dtype=torch.int8, device=W.device)
     if c_w is None:
         c_w = torch.empty((o,), dtype=torch.float32, device=W.device)
     st = _lib.i8mm_quantize_colwise_weights(
-        _dev(W, "W", torch.float16), h, o, _dev(Wq_t, "Wq_t", torch.int8, (o, h)),
+        _dev(W, "W", torch.float16), h, o, _dev(Wq, "Wq", torch.int8, shape),
         _dev(c_w, "c_w", torch.float32, (o,)), _stream(W))
     _check(st, "quantize_colwise_weights")
-    return Wq_t, c_w
+    return Wq, c_w
 
 
 def detect_outlier_cols(X: torch.Tensor, alpha: float = 6.0, mask: Optional[torch.Tensor] = None,
@@ -149,17 +172,17 @@ def quantize_rowwise(X: torch.Tensor, mask: torch.Tensor, idx: torch.Tensor, n_o
 
 
 def int8_mixed_matmul(Xq: torch.Tensor, c_x: torch.Tensor, X_O: torch.Tensor, idx: torch.Tensor,
-                      n_out: torch.Tensor, Wq_t: torch.Tensor, c_w: torch.Tensor, W: torch.Tensor,
+                      n_out: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: torch.Tensor,
                       C: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C fp16 [s, o] = fp16(C_i32 / (c_x ⊗ c_w) + X_O W[idx, :])."""
     s, h = Xq.shape
-    o = Wq_t.shape[0]
+    o = Wq.shape[1]
     if C is None:
         C = torch.empty((s, o), dtype=torch.float16, device=Xq.device)
     st = _lib.i8mm_int8_mixed_matmul(
         _dev(Xq, "Xq", torch.int8), _dev(c_x, "c_x", torch.float32, (s,)),
         _dev(X_O, "X_O", torch.float16), X_O.shape[1], _dev(idx, "idx", torch.int32),
-        _dev(n_out, "n_out", torch.int32, (1,)), _dev(Wq_t, "Wq_t", torch.int8, (o, h)),
+        _dev(n_out, "n_out", torch.int32, (1,)), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)),
         _dev(c_w, "c_w", torch.float32, (o,)), _dev(W, "W", torch.float16, (h, o)),
         s, h, o, _dev(C, "C", torch.float16, (s, o)), _stream(Xq))
     _check(st, "int8_mixed_matmul")
@@ -181,21 +204,21 @@ def outlier_matmul(X_O: torch.Tensor, idx: torch.Tensor, n_out: torch.Tensor, W:
     return C_O
 
 
-def int8_gemm_i32(Xq: torch.Tensor, Wq_t: torch.Tensor, C: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """C_i32 int32 [s, o] = Xq Wq_t^T exactly (same main loop as the mixed product)."""
+def int8_gemm_i32(Xq: torch.Tensor, Wq: torch.Tensor, C: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C_i32 int32 [s, o] = Xq W_i8 exactly (same main loop as the mixed product)."""
     s, h = Xq.shape
-    o = Wq_t.shape[0]
+    o = Wq.shape[1]
     if C is None:
         C = torch.empty((s, o), dtype=torch.int32, device=Xq.device)
     st = _lib.i8mm_int8_gemm_i32(
-        _dev(Xq, "Xq", torch.int8), _dev(Wq_t, "Wq_t", torch.int8, (o, h)), s, h, o,
+        _dev(Xq, "Xq", torch.int8), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)), s, h, o,
         _dev(C, "C", torch.int32, (s, o)), _stream(Xq))
     _check(st, "int8_gemm_i32")
     return C
 
 
 def forward_workspace(s: int, h: int, device) -> torch.Tensor:
-    """A zero-filled device workspace (uint8) for forward(). Its leading mask
+    """A zero-filled device workspace (uint8) for forward(). Its leading
     accumulator must start at zero; forward() leaves it zero again."""
     n = _lib.i8mm_forward_workspace_bytes(s, h)
     if n == 0:
@@ -214,8 +237,9 @@ def forward_workspace_views(workspace: torch.Tensor, s: int, h: int) -> Dict[str
     def view(i, nbytes, dtype, shape):
         return workspace[offs[i]:offs[i] + nbytes].view(dtype).view(shape)
 
+    acc_words = ACC_BYTES // 4
     return {
-        "acc": view(0, 4 * nw, torch.int32, (nw,)),
+        "acc": view(0, ACC_BYTES, torch.int32, (acc_words,)),
         "mask": view(1, 4 * nw, torch.int32, (nw,)),
         "idx": view(2, 4 * h, torch.int32, (h,)),
         "n_out": view(3, 4, torch.int32, (1,)),
@@ -225,12 +249,12 @@ def forward_workspace_views(workspace: torch.Tensor, s: int, h: int) -> Dict[str
     }
 
 
-def forward(X: torch.Tensor, Wq_t: torch.Tensor, c_w: torch.Tensor, W: torch.Tensor,
+def forward(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: torch.Tensor,
             alpha: float = 6.0, workspace: Optional[torch.Tensor] = None,
             C: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole per-forward path: detect -> quantise rows -> decomposed product."""
     s, h = X.shape
-    o = Wq_t.shape[0]
+    o = Wq.shape[1]
     if workspace is None:
         workspace = forward_workspace(s, h, X.device)
     if C is None:
@@ -239,7 +263,7 @@ def forward(X: torch.Tensor, Wq_t: torch.Tensor, c_w: torch.Tensor, W: torch.Ten
     if workspace.numel() < need or workspace.dtype != torch.uint8:
         raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
     st = _lib.i8mm_forward(
-        _dev(X, "X", torch.float16), s, h, o, float(alpha), _dev(Wq_t, "Wq_t", torch.int8, (o, h)),
+        _dev(X, "X", torch.float16), s, h, o, float(alpha), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)),
         _dev(c_w, "c_w", torch.float32, (o,)), _dev(W, "W", torch.float16, (h, o)),
         _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
     _check(st, "forward")

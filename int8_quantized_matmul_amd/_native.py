@@ -43,6 +43,15 @@ def header_functions(path: str = HEADER) -> List[str]:
     return sorted(set(re.findall(r"\b(i8mm_[a-z0-9_]+)\s*\(", text)))
 
 
+def header_define(name: str, path: str = HEADER) -> int:
+    """Integer value of a `#define name value` line of include/i8mm.h."""
+    with open(path) as f:
+        m = re.search(r"^#define\s+" + re.escape(name) + r"\s+(\d+)\s*$", f.read(), flags=re.M)
+    if m is None:
+        raise KeyError(name)
+    return int(m.group(1))
+
+
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libi8mm.so; raise if it has not been built (there is no fallback)."""
     global _lib

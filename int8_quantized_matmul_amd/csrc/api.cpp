@@ -30,7 +30,8 @@ bool valid_shape_sh(int64_t s, int64_t h) {
 
 bool valid_o(int64_t o) { return o >= 64 && o % 64 == 0 && o <= (int64_t(1) << 31) - 64; }
 
-// The fused product addresses W and X_O through 32-bit buffer offsets.
+// The products address Wq (h o bytes) and W (2 h o bytes, fused product
+// only) through 32-bit buffer offsets.
 bool valid_w_extent(int64_t h, int64_t o) { return h * o < (int64_t(1) << 31); }
 
 i8mm_status check_device() {
@@ -56,7 +57,7 @@ i8mm_status check_device() {
 
 i8mm_status launched(hipError_t e) { return e == hipSuccess ? I8MM_OK : I8MM_ELAUNCH; }
 
-// Workspace of i8mm_forward: the mask accumulator (fixed size, so that its
+// Workspace of i8mm_forward: the detection accumulator (fixed size, so that its
 // place does not depend on the shape), then mask, idx, n_out, Xq, c_x, X_O;
 // each 256-byte aligned.
 constexpr size_t kAccBytes = I8MM_FORWARD_ACC_BYTES;
@@ -97,12 +98,12 @@ const char* i8mm_status_string(i8mm_status st) {
 }
 
 i8mm_status i8mm_quantize_colwise_weights(const uint16_t* W, int64_t h, int64_t o,
-                                          int8_t* Wq_t, float* c_w, hipStream_t stream) {
-    if (!W || !Wq_t || !c_w) return I8MM_EINVAL;
+                                          int8_t* Wq, float* c_w, hipStream_t stream) {
+    if (!W || !Wq || !c_w) return I8MM_EINVAL;
     if (!valid_shape_sh(1, h) || !valid_o(o)) return I8MM_EINVAL;
-    if (!aligned16(W) || !aligned16(Wq_t) || !aligned16(c_w)) return I8MM_EINVAL;
+    if (!aligned16(W) || !aligned16(Wq) || !aligned16(c_w)) return I8MM_EINVAL;
     if (i8mm_status d = check_device()) return d;
-    return launched(i8mm::launch_quantize_cols(W, h, o, Wq_t, c_w, stream));
+    return launched(i8mm::launch_quantize_cols(W, h, o, Wq, c_w, stream));
 }
 
 i8mm_status i8mm_detect_outlier_cols(const uint16_t* X, int64_t s, int64_t h, float alpha,
@@ -132,16 +133,16 @@ i8mm_status i8mm_quantize_rowwise(const uint16_t* X, int64_t s, int64_t h,
 
 i8mm_status i8mm_int8_mixed_matmul(const int8_t* Xq, const float* c_x, const uint16_t* X_O, int64_t ldo,
                                    const int32_t* idx, const int32_t* n_out,
-                                   const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                                   const int8_t* Wq, const float* c_w, const uint16_t* W,
                                    int64_t s, int64_t h, int64_t o, uint16_t* C, hipStream_t stream) {
-    if (!Xq || !c_x || !X_O || !idx || !n_out || !Wq_t || !c_w || !W || !C) return I8MM_EINVAL;
+    if (!Xq || !c_x || !X_O || !idx || !n_out || !Wq || !c_w || !W || !C) return I8MM_EINVAL;
     if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
     if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
     if (!aligned16(Xq) || !aligned16(c_x) || !aligned16(X_O) || !aligned16(idx) || !aligned16(n_out) ||
-        !aligned16(Wq_t) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
+        !aligned16(Wq) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
         return I8MM_EINVAL;
     if (i8mm_status d = check_device()) return d;
-    return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W,
+    return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W,
                                            s, h, o, C, stream));
 }
 
@@ -157,13 +158,13 @@ i8mm_status i8mm_outlier_matmul(const uint16_t* X_O, int64_t ldo, const int32_t*
     return launched(i8mm::launch_outlier_matmul(X_O, ldo, idx, n_out, W, s, o, C_O, stream));
 }
 
-i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq_t, int64_t s, int64_t h, int64_t o,
+i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t s, int64_t h, int64_t o,
                                int32_t* C_i32, hipStream_t stream) {
-    if (!Xq || !Wq_t || !C_i32) return I8MM_EINVAL;
-    if (!valid_shape_sh(s, h) || !valid_o(o)) return I8MM_EINVAL;
-    if (!aligned16(Xq) || !aligned16(Wq_t) || !aligned16(C_i32)) return I8MM_EINVAL;
+    if (!Xq || !Wq || !C_i32) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
+    if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(C_i32)) return I8MM_EINVAL;
     if (i8mm_status d = check_device()) return d;
-    return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::Int32, Xq, nullptr, nullptr, 0, nullptr, nullptr, Wq_t,
+    return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::Int32, Xq, nullptr, nullptr, 0, nullptr, nullptr, Wq,
                                            nullptr, nullptr, s, h, o, C_i32, stream));
 }
 
@@ -183,13 +184,13 @@ i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[7
 }
 
 i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
-                         const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                         const int8_t* Wq, const float* c_w, const uint16_t* W,
                          void* workspace, uint16_t* C, hipStream_t stream) {
-    if (!X || !Wq_t || !c_w || !W || !workspace || !C) return I8MM_EINVAL;
+    if (!X || !Wq || !c_w || !W || !workspace || !C) return I8MM_EINVAL;
     if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
     if (std::isnan(alpha) || alpha < 0.0f) return I8MM_EINVAL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
-    if (!aligned16(X) || !aligned16(Wq_t) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
         return I8MM_EINVAL;
     if (i8mm_status d = check_device()) return d;
     size_t off[7], total;
@@ -203,12 +204,12 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
     int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[4]);
     float* c_x = reinterpret_cast<float*>(ws + off[5]);
     uint16_t* X_O = reinterpret_cast<uint16_t*>(ws + off[6]);
-    bool acc_used = false;
+    int clear_words = 0;
     hipError_t e = i8mm::launch_forward_prologue(X, s, h, alpha, acc, mask, idx, n_out, Xq, c_x, X_O, ldo, stream,
-                                                 &acc_used);
+                                                 &clear_words);
     if (e != hipSuccess) return I8MM_ELAUNCH;
-    e = i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W, s, h, o, C,
-                               stream, acc_used ? acc : nullptr, acc_used ? static_cast<int>((h + 31) / 32) : 0);
+    e = i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, s, h, o, C,
+                               stream, clear_words > 0 ? acc : nullptr, clear_words);
     return launched(e);
 }
 

@@ -30,11 +30,17 @@ __device__ __forceinline__ float absmax_scale(float m) {
 }
 
 // One fp32 multiply, then round half away from zero, clamped to [-127, 127].
+// Rounding: the float-to-int conversion truncates, and adding the largest
+// float below 1/2 with v's sign first pushes exactly the ties and everything
+// above them past the next integer (checked for every fp32 value of
+// magnitude at most 256). Clamping the sum to [-127.5, 127.5] before the
+// truncation equals clamping the rounded value to [-127, 127]. With
+// c = fl32(127 / m) and |x| <= m, |fl32(x c)| < 127.5, so the clamp never
+// changes a code; it only keeps the conversion in range for other inputs.
 __device__ __forceinline__ int quantize_one(float x, float c) {
-    float v = __fmul_rn(x, c);
-    float r = roundf(v);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return static_cast<int>(r);
+    const float v = __fmul_rn(x, c);
+    const float t = __fadd_rn(v, copysignf(0.49999997f, v));
+    return static_cast<int>(__builtin_amdgcn_fmed3f(t, -127.5f, 127.5f));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

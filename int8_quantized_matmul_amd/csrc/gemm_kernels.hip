@@ -1,5 +1,5 @@
 // The decomposed product of LLM.int8() on gfx950 matrix cores:
-//   C[s, o] = fp16( C_i32 / (c_x (x) c_w) + X_O W[idx, :] ),  C_i32 = Xq Wq_t^T.
+//   C[s, o] = fp16( C_i32 / (c_x (x) c_w) + X_O W[idx, :] ),  C_i32 = Xq W_i8.
 //
 // Page tags: [DIGEST] "LLM.int8(): 8-bit Matrix Multiplication for
 // Transformers at Scale" (paper-graph-ui digest), "The Full LLM.int8()
@@ -7,20 +7,24 @@
 // definition); [PY] "LLM.int8() 完全拆解" (pinghaoyang.com.cn),
 // "第二件武器：混合精度分解".
 //
-// Both operands of the int8 product keep the reduction dimension h
-// contiguous (Xq [s, h], Wq_t [o, h]), so every lane feeds the MFMA from one
-// 16-byte run. The matrix core computes D[o][s] (Wq_t as the A operand), so
-// each lane ends up holding runs of 4 consecutive output columns of one row
-// of C and stores them as one 8-byte fp16 quad.
+// Operand layouts keep the reduction dimension h contiguous in 16-byte runs:
+// Xq is [s, h] row-major, and the weights come in the panel layout
+// Wq [h / 64][o][64] (W_i8[k, j] at (k / 64) o 64 + 64 j + k % 64), in which
+// the A fragment of a 16x16x64 MFMA (16 columns x 64 reduction bytes) is one
+// contiguous KiB and a 256-column tile of one panel is 16 contiguous KiB.
+// The matrix core computes D[o][s] (W_i8 as the A operand), so each lane
+// ends up holding runs of 4 consecutive output columns of one row of C and
+// stores them as one 8-byte fp16 quad.
 //
 // Two main loops share the epilogue structure:
-//  * k_gemm_prefill: 256x256 output tile per 256-thread block, K step 128,
-//    LDS double buffering with a register-staged global prefetch,
-//    v_mfma_i32_32x32x32_i8, 2x2 waves of 128x128.
+//  * k_gemm_prefill: 256x256 output tile per 256-thread block, K step 128
+//    (two panels), LDS double buffering with a register-staged global
+//    prefetch, v_mfma_i32_32x32x32_i8, 2x2 waves of 128x128.
 //  * k_gemm_decode (s <= 16): weight streaming. Four wavefronts per 16*NT
-//    output columns split K and read their rows of Wq_t straight from HBM
-//    into the MFMA operand registers (v_mfma_i32_16x16x64_i8, rows of X
-//    beyond s read as zero), two register batches in flight.
+//    output columns split K and read their panels of Wq straight from HBM
+//    into the MFMA operand registers with non-temporal loads
+//    (v_mfma_i32_16x16x64_i8, rows of X beyond s read as zero), two
+//    register batches in flight.
 // The fused epilogue converts the int32 accumulator to fp32, multiplies by
 // 1/c_x_i * 1/c_w_j (S is never materialised), then accumulates the fp16
 // outlier product on top with fp16 MFMA (fp32 accumulate) and rounds once
@@ -57,12 +61,22 @@ __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t vof
     return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// Same, marked non-temporal (streamed data that no other block re-reads).
+__device__ __forceinline__ v4i buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
+
+// Bytes from byte `from` to the end of an array of `total` bytes (0 past it).
+__device__ __forceinline__ uint32_t bytes_left(int64_t total, int64_t from) {
+    return static_cast<uint32_t>(from < total ? total - from : 0);
+}
+
 constexpr uint32_t kOutOfRange = 0x80000000u;   // a per-lane offset past every buffer
 
 // Block -> output tile. Blocks are dealt to the 8 XCDs round robin
 // (block b runs on XCD b % 8); each XCD is given one contiguous run of the
-// s-fastest tile order so that the tiles sharing rows of Wq_t and Xq meet
-// in the same 4 MiB L2.
+// s-fastest tile order so that the tiles sharing weight columns and rows of
+// Xq meet in the same 4 MiB L2.
 __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t nb) {
     const int64_t q = nb / 8, r = nb % 8, x = b % 8, i = b / 8;
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
@@ -124,7 +138,7 @@ constexpr int kMaxOnceSlices = 5;               // extra slices staged at once
 
 template <GemmOut MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq_t,
+void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
                     int64_t s, int64_t h, int64_t o,
                     const float* __restrict__ c_x, const float* __restrict__ c_w,
                     const uint16_t* __restrict__ X_O, int64_t ldo,
@@ -142,34 +156,46 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     const int64_t ts_i = tile % n_ts, to_i = tile / n_ts;
     const int64_t o0 = to_i * kTO, s0 = ts_i * kTS;
 
-    // Tile-relative buffer resources: rows past o (or s) read as zero.
+    // Tile-relative buffer resources. B: rows past s read as zero. A: one
+    // resource per stage, based at the tile's first column in the stage's
+    // first panel (see gload); rows past o are masked in their offsets, as
+    // in the panel layout the bytes after a panel's last column belong to
+    // the next panel.
     const int64_t o_rows = o - o0 < kTO ? o - o0 : kTO;
     const int64_t s_rows = s - s0 < kTS ? s - s0 : kTS;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq_t + o0 * h, static_cast<uint32_t>(o_rows * h));
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(Xq + s0 * h, static_cast<uint32_t>(s_rows * h));
+    const int64_t wq_bytes = h * o;
 
     // Global -> register staging: thread t moves chunk (t & 7) of rows
-    // (t >> 3) + 32 p, p = 0..7, of both tiles. The row offset travels in
-    // the per-lane offset, which the range check covers, so rows past the
-    // tile read as zero; only the uniform K offset goes in the scalar offset.
+    // (t >> 3) + 32 p, p = 0..7, of both tiles. A stage's chunk c is the
+    // 16-byte piece c % 4 of panel 2 kt + c / 4. Offsets live in the
+    // per-lane part, which the range check covers; for B only the uniform
+    // K offset goes in the scalar offset.
     const int st_c = t & 7, st_r = t >> 3;
-    uint32_t voff[8];
+    uint32_t voffA[8], voffB[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) voff[p] = static_cast<uint32_t>((st_r + 32 * p) * h + st_c * 16);
+    for (int p = 0; p < 8; ++p) {
+        const int row = st_r + 32 * p;
+        voffA[p] = row < o_rows ? static_cast<uint32_t>(row * 64 + (st_c & 3) * 16 + (st_c >> 2) * o * 64)
+                                : kOutOfRange;
+        voffB[p] = static_cast<uint32_t>(row * h + st_c * 16);
+    }
     v4i ra[8], rb[8];
     const int64_t KT = (h + kTK - 1) / kTK;
 
     auto gload = [&](int64_t kt) {
         const uint32_t k = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kt * kTK));
-        // chunks past h (a half stage when h % 128 == 64, or the prefetch
-        // past the last stage) read as zero: their offset gets the top bit
-        // (row offsets stay below 2^31), computed without a branch
+        // The stage's A resource ends with the array, so a missing second
+        // panel (h % 128 == 64) and every stage past the last one lie
+        // outside it; chunks past h also get the top offset bit (row
+        // offsets stay below 2^31), computed without a branch.
+        const int64_t a0 = o0 * 64 + kt * kTK * o;
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq + (a0 < wq_bytes ? a0 : 0), bytes_left(wq_bytes, a0));
         const uint32_t oob = (k + st_c * 16 < static_cast<uint32_t>(h)) ? 0u : kOutOfRange;
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            const uint32_t v = voff[p] | oob;
-            ra[p] = buf_load16(rA, v, k);
-            rb[p] = buf_load16(rB, v, k);
+            ra[p] = buf_load16(rA, voffA[p] | oob, 0);
+            rb[p] = buf_load16(rB, voffB[p] | oob, k);
         }
     };
     auto lstore = [&](int buf) {
@@ -456,7 +482,7 @@ __device__ __forceinline__ v4f outlier_tile_16x16(v4f f, int lane, int64_t ocol0
 // range read as zero), then an exact int32 reduction of the partial tiles
 // through LDS.
 template <GemmOut MODE, int NT, int kDecodeU = 4, int kDecodeSplit = 4>
-__global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq_t,
+__global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
                                                      int64_t s, int64_t h, int64_t o,
                                                      const float* __restrict__ c_x, const float* __restrict__ c_w,
                                                      const uint16_t* __restrict__ X_O, int64_t ldo,
@@ -471,13 +497,15 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     const int64_t obase = static_cast<int64_t>(blockIdx.x) * 16 * NT;
     const int r16 = lane & 15, g = lane >> 4;
 
-    // Wq_t rows obase .. obase + 16 NT - 1 (always inside o: 16 NT divides 64).
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq_t + obase * h, static_cast<uint32_t>(16 * NT * h));
+    // Columns obase .. obase + 16 NT - 1 of every panel (always inside o:
+    // 16 NT divides 64): panel p of them starts p o 64 bytes past the
+    // resource base, a step's uniform offset.
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq + obase * 64, static_cast<uint32_t>(h * o - obase * 64));
     // Xq rows 0 .. s - 1; lanes of rows >= s fall past the range and read zero.
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(Xq, static_cast<uint32_t>(s * h));
     uint32_t vA[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) vA[nt] = static_cast<uint32_t>((nt * 16 + r16) * h + g * 16);
+    for (int nt = 0; nt < NT; ++nt) vA[nt] = static_cast<uint32_t>((nt * 16 + r16) * 64 + g * 16);
     const uint32_t vB = static_cast<uint32_t>(r16 * h + g * 16);
 
     // Wavefronts that finish an output tile fetch the first slice of its
@@ -500,14 +528,17 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
     v4i a0[kDecodeU][NT], b0[kDecodeU], a1[kDecodeU][NT], b1[kDecodeU];
 
+    // Steps past the wave's range get an out-of-range lane offset and a zero
+    // scalar offset, so no sum of the two can wrap back into the range.
     auto load = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU], int64_t stb) {
 #pragma unroll
         for (int u = 0; u < kDecodeU; ++u) {
             const bool ok = stb + u < st1;
-            const uint32_t k = ok ? static_cast<uint32_t>((stb + u) * 64) : 0u;
+            const uint32_t kA = ok ? static_cast<uint32_t>((stb + u) * o * 64) : 0u;
+            const uint32_t kB = ok ? static_cast<uint32_t>((stb + u) * 64) : 0u;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) a[u][nt] = buf_load16(rA, ok ? vA[nt] : kOutOfRange, k);
-            b[u] = buf_load16(rB, ok ? vB : kOutOfRange, k);
+            for (int nt = 0; nt < NT; ++nt) a[u][nt] = buf_load16_nt(rA, ok ? vA[nt] : kOutOfRange, kA);
+            b[u] = buf_load16(rB, ok ? vB : kOutOfRange, kB);
         }
     };
     auto mma = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU]) {
@@ -579,17 +610,17 @@ __global__ __launch_bounds__(256) void k_outlier_only(const uint16_t* __restrict
 
 template <GemmOut MODE>
 hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, int64_t ldo,
-                       const int32_t* idx, const int32_t* n_out, const int8_t* Wq_t, const float* c_w,
+                       const int32_t* idx, const int32_t* n_out, const int8_t* Wq, const float* c_w,
                        const uint16_t* W, int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
                        uint32_t* clear, int clear_words) {
     if (s <= 16) {
         constexpr int NT = 2;
         hipLaunchKernelGGL((k_gemm_decode<MODE, NT>), dim3(static_cast<unsigned>(o / (16 * NT))), dim3(256), 0,
-                           stream, Xq, Wq_t, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C, clear, clear_words);
+                           stream, Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C, clear, clear_words);
     } else {
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
         hipLaunchKernelGGL((k_gemm_prefill<MODE>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
-                           Xq, Wq_t, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C, clear, clear_words);
+                           Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C, clear, clear_words);
     }
     return hipGetLastError();
 }
@@ -599,13 +630,13 @@ hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, 
 hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                             const uint16_t* X_O, int64_t ldo,
                             const int32_t* idx, const int32_t* n_out,
-                            const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                            const int8_t* Wq, const float* c_w, const uint16_t* W,
                             int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
                             uint32_t* clear, int clear_words) {
     if (mode == GemmOut::Int32)
-        return launch_mode<GemmOut::Int32>(Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W, s, h, o, C, stream,
+        return launch_mode<GemmOut::Int32>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, s, h, o, C, stream,
                                            clear, clear_words);
-    return launch_mode<GemmOut::Mixed>(Xq, c_x, X_O, ldo, idx, n_out, Wq_t, c_w, W, s, h, o, C, stream,
+    return launch_mode<GemmOut::Mixed>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, s, h, o, C, stream,
                                        clear, clear_words);
 }
 

@@ -16,27 +16,27 @@ hipError_t launch_quantize_rows(const uint16_t* X, int64_t s, int64_t h,
                                 int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
                                 hipStream_t stream);
 
-// Forward path: detection + compaction + row quantisation. Small inputs use
-// one fused block; otherwise detection ORs into `acc` (which must be zero and
-// which the product kernel clears again, see launch_int8_gemm) and the
-// quantise kernel derives the index list from it. *acc_used tells whether
-// the product launch must clear `acc`.
+// Forward path: detection + index list + row quantisation in two launches.
+// Cross-block state (the mask accumulator, or the row maxima for inputs of
+// at most 64 rows) goes to `acc`, which must be zero on entry;
+// *clear_words is how many of its words the product launch must clear
+// again (see launch_int8_gemm).
 hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, float alpha, uint32_t* acc,
                                    uint32_t* mask, int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x,
-                                   uint16_t* X_O, int64_t ldo, hipStream_t stream, bool* acc_used);
+                                   uint16_t* X_O, int64_t ldo, hipStream_t stream, int* clear_words);
 
 hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
-                                int8_t* Wq_t, float* c_w, hipStream_t stream);
+                                int8_t* Wq, float* c_w, hipStream_t stream);
 
 // mode: product variant of the shared int8 main loop. `clear` (optional):
 // clear_words uint32 words that the first block zeroes (the forward path's
-// mask accumulator, whose readers have finished by then).
+// accumulator, whose readers have finished by then).
 enum class GemmOut { Mixed = 0, Int32 = 1 };
 
 hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                             const uint16_t* X_O, int64_t ldo,
                             const int32_t* idx, const int32_t* n_out,
-                            const int8_t* Wq_t, const float* c_w, const uint16_t* W,
+                            const int8_t* Wq, const float* c_w, const uint16_t* W,
                             int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
                             uint32_t* clear = nullptr, int clear_words = 0);
 

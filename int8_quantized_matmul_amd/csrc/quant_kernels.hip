@@ -1,17 +1,115 @@
 // Bandwidth-bound kernels of the LLM.int8() path for gfx950: outlier-column
-// detection, stream compaction of the outlier set, row-wise absmax
-// quantisation with the outlier gather, and load-time column-wise weight
-// quantisation.
+// detection, the index list of the outlier set, row-wise absmax quantisation
+// with the outlier gather, and load-time column-wise weight quantisation.
 //
 // Page tags: [DIGEST] "LLM.int8(): 8-bit Matrix Multiplication for
 // Transformers at Scale" (paper-graph-ui digest); [TM] transformer-math
 // LLM.int8() tutorial (aicassindra.com).
+//
+// X is read as 16-byte chunks of 8 fp16 values and handled two values per
+// 32-bit word with packed 16-bit integer operations where the result is
+// exact: for non-NaN fp16 values, the bit patterns of |x| (sign bit
+// cleared) order like the values, so maxima and threshold tests run on
+// them directly.
 
 #include "device_common.h"
 #include "launch.h"
 
+#include <cmath>
+
 namespace i8mm {
 namespace {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b) {   // lane-wise, modulo 2^16
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) - __builtin_bit_cast(u16x2, b));
+}
+
+constexpr uint32_t kAbs2 = 0x7fff7fffu;     // clears the sign bits of both fp16 halves
+constexpr uint32_t kInfBits = 0x7c00u;      // +inf; larger |x| patterns are NaN
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// ---------------------------------------------------------------------------
+// Outlier test ([DIGEST] "The Full LLM.int8() Algorithm", Step 1: column j
+// is an outlier iff some |X_ij| >= alpha). With thr = the smallest fp16 bit
+// pattern in [0, inf] whose value is >= alpha, |x| >= alpha holds iff
+// thr <= bits(|x|) <= inf (NaN fails both tests), i.e. iff
+// (bits(|x|) - thr) mod 2^16 <= inf - thr. A column's flag is therefore the
+// running minimum of that difference over the rows, tested once at the end.
+struct Threshold {
+    uint32_t thr2;    // thr in both halves
+    uint32_t span;    // inf - thr
+};
+
+__device__ __forceinline__ void detect_fold(uint4& d, const uint4& v, uint32_t thr2) {
+    d.x = pk_min_u16(d.x, pk_sub_u16(v.x & kAbs2, thr2));
+    d.y = pk_min_u16(d.y, pk_sub_u16(v.y & kAbs2, thr2));
+    d.z = pk_min_u16(d.z, pk_sub_u16(v.z & kAbs2, thr2));
+    d.w = pk_min_u16(d.w, pk_sub_u16(v.w & kAbs2, thr2));
+}
+
+__device__ __forceinline__ uint4 detect_init() { return make_uint4(~0u, ~0u, ~0u, ~0u); }
+
+// Bit e set iff column e of the chunk is flagged.
+__device__ __forceinline__ uint32_t detect_flags(const uint4& d, uint32_t span) {
+    uint32_t f = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f |= (((word_of(d, e >> 1) >> ((e & 1) * 16)) & 0xffffu) <= span ? 1u : 0u) << e;
+    return f;
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk row work ([DIGEST] Step 4; [TM] "Absmax INT8 quantization from
+// first principles").
+
+// The chunk with the values whose bit in `bits` is set replaced by +0.
+__device__ __forceinline__ uint4 chunk_clear(const uint4& v, uint32_t bits) {
+    auto keep = [&](int k) {
+        const uint32_t lo = (bits >> (2 * k)) & 1u ? 0u : 0x0000ffffu;
+        const uint32_t hi = (bits >> (2 * k + 1)) & 1u ? 0u : 0xffff0000u;
+        return lo | hi;
+    };
+    return make_uint4(v.x & keep(0), v.y & keep(1), v.z & keep(2), v.w & keep(3));
+}
+
+// Running packed maximum of the |x| bit patterns of a chunk.
+__device__ __forceinline__ uint32_t chunk_absmax_fold(const uint4& v, uint32_t m2) {
+    return pk_max_u16(pk_max_u16(m2, v.x & kAbs2),
+                      pk_max_u16(pk_max_u16(v.y & kAbs2, v.z & kAbs2), v.w & kAbs2));
+}
+
+// The larger of the two halves of a packed maximum, as a float.
+__device__ __forceinline__ float absmax_value(uint32_t m2) {
+    const uint32_t a = m2 & 0xffffu, b = m2 >> 16;
+    return half_bits_to_float(a > b ? a : b);
+}
+
+// The 8 quantised values of a chunk, packed bytewise.
+__device__ __forceinline__ uint2 chunk_quantize(const uint4& v, float sc) {
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int q = quantize_one(half_bits_to_float((word_of(v, e >> 1) >> ((e & 1) * 16)) & 0xffffu), sc);
+        packed[e >> 2] |= (static_cast<uint32_t>(q) & 0xffu) << ((e & 3) * 8);
+    }
+    return make_uint2(packed[0], packed[1]);
+}
+
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
 
 // ---------------------------------------------------------------------------
 // Fill a uint32 array (used to clear the outlier mask before detection; a
@@ -22,63 +120,38 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int6
 }
 
 // ---------------------------------------------------------------------------
-// Outlier-column detection ([DIGEST] "The Full LLM.int8() Algorithm", Step 1).
-//
-// Block = 256 threads covering 2048 columns (8 fp16 = 16 bytes per thread,
-// so one wavefront reads 1 KiB contiguous per row) and `rows` rows. Each
-// thread ORs its 8 per-column flags over its rows in a register; the four
-// threads of a 32-column mask word meet in LDS through atomicOr, and each
-// non-zero word reaches the global mask with one global atomicOr. The mask
-// must be zero beforehand.
-constexpr int kDetectCols = 2048;
+// Outlier-column detection into a mask. One wavefront per (512-column strip,
+// 8-row band): each lane loads its 8 columns of every row of the band at
+// once and folds them into its detection state; the 4 lanes of a mask word
+// combine through shuffles, and a non-zero word reaches the mask with one
+// atomicOr (the mask must be zero beforehand).
+constexpr int kDetBand = 8;
 
 __global__ __launch_bounds__(256) void k_detect(const uint16_t* __restrict__ X, int64_t s, int64_t h,
-                                                float alpha, int rows, int64_t n_col_blocks,
+                                                Threshold th, int64_t n_strips, int64_t n_waves,
                                                 uint32_t* __restrict__ mask) {
-    __shared__ uint32_t lmask[kDetectCols / 32];
-    const int t = threadIdx.x;
-    if (t < kDetectCols / 32) lmask[t] = 0u;
-    __syncthreads();
-
-    const int64_t cb = static_cast<int64_t>(blockIdx.x) % n_col_blocks;
-    const int64_t rb = static_cast<int64_t>(blockIdx.x) / n_col_blocks;
-    const int64_t col0 = cb * kDetectCols + static_cast<int64_t>(t) * 8;
+    const int lane = threadIdx.x & 63;
+    const int64_t wv = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (wv >= n_waves) return;
+    const int64_t strip = wv % n_strips, band = wv / n_strips;
+    const int64_t col = strip * 512 + lane * 8;
+    const int64_t r0 = band * kDetBand;
     uint32_t flags = 0;
-    if (col0 < h) {
-        const int64_t r0 = rb * rows;
-        const int64_t r1 = r0 + rows < s ? r0 + rows : s;
-        const uint16_t* p = X + r0 * h + col0;
-        int64_t r = r0;
-        for (; r + 4 <= r1; r += 4, p += 4 * h) {
-            uint4 v[4];
+    if (col < h) {
+        uint4 v[kDetBand];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(p + u * h);
+        for (int u = 0; u < kDetBand; ++u)
+            if (r0 + u < s) v[u] = load_chunk(X + (r0 + u) * h + col);
+        uint4 d = detect_init();
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x = half_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-                    flags |= (fabsf(x) >= alpha ? 1u : 0u) << e;
-                }
-            }
-        }
-        for (; r < r1; ++r, p += h) {
-            uint4 v = *reinterpret_cast<const uint4*>(p);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = half_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-                flags |= (fabsf(x) >= alpha ? 1u : 0u) << e;
-            }
-        }
+        for (int u = 0; u < kDetBand; ++u)
+            if (r0 + u < s) detect_fold(d, v[u], th.thr2);
+        flags = detect_flags(d, th.span);
     }
-    if (flags) atomicOr(&lmask[t >> 2], flags << ((t & 3) * 8));
-    __syncthreads();
-    if (t < kDetectCols / 32) {
-        uint32_t wbits = lmask[t];
-        if (wbits) atomicOr(&mask[cb * (kDetectCols / 32) + t], wbits);
-    }
+    uint32_t word = flags << ((lane & 3) * 8);
+    word |= __shfl_xor(word, 1, kWave);
+    word |= __shfl_xor(word, 2, kWave);
+    if ((lane & 3) == 0 && word != 0u) atomicOr(&mask[col >> 5], word);
 }
 
 // ---------------------------------------------------------------------------
@@ -118,104 +191,6 @@ __global__ __launch_bounds__(1024) void k_compact(const uint32_t* __restrict__ m
     if (t == 0) n_out[0] = wsum[15];
 }
 
-// Block-wide max of the per-thread partial absmax (256 threads), then the
-// row scale fl32(127 / m).
-__device__ __forceinline__ float block_absmax_scale(float m, float* red, int lane, int wid) {
-    m = wave_max(m);
-    if (lane == 0) red[wid] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    return absmax_scale(m);
-}
-
-// ---------------------------------------------------------------------------
-// Row-wise absmax quantisation over the non-outlier columns plus the gather
-// of the outlier columns ([DIGEST] "The Full LLM.int8() Algorithm", Steps 2
-// and 4; [TM] "Absmax INT8 quantization from first principles").
-//
-// One 256-thread block per row. Each thread owns 8-column chunks
-// c = t, t + 256, ...; with CPT > 0 the row stays in registers between the
-// absmax pass and the quantise pass (CPT chunks per thread), otherwise the
-// second pass re-reads the row (an L2 hit).
-template <int CPT>
-__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ X, int64_t h,
-                                                    const uint32_t* __restrict__ mask,
-                                                    const int32_t* __restrict__ idx,
-                                                    const int32_t* __restrict__ n_out,
-                                                    int8_t* __restrict__ Xq, float* __restrict__ c_x,
-                                                    uint16_t* __restrict__ X_O, int64_t ldo) {
-    __shared__ float red[4];
-    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    const int64_t i = blockIdx.x;
-    const uint16_t* xr = X + i * h;
-    const int64_t nch = h / 8;
-
-    float m = 0.0f;
-    auto absmax_chunk = [&](const uint4& v, int64_t c) {
-        const uint32_t bits = (mask[c >> 2] >> ((c & 3) * 8)) & 0xffu;
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = fabsf(half_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
-            if (!((bits >> e) & 1u)) m = fmaxf(m, x);
-        }
-    };
-    int8_t* qr = Xq + i * h;
-    auto quantize_chunk = [&](const uint4& v, int64_t c, float sc) {
-        const uint32_t bits = (mask[c >> 2] >> ((c & 3) * 8)) & 0xffu;
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = half_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-            int q = ((bits >> e) & 1u) ? 0 : quantize_one(x, sc);
-            packed[e >> 2] |= (static_cast<uint32_t>(q) & 0xffu) << ((e & 3) * 8);
-        }
-        *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(packed[0], packed[1]);
-    };
-
-    if constexpr (CPT > 0) {
-        uint4 cache[CPT];
-#pragma unroll
-        for (int p = 0; p < CPT; ++p) {
-            const int64_t c = t + 256 * p;
-            if (c < nch) cache[p] = *reinterpret_cast<const uint4*>(xr + c * 8);
-        }
-#pragma unroll
-        for (int p = 0; p < CPT; ++p) {
-            const int64_t c = t + 256 * p;
-            if (c < nch) absmax_chunk(cache[p], c);
-        }
-        const float sc = block_absmax_scale(m, red, lane, wid);
-        if (t == 0) c_x[i] = sc;
-#pragma unroll
-        for (int p = 0; p < CPT; ++p) {
-            const int64_t c = t + 256 * p;
-            if (c < nch) quantize_chunk(cache[p], c, sc);
-        }
-    } else {
-        for (int64_t c = t; c < nch; c += 256) absmax_chunk(*reinterpret_cast<const uint4*>(xr + c * 8), c);
-        const float sc = block_absmax_scale(m, red, lane, wid);
-        if (t == 0) c_x[i] = sc;
-        for (int64_t c = t; c < nch; c += 256) quantize_chunk(*reinterpret_cast<const uint4*>(xr + c * 8), c, sc);
-    }
-
-    // Gather X_O[i, k] = X[i, idx[k]], zero-padded to a multiple of 32.
-    const int n = n_out[0];
-    const int npad = (n + 31) & ~31;
-    uint16_t* orow = X_O + i * ldo;
-    for (int k = t; k < npad; k += 256) orow[k] = k < n ? xr[idx[k]] : static_cast<uint16_t>(0);
-}
-
-// ---------------------------------------------------------------------------
-// Forward-path variants. The detection kernel ORs into a mask accumulator
-// (kept zero between forwards; the product kernel clears it again), and the
-// quantise kernel below works from that accumulator directly: the rank of an
-// outlier column j in O is the number of set mask bits below j, so each
-// block writes X_O straight from the registers holding its row, and block 0
-// also emits the mask, the ascending index list and |O|. This replaces the
-// separate clear and compaction launches of the standalone entry points.
-
 // Exclusive prefix sum of the popcounts of mask words [0, nw) into pre[]
 // (LDS), for a block of `nthr` threads; returns |O|.
 __device__ __forceinline__ int block_mask_prefix(const uint32_t* smask, int* pre, int nw, int* wsum, int nthr) {
@@ -250,7 +225,7 @@ __device__ __forceinline__ void emit_outlier_set(const uint32_t* smask, const in
                                                  int32_t* __restrict__ n_out, int nthr) {
     for (int w = threadIdx.x; w < nw; w += nthr) {
         uint32_t bits = smask[w];
-        mask[w] = bits;
+        if (mask) mask[w] = bits;
         int r = pre[w];
         while (bits) {
             idx[r++] = w * 32 + (__ffs(bits) - 1);
@@ -265,221 +240,244 @@ __device__ __forceinline__ int outlier_rank(const uint32_t* smask, const int* pr
     return pre[j >> 5] + __popc(smask[j >> 5] & ((1u << (j & 31)) - 1u));
 }
 
-// One 256-thread block per row (as k_quant_rows), mask from the accumulator.
+// ---------------------------------------------------------------------------
+// Row-wise absmax quantisation over the non-outlier columns plus the gather
+// of the outlier columns ([DIGEST] "The Full LLM.int8() Algorithm", Steps 2
+// and 4; [TM] "Absmax INT8 quantization from first principles").
+//
+// One wavefront per row, four rows per block sharing an LDS copy of the
+// mask (read from `src_mask`) and its prefix counts, so that the rank of an
+// outlier column in O (the number of set mask bits below it) places it in
+// X_O straight from the registers. Lane l owns the 8-column chunks
+// l, l + 64, ...: chunks holding outlier columns first send those values to
+// X_O and replace them by +0, after which the absmax and the quantisation
+// run over whole chunks (a zero neither raises the maximum nor yields a
+// non-zero code). With CPL > 0 the row stays in registers (CPL chunks per
+// lane), otherwise the second pass re-reads it (an L2 hit). If idx is
+// non-null, block 0 also writes the index list and |O| (and the mask to
+// `mask_out` if that is non-null).
 // Dynamic LDS: nw mask words + nw prefix counts.
-template <int CPT>
-__global__ __launch_bounds__(256) void k_quant_rows_acc(const uint16_t* __restrict__ X, int64_t h,
-                                                        const uint32_t* __restrict__ acc,
-                                                        uint32_t* __restrict__ mask, int32_t* __restrict__ idx,
-                                                        int32_t* __restrict__ n_out,
-                                                        int8_t* __restrict__ Xq, float* __restrict__ c_x,
-                                                        uint16_t* __restrict__ X_O, int64_t ldo) {
+template <int CPL>
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ X, int64_t s, int64_t h,
+                                                    const uint32_t* __restrict__ src_mask,
+                                                    uint32_t* __restrict__ mask_out, int32_t* __restrict__ idx,
+                                                    int32_t* __restrict__ n_out,
+                                                    int8_t* __restrict__ Xq, float* __restrict__ c_x,
+                                                    uint16_t* __restrict__ X_O, int64_t ldo) {
     extern __shared__ uint32_t dyn[];
-    __shared__ float red[4];
     __shared__ int wsum[4];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     const int nw = static_cast<int>(h / 32);
     uint32_t* smask = dyn;
     int* pre = reinterpret_cast<int*>(dyn + nw);
-    const int64_t i = blockIdx.x;
-    const uint16_t* xr = X + i * h;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+    const bool live = i < s;
+    const uint16_t* xr = X + (live ? i : 0) * h;
     const int64_t nch = h / 8;
 
-    uint4 cache[CPT > 0 ? CPT : 1];
-    if constexpr (CPT > 0) {
+    uint4 cache[CPL > 0 ? CPL : 1];
+    if constexpr (CPL > 0) {
 #pragma unroll
-        for (int p = 0; p < CPT; ++p) {
-            const int64_t c = t + 256 * p;
-            if (c < nch) cache[p] = *reinterpret_cast<const uint4*>(xr + c * 8);
+        for (int p = 0; p < CPL; ++p) {
+            const int64_t c = lane + 64 * p;
+            if (live && c < nch) cache[p] = load_chunk(xr + c * 8);
         }
     }
-    for (int w = t; w < nw; w += 256) smask[w] = acc[w];
+    for (int w = t; w < nw; w += 256) smask[w] = src_mask[w];
     __syncthreads();
     const int n = block_mask_prefix(smask, pre, nw, wsum, 256);
+    if (blockIdx.x == 0 && idx != nullptr) emit_outlier_set(smask, pre, nw, n, mask_out, idx, n_out, 256);
+    if (!live) return;
 
-    float m = 0.0f;
-    auto chunk_bits = [&](int64_t c) { return (smask[c >> 2] >> ((c & 3) * 8)) & 0xffu; };
-    auto absmax_chunk = [&](const uint4& v, int64_t c) {
-        const uint32_t bits = chunk_bits(c);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = fabsf(half_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
-            if (!((bits >> e) & 1u)) m = fmaxf(m, x);
-        }
-    };
-    int8_t* qr = Xq + i * h;
     uint16_t* orow = X_O + i * ldo;
-    auto quantize_chunk = [&](const uint4& v, int64_t c, float sc) {
-        const uint32_t bits = chunk_bits(c);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t packed[2] = {0u, 0u};
+    auto bits_of = [&](int64_t c) { return (smask[c >> 2] >> ((c & 3) * 8)) & 0xffu; };
+    // Outlier values to X_O; the chunk comes back with them cleared.
+    auto split = [&](const uint4& v, int64_t c) {
+        const uint32_t bits = bits_of(c);
+        if (!bits) return v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t xb = (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-            const bool out = (bits >> e) & 1u;
-            int q = out ? 0 : quantize_one(half_bits_to_float(xb), sc);
-            packed[e >> 2] |= (static_cast<uint32_t>(q) & 0xffu) << ((e & 3) * 8);
-            if (out) orow[outlier_rank(smask, pre, static_cast<int>(c * 8 + e))] = static_cast<uint16_t>(xb);
-        }
-        *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(packed[0], packed[1]);
+        for (int e = 0; e < 8; ++e)
+            if ((bits >> e) & 1u)
+                orow[outlier_rank(smask, pre, static_cast<int>(c * 8 + e))] =
+                    static_cast<uint16_t>(word_of(v, e >> 1) >> ((e & 1) * 16));
+        return chunk_clear(v, bits);
     };
-
-    if constexpr (CPT > 0) {
+    uint32_t m2 = 0;
+    if constexpr (CPL > 0) {
 #pragma unroll
-        for (int p = 0; p < CPT; ++p) {
-            const int64_t c = t + 256 * p;
-            if (c < nch) absmax_chunk(cache[p], c);
-        }
-        const float sc = block_absmax_scale(m, red, lane, wid);
-        if (t == 0) c_x[i] = sc;
-#pragma unroll
-        for (int p = 0; p < CPT; ++p) {
-            const int64_t c = t + 256 * p;
-            if (c < nch) quantize_chunk(cache[p], c, sc);
+        for (int p = 0; p < CPL; ++p) {
+            const int64_t c = lane + 64 * p;
+            if (c < nch) {
+                cache[p] = split(cache[p], c);
+                m2 = chunk_absmax_fold(cache[p], m2);
+            }
         }
     } else {
-        for (int64_t c = t; c < nch; c += 256) absmax_chunk(*reinterpret_cast<const uint4*>(xr + c * 8), c);
-        const float sc = block_absmax_scale(m, red, lane, wid);
-        if (t == 0) c_x[i] = sc;
-        for (int64_t c = t; c < nch; c += 256) quantize_chunk(*reinterpret_cast<const uint4*>(xr + c * 8), c, sc);
+        for (int64_t c = lane; c < nch; c += 64) m2 = chunk_absmax_fold(split(load_chunk(xr + c * 8), c), m2);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m2 = pk_max_u16(m2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2), off, kWave)));
+    const float sc = absmax_scale(absmax_value(m2));
+    if (lane == 0) c_x[i] = sc;
+
+    int8_t* qr = Xq + i * h;
+    if constexpr (CPL > 0) {
+#pragma unroll
+        for (int p = 0; p < CPL; ++p) {
+            const int64_t c = lane + 64 * p;
+            if (c < nch) *reinterpret_cast<uint2*>(qr + c * 8) = chunk_quantize(cache[p], sc);
+        }
+    } else {
+        for (int64_t c = lane; c < nch; c += 64)
+            *reinterpret_cast<uint2*>(qr + c * 8) =
+                chunk_quantize(chunk_clear(load_chunk(xr + c * 8), bits_of(c)), sc);
     }
     const int npad = (n + 31) & ~31;
-    for (int k = n + t; k < npad; k += 256) orow[k] = 0;
-    if (i == 0) emit_outlier_set(smask, pre, nw, n, mask, idx, n_out, 256);
-}
-
-// Small inputs (s <= 16 rows, s * ceil(h / 8192) <= 16): detection,
-// compaction and row quantisation in one 1024-thread block. Thread t owns
-// the 8-column chunks t and t + 1024 of every row and keeps them in
-// registers (at most 16 chunks); column flags are ORed over the rows in a
-// register and meet in an LDS mask through atomicOr, per-row maxima are
-// reduced across each wavefront and combined with an integer atomicMax on
-// the float bits (non-negative floats order like their bit patterns).
-constexpr int kSmallThreads = 1024;
-constexpr int kSmallMaxRows = 16;       // per-row LDS tables below hold 16 rows
-
-template <int CC>   // column chunks per thread (1: h <= 8192, 2: h <= 16384)
-__global__ __launch_bounds__(kSmallThreads) void k_prologue_small(const uint16_t* __restrict__ X, int s, int h,
-                                                                  float alpha, uint32_t* __restrict__ mask,
-                                                                  int32_t* __restrict__ idx,
-                                                                  int32_t* __restrict__ n_out,
-                                                                  int8_t* __restrict__ Xq, float* __restrict__ c_x,
-                                                                  uint16_t* __restrict__ X_O, int64_t ldo) {
-    constexpr int R = kSmallMaxRows / CC;   // rows held per column chunk
-    extern __shared__ uint32_t dyn[];
-    __shared__ int wsum[kSmallThreads / 64];
-    __shared__ uint32_t rmax[kSmallMaxRows];
-    __shared__ float rscale[kSmallMaxRows];
-    if (s > R || h > CC * kSmallThreads * 8) return;   // the launcher never sends these
-    const int t = threadIdx.x, lane = t & 63;
-    const int nw = h / 32;
-    const int nch_row = h / 8;
-    uint32_t* smask = dyn;
-    int* pre = reinterpret_cast<int*>(dyn + nw);
-
-    for (int w = t; w < nw; w += kSmallThreads) smask[w] = 0u;
-    if (t < kSmallMaxRows) rmax[t] = 0u;
-    uint4 v[CC][R];
-#pragma unroll
-    for (int cc = 0; cc < CC; ++cc) {
-        const int c = t + kSmallThreads * cc;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (c < nch_row && r < s) v[cc][r] = *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(r) * h + c * 8);
-    }
-    __syncthreads();
-    // Step 1: column flags, ORed over the rows first.
-#pragma unroll
-    for (int cc = 0; cc < CC; ++cc) {
-        const int c = t + kSmallThreads * cc;
-        uint32_t flags = 0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (c < nch_row && r < s) {
-                const uint32_t w[4] = {v[cc][r].x, v[cc][r].y, v[cc][r].z, v[cc][r].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x = half_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-                    flags |= (fabsf(x) >= alpha ? 1u : 0u) << e;
-                }
-            }
-        }
-        if (flags) atomicOr(&smask[c >> 2], flags << ((c & 3) * 8));
-    }
-    __syncthreads();
-    const int n = block_mask_prefix(smask, pre, nw, wsum, kSmallThreads);
-    // Row absmax over the non-outlier columns.
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (r < s) {
-            float m = 0.0f;
-#pragma unroll
-            for (int cc = 0; cc < CC; ++cc) {
-                const int c = t + kSmallThreads * cc;
-                if (c < nch_row) {
-                    const uint32_t bits = (smask[c >> 2] >> ((c & 3) * 8)) & 0xffu;
-                    const uint32_t w[4] = {v[cc][r].x, v[cc][r].y, v[cc][r].z, v[cc][r].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        float x = fabsf(half_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
-                        if (!((bits >> e) & 1u)) m = fmaxf(m, x);
-                    }
-                }
-            }
-            m = wave_max(m);
-            if (lane == 0 && m > 0.0f) atomicMax(&rmax[r], __float_as_uint(m));
-        }
-    }
-    __syncthreads();
-    if (t < s) {
-        const float sc = absmax_scale(__uint_as_float(rmax[t]));
-        rscale[t] = sc;
-        c_x[t] = sc;
-    }
-    __syncthreads();
-    // Quantise, gather the outlier columns by rank, pad X_O rows.
-#pragma unroll
-    for (int cc = 0; cc < CC; ++cc) {
-        const int c = t + kSmallThreads * cc;
-        if (c < nch_row) {
-            const uint32_t bits = (smask[c >> 2] >> ((c & 3) * 8)) & 0xffu;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (r < s) {
-                    const uint32_t w[4] = {v[cc][r].x, v[cc][r].y, v[cc][r].z, v[cc][r].w};
-                    const float sc = rscale[r];
-                    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t xb = (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                        const bool out = (bits >> e) & 1u;
-                        int qv = out ? 0 : quantize_one(half_bits_to_float(xb), sc);
-                        packed[e >> 2] |= (static_cast<uint32_t>(qv) & 0xffu) << ((e & 3) * 8);
-                        if (out) X_O[r * ldo + outlier_rank(smask, pre, c * 8 + e)] = static_cast<uint16_t>(xb);
-                    }
-                    *reinterpret_cast<uint2*>(Xq + static_cast<int64_t>(r) * h + c * 8) = make_uint2(packed[0], packed[1]);
-                }
-            }
-        }
-    }
-    const int npad = (n + 31) & ~31;
-    for (int r = 0; r < s; ++r)
-        for (int k = n + t; k < npad; k += kSmallThreads) X_O[r * ldo + k] = 0;
-    emit_outlier_set(smask, pre, nw, n, mask, idx, n_out, kSmallThreads);
+    for (int k = n + lane; k < npad; k += 64) orow[k] = 0;
 }
 
 // ---------------------------------------------------------------------------
-// Load-time column-wise quantisation of W [h, o] into Wq_t [o, h]
+// Forward path for few rows (s <= 16 RG): blocks of 256 threads on
+// 128-column slabs, thread t on the 8-column chunk t % 16 of rows
+// t / 16 + 16 g, g < RG. A block of k_small_detect sees every row of its
+// slab, so it writes the slab's mask words itself and folds the per-row
+// maxima over its non-outlier columns into `rowmax` with an integer
+// atomicMax on the float bits (non-negative floats order like their bit
+// patterns); k_small_quant then quantises with the finished row maxima.
+// rowmax must be zero beforehand.
+constexpr int kSlabCols = 128;
+constexpr int kSmallRowsMax = 64;
+
+template <int RG>
+__global__ __launch_bounds__(256) void k_small_detect(const uint16_t* __restrict__ X, int s, int h, Threshold th,
+                                                      uint32_t* __restrict__ mask, uint32_t* __restrict__ rowmax) {
+    __shared__ uint32_t smask[kSlabCols / 32];
+    const int t = threadIdx.x, c = t & 15, r = t >> 4;
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * kSlabCols + c * 8;
+    const bool cok = col < h;
+    if (t < kSlabCols / 32) smask[t] = 0u;
+    uint4 v[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+        v[g] = cok && r + 16 * g < s ? load_chunk(X + static_cast<int64_t>(r + 16 * g) * h + col)
+                                     : make_uint4(0, 0, 0, 0);
+    uint4 d = detect_init();
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+        if (cok && r + 16 * g < s) detect_fold(d, v[g], th.thr2);
+    const uint32_t flags = detect_flags(d, th.span);
+    __syncthreads();
+    if (flags) atomicOr(&smask[c >> 2], flags << ((c & 3) * 8));
+    __syncthreads();
+    const int64_t w0 = static_cast<int64_t>(blockIdx.x) * (kSlabCols / 32);
+    if (t < kSlabCols / 32 && w0 + t < h / 32) mask[w0 + t] = smask[t];
+    const uint32_t bits = (smask[c >> 2] >> ((c & 3) * 8)) & 0xffu;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int row = r + 16 * g;
+        uint32_t m2 = chunk_absmax_fold(chunk_clear(v[g], bits), 0u);
+        // the 16 lanes of one row are lanes 16 k .. 16 k + 15 of the wavefront
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1)
+            m2 = pk_max_u16(m2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2), off, kWave)));
+        const float m = absmax_value(m2);
+        if (c == 0 && row < s && m > 0.0f) atomicMax(&rowmax[row], __float_as_uint(m));
+    }
+}
+
+template <int RG>
+__global__ __launch_bounds__(256) void k_small_quant(const uint16_t* __restrict__ X, int s, int h,
+                                                     const uint32_t* __restrict__ mask,
+                                                     const uint32_t* __restrict__ rowmax,
+                                                     int32_t* __restrict__ idx, int32_t* __restrict__ n_out,
+                                                     int8_t* __restrict__ Xq, float* __restrict__ c_x,
+                                                     uint16_t* __restrict__ X_O, int64_t ldo) {
+    __shared__ int part[2][4];
+    __shared__ float rscale[16 * RG];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6, c = t & 15, r = t >> 4;
+    const int nw = h / 32;
+    const int w0 = static_cast<int>(blockIdx.x) * (kSlabCols / 32);
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * kSlabCols + c * 8;
+    const bool cok = col < h;
+    uint4 v[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+        v[g] = cok && r + 16 * g < s ? load_chunk(X + static_cast<int64_t>(r + 16 * g) * h + col)
+                                     : make_uint4(0, 0, 0, 0);
+    // Outlier columns before this slab and in total.
+    int before = 0, total = 0;
+    for (int w = t; w < nw; w += 256) {
+        const int p = __popc(mask[w]);
+        total += p;
+        before += w < w0 ? p : 0;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        before += __shfl_xor(before, off, kWave);
+        total += __shfl_xor(total, off, kWave);
+    }
+    if (lane == 0) {
+        part[0][wid] = before;
+        part[1][wid] = total;
+    }
+    if (t < s) rscale[t] = absmax_scale(__uint_as_float(rowmax[t]));
+    __syncthreads();
+    before = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+    total = part[1][0] + part[1][1] + part[1][2] + part[1][3];
+
+    // Rank of this chunk's first outlier column: the slab's words below it,
+    // then the bits below it in its own word.
+    const int q = c >> 2;
+    int rank = before;
+    uint32_t word = 0u;
+    for (int j = 0; j <= q; ++j) {
+        word = w0 + j < nw ? mask[w0 + j] : 0u;
+        if (j < q) rank += __popc(word);
+    }
+    rank += __popc(word & ((1u << ((c & 3) * 8)) - 1u));
+    const uint32_t bits = (word >> ((c & 3) * 8)) & 0xffu;
+
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int row = r + 16 * g;
+        if (cok && row < s) {
+            if (bits) {
+                int k = rank;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if ((bits >> e) & 1u)
+                        X_O[row * ldo + k++] = static_cast<uint16_t>(word_of(v[g], e >> 1) >> ((e & 1) * 16));
+            }
+            *reinterpret_cast<uint2*>(Xq + static_cast<int64_t>(row) * h + col) =
+                chunk_quantize(chunk_clear(v[g], bits), rscale[row]);
+        }
+    }
+    if (r == 0 && cok && bits) {
+        int k = rank;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((bits >> e) & 1u) idx[k++] = static_cast<int32_t>(col + e);
+    }
+    if (blockIdx.x == 0) {
+        if (t < s) c_x[t] = rscale[t];
+        if (t == 0) n_out[0] = total;
+        const int pad = ((total + 31) & ~31) - total;
+        for (int e = t; e < s * pad; e += 256) X_O[(e / pad) * ldo + total + e % pad] = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Load-time column-wise quantisation of W [h, o] into the panel layout
+// Wq [h / 64][o][64] (W_i8[k, j] at (k / 64) o 64 + 64 j + k % 64)
 // ([DIGEST] "The Full LLM.int8() Algorithm", Step 4; "Why vector-wise
 // rather than row-wise": constants computed once at load time).
 //
 // One 256-thread block per 64-column strip. Pass 1: per-column absmax over
 // all h rows (thread = 8 columns x every 32nd row; one wavefront reads 8
 // rows x 128 bytes). Pass 2: 64x64 tiles are quantised, transposed through
-// LDS and written as 16-byte runs of Wq_t rows.
+// LDS and written as the strip's contiguous 4 KiB of each panel.
 __global__ __launch_bounds__(256) void k_quant_cols(const uint16_t* __restrict__ W, int64_t h, int64_t o,
-                                                    int8_t* __restrict__ Wq_t, float* __restrict__ c_w) {
+                                                    int8_t* __restrict__ Wq, float* __restrict__ c_w) {
     __shared__ float red[32][65];
     __shared__ float scale[64];
     __shared__ __attribute__((aligned(16))) int8_t tile[64][80];
@@ -524,10 +522,61 @@ __global__ __launch_bounds__(256) void k_quant_cols(const uint16_t* __restrict__
         }
         __syncthreads();
         const int col = t >> 2, seg = t & 3;
-        *reinterpret_cast<uint4*>(Wq_t + (j0 + col) * h + r0 + seg * 16) =
+        *reinterpret_cast<uint4*>(Wq + (r0 / 64) * o * 64 + (j0 + col) * 64 + seg * 16) =
             *reinterpret_cast<const uint4*>(&tile[col][seg * 16]);
         __syncthreads();
     }
+}
+
+}  // namespace
+
+namespace {
+
+// Exact fp16 value of a bit pattern in [0, 0x7c00].
+float half_value(uint32_t b) {
+    const int e = static_cast<int>(b >> 10), m = static_cast<int>(b & 0x3ffu);
+    if (e == 31) return INFINITY;
+    return e == 0 ? std::ldexp(static_cast<float>(m), -24) : std::ldexp(static_cast<float>(m + 1024), e - 25);
+}
+
+// The smallest fp16 bit pattern in [0, inf] whose value is >= alpha (alpha
+// >= 0, not NaN); the values of [0, inf] increase with their patterns.
+Threshold make_threshold(float alpha) {
+    uint32_t lo = 0, hi = kInfBits;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) / 2;
+        if (half_value(mid) >= alpha) hi = mid;
+        else lo = mid + 1;
+    }
+    return Threshold{lo | (lo << 16), kInfBits - lo};
+}
+
+hipError_t launch_detect_into(const uint16_t* X, int64_t s, int64_t h, float alpha, uint32_t* mask,
+                              hipStream_t stream) {
+    const int64_t n_strips = (h + 511) / 512;
+    const int64_t n_waves = n_strips * ((s + kDetBand - 1) / kDetBand);
+    hipLaunchKernelGGL(k_detect, dim3(static_cast<unsigned>((n_waves + 3) / 4)), dim3(256), 0, stream,
+                       X, s, h, make_threshold(alpha), n_strips, n_waves, mask);
+    return hipGetLastError();
+}
+
+hipError_t launch_rows(const uint16_t* X, int64_t s, int64_t h, const uint32_t* src_mask, uint32_t* mask_out,
+                       int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
+                       hipStream_t stream) {
+    const int64_t per_lane = (h / 8 + 63) / 64;
+    const dim3 grid(static_cast<unsigned>((s + 3) / 4)), block(256);
+    const size_t dyn = static_cast<size_t>(2 * (h / 32) * 4);
+#define I8MM_QROWS(CPL)                                                                                     \
+    hipLaunchKernelGGL(k_quant_rows<CPL>, grid, block, dyn, stream, X, s, h, src_mask, mask_out, idx, n_out, \
+                       Xq, c_x, X_O, ldo)
+    if (per_lane <= 2) I8MM_QROWS(2);
+    else if (per_lane <= 4) I8MM_QROWS(4);
+    else if (per_lane <= 8) I8MM_QROWS(8);
+    else if (per_lane <= 16) I8MM_QROWS(16);
+    else if (per_lane <= 32) I8MM_QROWS(32);
+    else I8MM_QROWS(0);
+#undef I8MM_QROWS
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -537,13 +586,8 @@ hipError_t launch_detect(const uint16_t* X, int64_t s, int64_t h, float alpha,
     const int64_t nw = (h + 31) / 32;
     hipLaunchKernelGGL(k_fill_u32, dim3(static_cast<unsigned>((nw + 255) / 256)), dim3(256), 0, stream,
                        mask, nw, 0u);
-    const int64_t n_cb = (h + kDetectCols - 1) / kDetectCols;
-    // Aim for about 2048 blocks; at least 4 rows per thread for load overlap.
-    int64_t rows = (s * n_cb + 2047) / 2048;
-    if (rows < 4) rows = 4;
-    const int64_t n_rb = (s + rows - 1) / rows;
-    hipLaunchKernelGGL(k_detect, dim3(static_cast<unsigned>(n_cb * n_rb)), dim3(256), 0, stream,
-                       X, s, h, alpha, static_cast<int>(rows), n_cb, mask);
+    hipError_t e = launch_detect_into(X, s, h, alpha, mask, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, stream, mask, static_cast<int>(nw), idx, n_out);
     return hipGetLastError();
 }
@@ -552,63 +596,43 @@ hipError_t launch_quantize_rows(const uint16_t* X, int64_t s, int64_t h,
                                 const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
                                 int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
                                 hipStream_t stream) {
-    const int64_t nch = h / 8;
-    const dim3 grid(static_cast<unsigned>(s)), block(256);
-    if (nch <= 256)
-        hipLaunchKernelGGL(k_quant_rows<1>, grid, block, 0, stream, X, h, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    else if (nch <= 512)
-        hipLaunchKernelGGL(k_quant_rows<2>, grid, block, 0, stream, X, h, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    else if (nch <= 1024)
-        hipLaunchKernelGGL(k_quant_rows<4>, grid, block, 0, stream, X, h, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    else if (nch <= 2048)
-        hipLaunchKernelGGL(k_quant_rows<8>, grid, block, 0, stream, X, h, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    else
-        hipLaunchKernelGGL(k_quant_rows<0>, grid, block, 0, stream, X, h, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    return hipGetLastError();
+    // The index list and |O| are re-derived from the mask on the device (the
+    // caller's copies are read-only here and equal by construction).
+    (void)idx;
+    (void)n_out;
+    return launch_rows(X, s, h, mask, nullptr, nullptr, nullptr, Xq, c_x, X_O, ldo, stream);
 }
 
 hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, float alpha, uint32_t* acc,
                                    uint32_t* mask, int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x,
-                                   uint16_t* X_O, int64_t ldo, hipStream_t stream, bool* acc_used) {
-    const int64_t nw = h / 32;
-    const size_t dyn = static_cast<size_t>(2 * nw * 4);
-    const int64_t cc = (h + 8 * kSmallThreads - 1) / (8 * kSmallThreads);   // column chunks per thread
-    if (cc <= 2 && s * cc <= kSmallMaxRows) {
-        *acc_used = false;
-        if (cc == 1)
-            hipLaunchKernelGGL(k_prologue_small<1>, dim3(1), dim3(kSmallThreads), dyn, stream, X, static_cast<int>(s),
-                               static_cast<int>(h), alpha, mask, idx, n_out, Xq, c_x, X_O, ldo);
-        else
-            hipLaunchKernelGGL(k_prologue_small<2>, dim3(1), dim3(kSmallThreads), dyn, stream, X, static_cast<int>(s),
-                               static_cast<int>(h), alpha, mask, idx, n_out, Xq, c_x, X_O, ldo);
+                                   uint16_t* X_O, int64_t ldo, hipStream_t stream, int* clear_words) {
+    if (s <= kSmallRowsMax) {
+        // acc[0 .. s) holds the row maxima.
+        *clear_words = static_cast<int>(s);
+        const dim3 grid(static_cast<unsigned>((h + kSlabCols - 1) / kSlabCols)), block(256);
+        const int si = static_cast<int>(s), hi = static_cast<int>(h);
+        const Threshold th = make_threshold(alpha);
+#define I8MM_SMALL(RG)                                                                                      \
+    hipLaunchKernelGGL(k_small_detect<RG>, grid, block, 0, stream, X, si, hi, th, mask, acc);              \
+    hipLaunchKernelGGL(k_small_quant<RG>, grid, block, 0, stream, X, si, hi, mask, acc, idx, n_out, Xq, c_x, \
+                       X_O, ldo)
+        if (s <= 16) { I8MM_SMALL(1); }
+        else if (s <= 32) { I8MM_SMALL(2); }
+        else { I8MM_SMALL(4); }
+#undef I8MM_SMALL
         return hipGetLastError();
     }
-    *acc_used = true;
-    const int64_t n_cb = (h + kDetectCols - 1) / kDetectCols;
-    int64_t rows = (s * n_cb + 2047) / 2048;
-    if (rows < 4) rows = 4;
-    const int64_t n_rb = (s + rows - 1) / rows;
-    hipLaunchKernelGGL(k_detect, dim3(static_cast<unsigned>(n_cb * n_rb)), dim3(256), 0, stream,
-                       X, s, h, alpha, static_cast<int>(rows), n_cb, acc);
-    const int64_t nch = h / 8;
-    const dim3 grid(static_cast<unsigned>(s)), block(256);
-    if (nch <= 256)
-        hipLaunchKernelGGL(k_quant_rows_acc<1>, grid, block, dyn, stream, X, h, acc, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    else if (nch <= 512)
-        hipLaunchKernelGGL(k_quant_rows_acc<2>, grid, block, dyn, stream, X, h, acc, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    else if (nch <= 1024)
-        hipLaunchKernelGGL(k_quant_rows_acc<4>, grid, block, dyn, stream, X, h, acc, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    else if (nch <= 2048)
-        hipLaunchKernelGGL(k_quant_rows_acc<8>, grid, block, dyn, stream, X, h, acc, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    else
-        hipLaunchKernelGGL(k_quant_rows_acc<0>, grid, block, dyn, stream, X, h, acc, mask, idx, n_out, Xq, c_x, X_O, ldo);
-    return hipGetLastError();
+    // acc[0 .. h / 32) accumulates the mask.
+    *clear_words = static_cast<int>(h / 32);
+    hipError_t e = launch_detect_into(X, s, h, alpha, acc, stream);
+    if (e != hipSuccess) return e;
+    return launch_rows(X, s, h, acc, mask, idx, n_out, Xq, c_x, X_O, ldo, stream);
 }
 
 hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
-                                int8_t* Wq_t, float* c_w, hipStream_t stream) {
+                                int8_t* Wq, float* c_w, hipStream_t stream) {
     hipLaunchKernelGGL(k_quant_cols, dim3(static_cast<unsigned>(o / 64)), dim3(256), 0, stream,
-                       W, h, o, Wq_t, c_w);
+                       W, h, o, Wq, c_w);
     return hipGetLastError();
 }
 

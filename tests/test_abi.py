@@ -68,6 +68,7 @@ def test_mixed_matmul_and_gemm_reject():
     assert lib.i8mm_int8_gemm_i32(P, P, 4, 64, 65, P, None) == -1
     # W larger than 32-bit byte offsets can address (h * o >= 2^31)
     assert lib.i8mm_int8_mixed_matmul(P, P, P, 65536, P, P, P, P, P, 4, 65536, 32768, P, None) == -1
+    assert lib.i8mm_int8_gemm_i32(P, P, 4, 65536, 32768, P, None) == -1
     assert lib.i8mm_outlier_matmul(P, 64, P, P, P, 4, 64, 64, MIS, None) == -1
 
 

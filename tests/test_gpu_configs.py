@@ -3,7 +3,7 @@ the benchmark times (i8mm_forward after the load-time weight conversion).
 
 Exact over the whole input: the outlier set, Xq, c_x and X_O. Exact on
 sampled output columns (the conversion of each W column is independent):
-Wq_t and c_w. On sampled rows x columns: C_i32 exactly and C within
+Wq (as W_i8 transposed) and c_w. On sampled rows x columns: C_i32 exactly and C within
 2e-3 ||C_ref||_inf of the oracle. Over every output element: the
 closed-form error bound |C - X W| <= sum_k (|w| m_i + |x| m'_j + m_i m'_j / 254) / 254
 (from the absmax/254 per-element bound), with X W taken in fp32 on the GPU.
@@ -57,9 +57,9 @@ def test_full_size_config(name):
     X, W = inp["X"], inp["W"]
     Xd, Wd = T(X), T(W)
     say(f"[{name}] launch: quantize_colwise_weights + forward")
-    Wq_t, c_w = i8.quantize_colwise_weights(Wd)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
     ws = i8.forward_workspace(s, h, DEV)
-    C = i8.forward(Xd, Wq_t, c_w, Wd, w.alpha, workspace=ws)
+    C = i8.forward(Xd, Wq, c_w, Wd, w.alpha, workspace=ws)
     torch.cuda.synchronize()
     v = i8.forward_workspace_views(ws, s, h)
 
@@ -74,11 +74,11 @@ def test_full_size_config(name):
     cols_d = torch.from_numpy(cols).to(DEV)
     rows_d = torch.from_numpy(rows).to(DEV)
     Wq_s, cw_s = oracle.quantize_colwise_weights(W[:, cols])
-    assert np.array_equal(H(Wq_t.index_select(0, cols_d)), Wq_s), "Wq_t differs"
+    assert np.array_equal(H(i8.panels_to_rows(Wq.index_select(1, cols_d))), Wq_s), "Wq differs"
     assert np.array_equal(H(c_w.index_select(0, cols_d)).view(np.uint32), cw_s.view(np.uint32)), "c_w differs"
 
     say(f"[{name}] launch: int8_gemm_i32")
-    Ci = i8.int8_gemm_i32(v["Xq"], Wq_t)
+    Ci = i8.int8_gemm_i32(v["Xq"], Wq)
     torch.cuda.synchronize()
     Ci_s = H(Ci.index_select(0, rows_d).index_select(1, cols_d))
     del Ci

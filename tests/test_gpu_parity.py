@@ -31,6 +31,9 @@ SHAPES = [
     (6, 513, 384, 768, 40, 0.28),
     (7, 8, 1024, 1024, 64, 1.0),
     (8, 257, 1152, 832, 1, 1.0),
+    (9, 40, 64, 320, 1, 0.5),        # one panel: the only K stage is half empty
+    (10, 300, 1088, 448, 3, 0.3),    # 8.5 K stages; o past one 256-column tile
+    (11, 16, 1088, 448, 3, 0.3),     # the same shape on the streaming path
 ]
 
 
@@ -39,19 +42,19 @@ def _run_all(X, W, alpha):
     say(f"  launch: detect/quantize/gemm s={X.shape[0]} h={X.shape[1]} o={W.shape[1]} alpha={alpha}")
     mask, idx, n_out = i8.detect_outlier_cols(Xd, alpha)
     Xq, c_x, X_O = i8.quantize_rowwise(Xd, mask, idx, n_out)
-    Wq_t, c_w = i8.quantize_colwise_weights(Wd)
-    C = i8.int8_mixed_matmul(Xq, c_x, X_O, idx, n_out, Wq_t, c_w, Wd)
-    Ci = i8.int8_gemm_i32(Xq, Wq_t)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    C = i8.int8_mixed_matmul(Xq, c_x, X_O, idx, n_out, Wq, c_w, Wd)
+    Ci = i8.int8_gemm_i32(Xq, Wq)
     CO = i8.outlier_matmul(X_O, idx, n_out, Wd)
     torch.cuda.synchronize()
-    return dict(mask=mask, idx=idx, n_out=n_out, Xq=Xq, c_x=c_x, X_O=X_O, Wq_t=Wq_t, c_w=c_w, C=C, Ci=Ci, CO=CO)
+    return dict(mask=mask, idx=idx, n_out=n_out, Xq=Xq, c_x=c_x, X_O=X_O, Wq=Wq, c_w=c_w, C=C, Ci=Ci, CO=CO)
 
 
 def _check_all(X, W, alpha, g):
     idx_r = check_detect(X, alpha, g["mask"], g["idx"], g["n_out"])
     Xq_r, cx_r, XO_r = check_rows(X, idx_r, g["Xq"], g["c_x"], g["X_O"])
     Wq_r, cw_r = oracle.quantize_colwise_weights(W)
-    assert np.array_equal(H(g["Wq_t"]), Wq_r), "Wq_t differs"
+    assert np.array_equal(H(i8.panels_to_rows(g["Wq"])), Wq_r), "Wq differs"
     assert np.array_equal(H(g["c_w"]).view(np.uint32), cw_r.view(np.uint32)), "c_w differs"
     Ci_r = oracle.int8_matmul_i32(Xq_r, Wq_r)
     assert np.array_equal(H(g["Ci"]), Ci_r), "C_i32 differs"
@@ -129,9 +132,9 @@ def test_max_h_int32_accumulator_bound(s):
     say(f"  launch: max-h s={s}")
     mask, idx, n_out = i8.detect_outlier_cols(Xd, 6.0)
     Xq, c_x, X_O = i8.quantize_rowwise(Xd, mask, idx, n_out)
-    Wq_t, c_w = i8.quantize_colwise_weights(Wd)
-    Ci = i8.int8_gemm_i32(Xq, Wq_t)
-    C = i8.int8_mixed_matmul(Xq, c_x, X_O, idx, n_out, Wq_t, c_w, Wd)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    Ci = i8.int8_gemm_i32(Xq, Wq)
+    C = i8.int8_mixed_matmul(Xq, c_x, X_O, idx, n_out, Wq, c_w, Wd)
     torch.cuda.synchronize()
     assert int(H(n_out)[0]) == 0
     assert (H(Ci) == h * 127 * 127).all()
@@ -143,11 +146,11 @@ def test_forward_matches_separate_calls_and_is_deterministic():
     inp = random_case(60, 70, 768, 640, 6, row_frac=0.75)
     X, W = inp["X"], inp["W"]
     Xd, Wd = T(X), T(W)
-    Wq_t, c_w = i8.quantize_colwise_weights(Wd)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
     ws = i8.forward_workspace(70, 768, DEV)
-    C1 = i8.forward(Xd, Wq_t, c_w, Wd, 6.0, workspace=ws)
+    C1 = i8.forward(Xd, Wq, c_w, Wd, 6.0, workspace=ws)
     v = {k: t.clone() for k, t in i8.forward_workspace_views(ws, 70, 768).items()}
-    C2 = i8.forward(Xd, Wq_t, c_w, Wd, 6.0, workspace=ws)
+    C2 = i8.forward(Xd, Wq, c_w, Wd, 6.0, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(C1, C2)
     g = _run_all(X, W, 6.0)
@@ -157,11 +160,14 @@ def test_forward_matches_separate_calls_and_is_deterministic():
     assert torch.equal(v["Xq"], g["Xq"]) and torch.equal(v["c_x"], g["c_x"])
 
 
-# Forward paths: s * ceil(h / 8192) <= 16 (h <= 16384) runs the single-block
-# fused prologue, other inputs the accumulator path (detect -> quantise with ranks
-# -> product); (70, 768) once overran the small path's 16-row tables.
-FWD = [(70, 768, 640, 6, 6.0), (16, 8192, 256, 7, 6.0), (17, 8192, 256, 7, 6.0), (300, 640, 576, 5, 6.0),
-       (8, 16384, 128, 9, 6.0), (9, 12288, 128, 9, 6.0),
+# Forward paths: s <= 64 runs the slab kernels (row groups of 16: s <= 16, 32,
+# 64), larger s the accumulator path with one wavefront per row, the row held
+# in registers for h <= 16384 (chunks per lane 2 .. 32) and re-read above.
+# (70, 768) once overran a former single-block path's 16-row tables.
+FWD = [(70, 768, 640, 6, 6.0), (16, 8192, 256, 7, 6.0), (17, 8192, 256, 7, 6.0), (33, 1024, 256, 7, 6.0),
+       (64, 2048, 256, 7, 6.0), (65, 2048, 256, 7, 6.0), (300, 640, 576, 5, 6.0),
+       (8, 16384, 128, 9, 6.0), (9, 12288, 128, 9, 6.0), (66, 16384, 128, 9, 6.0), (70, 20480, 128, 9, 6.0),
+       (3, 133120, 64, 9, 6.0),
        (40, 128, 192, 0, 0.0), (1100, 128, 192, 0, 0.0), (513, 384, 768, 40, 6.0), (2, 64, 64, 0, 6.0)]
 
 
@@ -170,13 +176,13 @@ def test_forward_paths_match_separate_calls(s, h, o, nout, alpha):
     inp = random_case(70 + s, s, h, o, nout, row_frac=0.5)
     X, W = inp["X"], inp["W"]
     Xd, Wd = T(X), T(W)
-    Wq_t, c_w = i8.quantize_colwise_weights(Wd)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
     ws = i8.forward_workspace(s, h, DEV)
     say(f"  launch: forward s={s} h={h} o={o} alpha={alpha}")
-    C1 = i8.forward(Xd, Wq_t, c_w, Wd, alpha, workspace=ws)
+    C1 = i8.forward(Xd, Wq, c_w, Wd, alpha, workspace=ws)
     torch.cuda.synchronize()
     v = {k: t.clone() for k, t in i8.forward_workspace_views(ws, s, h).items()}
-    assert not v["acc"].any(), "mask accumulator not returned to zero"
+    assert not v["acc"].any(), "accumulator not returned to zero"
     g = _run_all(X, W, alpha)
     n = int(H(g["n_out"])[0])
     assert int(H(v["n_out"])[0]) == n
@@ -187,7 +193,7 @@ def test_forward_paths_match_separate_calls(s, h, o, nout, alpha):
     assert torch.equal(C1, g["C"])
     _check_all(X, W, alpha, dict(g, mask=v["mask"], idx=v["idx"], n_out=v["n_out"], Xq=v["Xq"], c_x=v["c_x"],
                                  X_O=v["X_O"], C=C1))
-    C2 = i8.forward(Xd, Wq_t, c_w, Wd, alpha, workspace=ws)
+    C2 = i8.forward(Xd, Wq, c_w, Wd, alpha, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(C1, C2)
 
@@ -199,9 +205,9 @@ def test_forward_workspace_reuse_across_shapes():
         inp = random_case(90 + s + nout, s, h, o, nout, row_frac=0.5)
         X, W = inp["X"], inp["W"]
         Xd, Wd = T(X), T(W)
-        Wq_t, c_w = i8.quantize_colwise_weights(Wd)
+        Wq, c_w = i8.quantize_colwise_weights(Wd)
         say(f"  launch: forward reuse s={s} h={h}")
-        C = i8.forward(Xd, Wq_t, c_w, Wd, 6.0, workspace=big)
+        C = i8.forward(Xd, Wq, c_w, Wd, 6.0, workspace=big)
         torch.cuda.synchronize()
         ref = _run_all(X, W, 6.0)
         assert torch.equal(C, ref["C"])
