@@ -40,14 +40,11 @@ namespace {
 constexpr int kTO = 256;   // output columns (o) per block
 constexpr int kTS = 256;   // output rows (s) per block
 constexpr int kTK = 128;   // reduction bytes per LDS stage
-constexpr int kStageA = kTO * kTK / 16;  // v4i slots
-constexpr int kStageB = kTS * kTK / 16;
-constexpr int kStage = kStageA + kStageB;
+constexpr int kBuf = 256 * kTK / 16;   // v4i slots of one operand's stage buffer (32 KiB)
 
-// 16-byte slot of chunk `c` (0..7) of LDS row `row` (rows are 128 bytes):
-// XOR swizzle so that 8 consecutive rows reading the same chunk hit 8
-// different 16-byte bank groups.
-__device__ __forceinline__ int swz(int row, int c) { return row * 8 + (c ^ (row & 7)); }
+// LDS layout of a stage buffer: 256 rows of 128 bytes; row r keeps its
+// 16-byte chunk c in slot 8 r + (c ^ (r & 7)), so that 8 consecutive rows
+// reading the same chunk hit 8 different 16-byte bank groups.
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
 // return zero, which pads ragged tiles without branches. Word 3 selects the
@@ -130,12 +127,48 @@ __device__ __forceinline__ v16f apply_outlier_slice(const uint16_t* sl, int wo, 
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb, f, 0, 0, 0);
 }
 
+// In-place transpose of the W part of a staged slice, [16 k][256 columns]
+// -> [256 columns][16 k] as two 16-byte halves per column (k 0-7, 8-15)
+// whose order flips with bit 3 of the column, so that 16 consecutive
+// columns read at one k half hit 16 different bank groups. Thread t owns
+// column t; two block barriers.
+__device__ __forceinline__ void transpose_w_slice(uint16_t* sl) {
+    const int t = threadIdx.x;
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = static_cast<uint32_t>(sl[(2 * j) * 256 + t]) | (static_cast<uint32_t>(sl[(2 * j + 1) * 256 + t]) << 16);
+    __syncthreads();
+    const int sw = (t >> 3) & 1;
+    uint4* dst = reinterpret_cast<uint4*>(sl);
+    dst[t * 2 + sw] = make_uint4(v[0], v[1], v[2], v[3]);
+    dst[t * 2 + (sw ^ 1)] = make_uint4(v[4], v[5], v[6], v[7]);
+    __syncthreads();
+}
+
+// apply_outlier_slice on a transposed slice: both operands are one 16-byte read.
+__device__ __forceinline__ v16f apply_outlier_slice_t(const uint16_t* sl, int wo, int ws, int sb, int ob, int r32,
+                                                      int khalf, v16f f) {
+    const v8h xb = *reinterpret_cast<const v8h*>(sl + kSlice + (ws * 128 + sb * 32 + r32) * 16 + 8 * khalf);
+    const int col = wo * 128 + ob * 32 + r32;
+    const v8h wa = *reinterpret_cast<const v8h*>(sl + (col * 2 + (khalf ^ ((col >> 3) & 1))) * 8);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb, f, 0, 0, 0);
+}
+
 // LDS staging of the fp16 output: each wavefront owns 32 rows x 128
 // columns, rows padded to 136 halves (272 bytes) against bank conflicts.
 constexpr int kOutRow = 136;
 constexpr int kOutWave = 32 * kOutRow;          // halves per wavefront
 constexpr int kMaxOnceSlices = 5;               // extra slices staged at once
 
+// Prefill main loop: both operand tiles reach LDS through direct-to-LDS
+// buffer loads, double buffered in four separate arrays (A0/A1 weights,
+// B0/B1 activations) so that the compiler's wait tracking for these loads
+// can tell the buffer being filled from the one being read. A stage's
+// 16 loads per wavefront go out in three parts spread over three
+// sub-steps, interleaved with the MFMAs, so that the loads never queue up
+// in front of the matrix-core instructions; the fourth sub-step before the
+// barrier covers their latency.
 template <GemmOut MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
@@ -145,85 +178,80 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out,
                     const uint16_t* __restrict__ W, void* __restrict__ Cout,
                     uint32_t* __restrict__ clear, int clear_words) {
-    __shared__ v4i lds[2 * kStage];
+    __shared__ v4i A0[kBuf], A1[kBuf], B0[kBuf], B1[kBuf];
+    __shared__ __attribute__((aligned(16))) uint16_t olds[2 * kSlice];
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
 
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(wid);
     const int wo = wid & 1, ws = wid >> 1;
+    const int r32 = lane & 31, khalf = lane >> 5;
     const int64_t n_ts = (s + kTS - 1) / kTS;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t ts_i = tile % n_ts, to_i = tile / n_ts;
     const int64_t o0 = to_i * kTO, s0 = ts_i * kTS;
-
-    // Tile-relative buffer resources. B: rows past s read as zero. A: one
-    // resource per stage, based at the tile's first column in the stage's
-    // first panel (see gload); rows past o are masked in their offsets, as
-    // in the panel layout the bytes after a panel's last column belong to
-    // the next panel.
     const int64_t o_rows = o - o0 < kTO ? o - o0 : kTO;
     const int64_t s_rows = s - s0 < kTS ? s - s0 : kTS;
+
+    // Buffer resources. B: rows past s read as zero. A: one resource per
+    // stage, based at the tile's first column in the stage's first panel,
+    // ending with the array, so that a missing second panel (h % 128 == 64)
+    // and every stage past the last one lie outside it.
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(Xq + s0 * h, static_cast<uint32_t>(s_rows * h));
     const int64_t wq_bytes = h * o;
 
-    // Global -> register staging: thread t moves chunk (t & 7) of rows
-    // (t >> 3) + 32 p, p = 0..7, of both tiles. A stage's chunk c is the
-    // 16-byte piece c % 4 of panel 2 kt + c / 4. Offsets live in the
-    // per-lane part, which the range check covers; for B only the uniform
-    // K offset goes in the scalar offset.
-    const int st_c = t & 7, st_r = t >> 3;
-    uint32_t voffA[8], voffB[8];
+    // Load q (0..7) of wavefront w fills LDS rows 64 w + 8 q .. + 7 (one
+    // KiB; lane i writes slot 8 r + i % 8 of row r = 64 w + 8 q + i / 8),
+    // so lane i fetches chunk c = (i % 8) ^ (i / 8) of its row: panel
+    // 2 kt + c / 4, bytes 16 (c % 4) of the row's 64 there. Rows past o
+    // (whole wavefronts, as o_rows is a multiple of 64) and chunks past h
+    // get the out-of-range offset.
+    const int dr = lane >> 3;
+    const int c = (lane & 7) ^ dr;
+    const uint32_t vA = 64 * wu < o_rows
+                            ? static_cast<uint32_t>((64 * wu + dr) * 64 + (c & 3) * 16 + (c >> 2) * o * 64)
+                            : kOutOfRange;
+    uint32_t vB[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int row = st_r + 32 * p;
-        voffA[p] = row < o_rows ? static_cast<uint32_t>(row * 64 + (st_c & 3) * 16 + (st_c >> 2) * o * 64)
-                                : kOutOfRange;
-        voffB[p] = static_cast<uint32_t>(row * h + st_c * 16);
-    }
-    v4i ra[8], rb[8];
+    for (int q = 0; q < 8; ++q) vB[q] = static_cast<uint32_t>((64 * wu + 8 * q + dr) * h + c * 16);
     const int64_t KT = (h + kTK - 1) / kTK;
-
-    auto gload = [&](int64_t kt) {
+    // Loads q in [q0, q1) of stage kt into (A, B).
+    auto load_part = [&](int64_t kt, v4i* A, v4i* B, int q0, int q1) {
         const uint32_t k = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kt * kTK));
-        // The stage's A resource ends with the array, so a missing second
-        // panel (h % 128 == 64) and every stage past the last one lie
-        // outside it; chunks past h also get the top offset bit (row
-        // offsets stay below 2^31), computed without a branch.
         const int64_t a0 = o0 * 64 + kt * kTK * o;
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq + (a0 < wq_bytes ? a0 : 0), bytes_left(wq_bytes, a0));
-        const uint32_t oob = (k + st_c * 16 < static_cast<uint32_t>(h)) ? 0u : kOutOfRange;
+        const uint32_t oob = (k + c * 16 < static_cast<uint32_t>(h)) ? 0u : kOutOfRange;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            ra[p] = buf_load16(rA, voffA[p] | oob, 0);
-            rb[p] = buf_load16(rB, voffB[p] | oob, k);
-        }
-    };
-    auto lstore = [&](int buf) {
-        v4i* A = lds + buf * kStage;
-        v4i* B = A + kStageA;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int row = st_r + 32 * p;
-            A[swz(row, st_c)] = ra[p];
-            B[swz(row, st_c)] = rb[p];
+        for (int q = q0; q < q1; ++q) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(A + (wu * 8 + q) * 64), 16, (vA | oob) + q * 512, 0,
+                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(B + (wu * 8 + q) * 64), 16, vB[q] | oob, k, 0, 0);
         }
     };
 
-    const int r32 = lane & 31, khalf = lane >> 5;
-
-    // The first slice of the outlier operands goes to its own LDS region
-    // now; the loads complete under the main loop and hold no registers.
-    __shared__ __attribute__((aligned(16))) uint16_t olds[2 * kSlice];
+    // The first slice of the outlier operands goes to its own LDS region,
+    // and the scales of this wavefront's rows and columns to registers: the
+    // loads complete under the main loop.
     int n_o = 0;
-    const bool mixed = MODE == GemmOut::Mixed;
+    constexpr bool mixed = MODE == GemmOut::Mixed;
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(mixed ? W + o0 : nullptr, mixed ? static_cast<uint32_t>((h * o - o0) * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(mixed ? X_O + s0 * ldo : nullptr,
                                                 mixed ? static_cast<uint32_t>(s_rows * ldo * 2) : 0u);
-    if constexpr (MODE == GemmOut::Mixed) {
+    float cx_pf[4], cw_pf[2];
+    if constexpr (mixed) {
         n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
-        if (n_o > 0)
-            stage_outlier_slice(0, n_o, __builtin_amdgcn_readfirstlane(wid), lane, o0, s0, s, o, ldo, idx, rW, rX,
-                                olds);
+        if (n_o > 0) stage_outlier_slice(0, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, olds);
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            const int64_t srow = s0 + ws * 128 + sb * 32 + r32;
+            cx_pf[sb] = srow < s ? c_x[srow] : 1.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t col = o0 + wo * 128 + lane + 64 * i;
+            cw_pf[i] = col < o ? c_w[col] : 1.0f;
+        }
     }
 
     v16i acc[4][4];
@@ -234,24 +262,21 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
-    gload(0);
-    lstore(0);
-    gload(1);
-    __syncthreads();
-    // LDS slots of this lane's fragments (chunk added per sub-step)
-    int rowA[4], rowB[4];
+    // Fragment slots: the four rows a lane reads share r & 7 (= r32 & 7),
+    // so slot(row_i, chunk) = slot(row_0, chunk) + 256 i.
+    int offA[4], offB[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        rowA[i] = wo * 128 + i * 32 + r32;
-        rowB[i] = ws * 128 + i * 32 + r32;
+    for (int kk = 0; kk < 4; ++kk) {
+        const int x = (kk * 2 + khalf) ^ (r32 & 7);
+        offA[kk] = (wo * 128 + r32) * 8 + x;
+        offB[kk] = (ws * 128 + r32) * 8 + x;
     }
     v4i fa[2][4], fb[2][4];
     auto frags = [&](const v4i* A, const v4i* B, int kk, v4i* a, v4i* b) {
-        const int c = kk * 2 + khalf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = A[swz(rowA[i], c)];
+        for (int i = 0; i < 4; ++i) a[i] = A[offA[kk] + 256 * i];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = B[swz(rowB[i], c)];
+        for (int i = 0; i < 4; ++i) b[i] = B[offB[kk] + 256 * i];
     };
     auto mma = [&](const v4i* a, const v4i* b) {
 #pragma unroll
@@ -260,61 +285,66 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             for (int sb = 0; sb < 4; ++sb)
                 acc[ob][sb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ob], b[sb], acc[ob][sb], 0, 0, 0);
     };
-
-    frags(lds, lds + kStageA, 0, fa[0], fb[0]);
-    // Software pipeline across the stage barrier: the fragments of the
-    // last sub-step are read before the barrier and multiplied after it,
-    // covering the latency of the next stage's first LDS reads. The global
-    // prefetch runs two stages ahead of its LDS store. Past the last stage
-    // every offset is >= h and the range-checked loads return zeros that
-    // land in the idle buffer.
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        const v4i* A = lds + (kt & 1) * kStage;
-        const v4i* B = A + kStageA;
-        frags(A, B, 1, fa[1], fb[1]);
-        mma(fa[0], fb[0]);
-        frags(A, B, 2, fa[0], fb[0]);
-        mma(fa[1], fb[1]);
-        frags(A, B, 3, fa[1], fb[1]);
-        // The other buffer was last read before the previous barrier.
-        lstore((kt + 1) & 1);
-        mma(fa[0], fb[0]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        }
+    // One sub-step's order: MFMAs interleaved with the next sub-step's LDS
+    // reads and with this part's loads.
+    auto sched_sub = [&]() {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // DS write
-        }
-        __syncthreads();
-        const v4i* A2 = lds + ((kt + 1) & 1) * kStage;
-        frags(A2, A2 + kStageA, 0, fa[0], fb[0]);
-        gload(kt + 2);
-        mma(fa[1], fb[1]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // VMEM read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
+    };
+    // Stage kt from (Ac, Bc); stage kt + 1 sits in (An, Bn), of which loads
+    // 3..7 are still to go out (loads 0..2 left with the previous stage's
+    // last sub-step). Software pipeline across the barrier: the fragments of
+    // sub-step 3 are read before it and multiplied after it, and right after
+    // it (Ac, Bc) are free and receive loads 0..2 of stage kt + 2. Loads of
+    // stages past the last one fall outside their resources and land as
+    // zeros in the idle buffers, so the loop carries no branch around them.
+    auto stage = [&](int64_t kt, v4i* Ac, v4i* Bc, v4i* An, v4i* Bn) {
+        frags(Ac, Bc, 1, fa[1], fb[1]);
+        load_part(kt + 1, An, Bn, 3, 6);
+        mma(fa[0], fb[0]);
+        sched_sub();
+        frags(Ac, Bc, 2, fa[0], fb[0]);
+        load_part(kt + 1, An, Bn, 6, 8);
+        mma(fa[1], fb[1]);
+        sched_sub();
+        frags(Ac, Bc, 3, fa[1], fb[1]);
+        mma(fa[0], fb[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        // The barrier's fence does not cover direct-to-LDS loads: each
+        // wavefront first waits for its own loads of stage kt + 1.
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        __syncthreads();
+        frags(An, Bn, 0, fa[0], fb[0]);
+        load_part(kt + 2, Ac, Bc, 0, 3);
+        mma(fa[1], fb[1]);
+        sched_sub();
+    };
+
+    load_part(0, A0, B0, 0, 8);
+    load_part(1, A1, B1, 0, 3);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    __syncthreads();
+    frags(A0, B0, 0, fa[0], fb[0]);
+    int64_t kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        stage(kt, A0, B0, A1, B1);
+        stage(kt + 1, A1, B1, A0, B0);
     }
+    if (kt < KT) stage(kt, A0, B0, A1, B1);   // an odd number of stages
 
     // Lane layout of a 32x32 accumulator: register r holds
     // D[o = 8 (r / 4) + 4 (lane / 32) + r % 4][s = lane % 32].
@@ -337,33 +367,37 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             }
     } else {
         uint16_t* C = static_cast<uint16_t*>(Cout);
-        // Slices past the first go to the main-loop buffers, free now: all
-        // at once when they fit (|O| <= 96), else in rounds per row block.
-        // The output staging area follows them.
-        const int wid_u = __builtin_amdgcn_readfirstlane(wid);
-        uint16_t* big = reinterpret_cast<uint16_t*>(lds);
-        uint16_t* out_st = big + kMaxOnceSlices * 2 * kSlice + wid * kOutWave;
+        __syncthreads();   // every wavefront is done with the stage buffers
+        // Epilogue LDS: extra outlier slices q = 1, 2 in A0, 3, 4 in B0 and
+        // 5 in B1; output staging of waves 0-2 in A1 and of wave 3 in B1,
+        // followed there by 1 / c_w.
+        auto slice_at = [&](int q) -> uint16_t* {   // q = 1 .. kMaxOnceSlices
+            uint16_t* base = q <= 2 ? reinterpret_cast<uint16_t*>(A0)
+                           : q <= 4 ? reinterpret_cast<uint16_t*>(B0)
+                                    : reinterpret_cast<uint16_t*>(B1) + kOutWave + 1024;
+            return base + (q <= 4 ? ((q - 1) & 1) * 2 * kSlice : 0);
+        };
+        uint16_t* out_st = wid < 3 ? reinterpret_cast<uint16_t*>(A1) + wid * kOutWave : reinterpret_cast<uint16_t*>(B1);
+        float* invw = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(B1) + kOutWave) + wid * 128;
         const int nsl = (n_o + 15) / 16;
         const bool once = nsl <= 1 + kMaxOnceSlices;
-        if (once && nsl > 1) {
-            for (int q = 1; q < nsl; ++q)
-                stage_outlier_slice(q, n_o, wid_u, lane, o0, s0, s, o, ldo, idx, rW, rX, big + (q - 1) * 2 * kSlice);
-        }
+        if (once)
+            for (int q = 1; q < nsl; ++q) stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q));
+        // 1 / c_w of the wave's 128 columns (reciprocals to 1 ulp)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) invw[lane + 64 * i] = __builtin_amdgcn_rcpf(cw_pf[i]);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // 1 / c_w of the wave's 128 columns, kept in its LDS area (reciprocals to 1 ulp).
-        float* invw = reinterpret_cast<float*>(big + kMaxOnceSlices * 2 * kSlice + 4 * kOutWave) + wid * 128;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t col = o0 + wo * 128 + lane + 64 * i;
-            invw[lane + 64 * i] = __builtin_amdgcn_rcpf(col < o ? c_w[col] : 1.0f);
+        if (once) {
+            // W parts transposed once, so that both MFMA operands are 16-byte reads
+            if (nsl > 0) transpose_w_slice(olds);
+            for (int q = 1; q < nsl; ++q) transpose_w_slice(slice_at(q));
         }
         // One 32-row block at a time: a lane then holds 4-column runs of one
         // row across all 128 columns of the wave.
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
-            const int64_t srow = s0 + ws * 128 + sb * 32 + r32;
-            const float inv_x = __builtin_amdgcn_rcpf(srow < s ? c_x[srow] : 1.0f);
+            const float inv_x = __builtin_amdgcn_rcpf(cx_pf[sb]);
             if (!once) __syncthreads();   // the previous row block's rounds are done
 #pragma unroll
             for (int ob = 0; ob < 4; ++ob) {
@@ -377,21 +411,21 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                         f[4 * g + e] = static_cast<float>(acc[ob][sb][4 * g + e]) * (inv_x * iw[e]);
                 }
                 // Outlier product X_O W[idx, :] on top (fp32 accumulate).
-                if (n_o > 0) f = apply_outlier_slice(olds, wo, ws, sb, ob, r32, khalf, f);
                 if (once) {
-                    for (int q = 1; q < nsl; ++q)
-                        f = apply_outlier_slice(big + (q - 1) * 2 * kSlice, wo, ws, sb, ob, r32, khalf, f);
+                    if (nsl > 0) f = apply_outlier_slice_t(olds, wo, ws, sb, ob, r32, khalf, f);
+                    for (int q = 1; q < nsl; ++q) f = apply_outlier_slice_t(slice_at(q), wo, ws, sb, ob, r32, khalf, f);
                 } else {
+                    // more than 96 outlier columns: further slices in rounds
+                    f = apply_outlier_slice(olds, wo, ws, sb, ob, r32, khalf, f);
                     for (int rb = 1; rb < nsl; rb += kMaxOnceSlices) {
                         const int re = rb + kMaxOnceSlices < nsl ? rb + kMaxOnceSlices : nsl;
                         __syncthreads();
                         for (int q = rb; q < re; ++q)
-                            stage_outlier_slice(q, n_o, wid_u, lane, o0, s0, s, o, ldo, idx, rW, rX,
-                                                big + (q - rb) * 2 * kSlice);
+                            stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q - rb + 1));
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                         __syncthreads();
                         for (int q = rb; q < re; ++q)
-                            f = apply_outlier_slice(big + (q - rb) * 2 * kSlice, wo, ws, sb, ob, r32, khalf, f);
+                            f = apply_outlier_slice(slice_at(q - rb + 1), wo, ws, sb, ob, r32, khalf, f);
                     }
                 }
                 // Round once to fp16 and stage in this wavefront's LDS area
