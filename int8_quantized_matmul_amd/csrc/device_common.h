@@ -20,6 +20,11 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
 }
 
 __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
+    // The empty asm pins f as an fp32 register value: otherwise the
+    // compiler may fold the multiply that produced f into a mixed-precision
+    // FMA that rounds the exact product once, straight to fp16, which
+    // differs from rounding to fp32 first at fp16 ties. It emits nothing.
+    asm("" : "+v"(f));
     // v_cvt_f16_f32 rounds to nearest even in the default mode.
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }

@@ -120,38 +120,43 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int6
 }
 
 // ---------------------------------------------------------------------------
-// Outlier-column detection into a mask. One wavefront per (512-column strip,
-// 8-row band): each lane loads its 8 columns of every row of the band at
-// once and folds them into its detection state; the 4 lanes of a mask word
-// combine through shuffles, and a non-zero word reaches the mask with one
-// atomicOr (the mask must be zero beforehand).
-constexpr int kDetBand = 8;
+// Outlier-column detection into a mask. One block per (512-column strip,
+// 32-row block): wavefront w folds rows 8 w .. 8 w + 7 of the block into
+// its lanes' detection state (each lane owns 8 columns and keeps its 8 row
+// loads in flight at once), the 4 lanes of a mask word combine through
+// shuffles, the 4 wavefronts meet in LDS, and each non-zero word of the
+// strip reaches the mask with one atomicOr per block (the mask must be zero
+// beforehand). Same-address global atomics serialise, so the per-block
+// merge keeps their count per word at s / 32.
+constexpr int kDetRows = 32;
 
 __global__ __launch_bounds__(256) void k_detect(const uint16_t* __restrict__ X, int64_t s, int64_t h,
-                                                Threshold th, int64_t n_strips, int64_t n_waves,
-                                                uint32_t* __restrict__ mask) {
-    const int lane = threadIdx.x & 63;
-    const int64_t wv = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (wv >= n_waves) return;
-    const int64_t strip = wv % n_strips, band = wv / n_strips;
+                                                Threshold th, int64_t n_strips, uint32_t* __restrict__ mask) {
+    __shared__ uint32_t words[16];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    if (t < 16) words[t] = 0u;
+    const int64_t strip = blockIdx.x % n_strips, rb = blockIdx.x / n_strips;
     const int64_t col = strip * 512 + lane * 8;
-    const int64_t r0 = band * kDetBand;
+    const int64_t r0 = rb * kDetRows + wid * 8;
     uint32_t flags = 0;
     if (col < h) {
-        uint4 v[kDetBand];
+        uint4 v[8];
 #pragma unroll
-        for (int u = 0; u < kDetBand; ++u)
-            if (r0 + u < s) v[u] = load_chunk(X + (r0 + u) * h + col);
+        for (int u = 0; u < 8; ++u)
+            v[u] = r0 + u < s ? load_chunk(X + (r0 + u) * h + col) : make_uint4(0, 0, 0, 0);
         uint4 d = detect_init();
 #pragma unroll
-        for (int u = 0; u < kDetBand; ++u)
+        for (int u = 0; u < 8; ++u)
             if (r0 + u < s) detect_fold(d, v[u], th.thr2);
         flags = detect_flags(d, th.span);
     }
     uint32_t word = flags << ((lane & 3) * 8);
     word |= __shfl_xor(word, 1, kWave);
     word |= __shfl_xor(word, 2, kWave);
-    if ((lane & 3) == 0 && word != 0u) atomicOr(&mask[col >> 5], word);
+    __syncthreads();
+    if ((lane & 3) == 0 && word != 0u) atomicOr(&words[lane >> 2], word);
+    __syncthreads();
+    if (t < 16 && words[t] != 0u) atomicOr(&mask[strip * 16 + t], words[t]);
 }
 
 // ---------------------------------------------------------------------------
@@ -554,9 +559,9 @@ Threshold make_threshold(float alpha) {
 hipError_t launch_detect_into(const uint16_t* X, int64_t s, int64_t h, float alpha, uint32_t* mask,
                               hipStream_t stream) {
     const int64_t n_strips = (h + 511) / 512;
-    const int64_t n_waves = n_strips * ((s + kDetBand - 1) / kDetBand);
-    hipLaunchKernelGGL(k_detect, dim3(static_cast<unsigned>((n_waves + 3) / 4)), dim3(256), 0, stream,
-                       X, s, h, make_threshold(alpha), n_strips, n_waves, mask);
+    const int64_t blocks = n_strips * ((s + kDetRows - 1) / kDetRows);
+    hipLaunchKernelGGL(k_detect, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       X, s, h, make_threshold(alpha), n_strips, mask);
     return hipGetLastError();
 }
 
