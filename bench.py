@@ -58,6 +58,70 @@ def product_kernel_ms(i8, torch, n, launch):
     return e0.elapsed_time(e1) / n
 
 
+def timed_ms(torch, n, fn, warmup=3):
+    """Average of n back-to-back calls of fn between one pair of HIP events."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def step_percentiles(torch, n, fn):
+    """p10 / p50 / p90 of n individually timed calls (an event pair per call)."""
+    evs = [_events(torch) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    q = lambda f: ts[min(n - 1, int(round(f * (n - 1))))]
+    return {"p10": round(q(0.1), 5), "p50": round(q(0.5), 5), "p90": round(q(0.9), 5)}
+
+
+def table5_set(i8, torch, X, W, Wq, c_w, alpha, n, ws=None):
+    """The pages' Table 5 comparison set on one layer (raw matmul time, inputs
+    resident): the FP16 GEMM of the vendor library (torch.matmul -> hipBLASLt),
+    the int8 product alone ("Int8 without overhead": the same main loop with an
+    int32 store, and the fused product with no outlier columns), vector-wise
+    quantisation only (forward at alpha = inf: no decomposition) and the full
+    LLM.int8() forward. Speed-ups are FP16 time / variant time."""
+    s, h = X.shape
+    o = W.shape[1]
+    dev = X.device
+    if ws is None:
+        ws = i8.forward_workspace(s, h, dev)
+    v = i8.forward_workspace_views(ws, s, h)
+    C = torch.empty((s, o), dtype=torch.float16, device=dev)
+    Cf = torch.empty((s, o), dtype=torch.float16, device=dev)
+    Ci = torch.empty((s, o), dtype=torch.int32, device=dev)
+    t_fp16 = timed_ms(torch, n, lambda: torch.matmul(X, W, out=Cf))
+    t_llm = timed_ms(torch, n, lambda: i8.forward(X, Wq, c_w, W, alpha, workspace=ws, C=C))
+    t_vec = timed_ms(torch, n, lambda: i8.forward(X, Wq, c_w, W, float("inf"), workspace=ws, C=C))
+    # the forward at alpha = inf left Xq / c_x for the no-outlier product in the workspace
+    zero = torch.zeros((1,), dtype=torch.int32, device=dev)
+    t_i32 = timed_ms(torch, n, lambda: i8.int8_gemm_i32(v["Xq"], Wq, C=Ci))
+    t_fused0 = timed_ms(torch, n, lambda: i8.int8_mixed_matmul(v["Xq"], v["c_x"], v["X_O"], v["idx"], zero,
+                                                                Wq, c_w, W, C))
+    r = lambda t: round(t_fp16 / t, 3)
+    return {
+        "fp16_library_ms": round(t_fp16, 5),
+        "int8_gemm_i32_ms": round(t_i32, 5),
+        "int8_product_no_outliers_ms": round(t_fused0, 5),
+        "vectorwise_only_ms": round(t_vec, 5),
+        "llm_int8_ms": round(t_llm, 5),
+        "speedup_vs_fp16": {"int8_without_overhead": r(min(t_i32, t_fused0)), "vectorwise_only": r(t_vec),
+                            "llm_int8": r(t_llm)},
+    }
+
+
 def run_prefill(i8, torch, w, steps, warmup, dev):
     from workloads import make_inputs
     inp = make_inputs(w)
@@ -101,8 +165,26 @@ def run_prefill(i8, torch, w, steps, warmup, dev):
         v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
 
     n_out = int(v["n_out"].cpu()[0])
+    pct = step_percentiles(torch, steps, step)
+    table5 = table5_set(i8, torch, X, W, Wq, c_w, w.alpha, steps)
+    # MALL-cold steps: rotate over weight copies whose total exceeds the
+    # 256 MB Infinity Cache, so every step streams its weights from HBM
+    copies = max(2, -(-512 * 2**20 // (3 * h * o)))
+    sets = [(Wq, c_w, W)] + [(Wq.clone(), c_w.clone(), W.clone()) for _ in range(copies - 1)]
+    it = [0]
+
+    def cold_step():
+        a, b, c = sets[it[0] % copies]
+        it[0] += 1
+        i8.forward(X, a, b, c, w.alpha, workspace=ws, C=C)
+
+    cold_ms = timed_ms(torch, steps, cold_step, warmup=copies)
+    del sets
+    # the step's intermediates again for anything that reads them later
+    step()
+    torch.cuda.synchronize()
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out,
-                inputs=inp)
+                inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies)
 
 
 def run_decode(i8, torch, w, steps, warmup, dev):
@@ -131,6 +213,44 @@ def run_decode(i8, torch, w, steps, warmup, dev):
     n_out = int(v["n_out"].cpu()[0])
     weight_bytes = h * o + 2 * n_out * o + 4 * o
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes)
+
+
+# The pages' Table 5 (raw matmul of the first FFN layer of GPT-3 models, X [s, d]
+# times W [d, 4d], speed-up over FP16): widths and their printed ratios.
+TABLE5_WIDTHS = [768, 2560, 4096, 5120, 12288]
+TABLE5_PAGES = {"llm_int8": {"768": 0.14, "2560": 0.64, "4096": 0.86, "5120": 1.22, "12288": 1.81},
+                "vectorwise_only": {"5120": 1.59, "12288": 2.00},
+                "int8_without_overhead": {"768": 0.99, "12288": 2.29}}
+
+
+def run_table5(i8, torch, dev, s, n):
+    """The Table 5 comparison set at each width on inputs drawn on the GPU from
+    a seeded generator: X ~ N(0,1) clipped to |x| < 5.5 with 6 (7 at 12288)
+    one-sided outlier columns of magnitude U(6, 20) in 75 % of the rows,
+    W ~ 0.02 N(0,1). (The pages give 5140 for the 13B width; 5120 is used, as
+    the library takes widths that are multiples of 64.)"""
+    rows = []
+    for d in TABLE5_WIDTHS:
+        g = torch.Generator(device=dev)
+        g.manual_seed(d)
+        o = 4 * d
+        X = torch.randn((s, d), generator=g, device=dev).clamp_(-5.49, 5.49)
+        n_out = 7 if d >= 12288 else 6
+        cols = torch.randperm(d, generator=g, device=dev)[:n_out]
+        for c in cols.tolist():
+            sel = torch.randperm(s, generator=g, device=dev)[: round(0.75 * s)]
+            sign = 1.0 if torch.rand((), generator=g, device=dev).item() < 0.5 else -1.0
+            X[sel, c] = sign * (6.0 + 14.0 * torch.rand((sel.numel(),), generator=g, device=dev))
+        X = X.half()
+        W = (0.02 * torch.randn((d, o), generator=g, device=dev)).half()
+        Wq, c_w = i8.quantize_colwise_weights(W)
+        res = table5_set(i8, torch, X, W, Wq, c_w, 6.0, n)
+        res.update({"d": d, "s": s, "o": o, "planted_outliers": n_out})
+        rows.append(res)
+        _log(f"[table5] d={d}: {res['speedup_vs_fp16']}")
+        del X, W, Wq, c_w
+        torch.cuda.empty_cache()
+    return rows
 
 
 def cpu_baseline(w, inputs, budget_s):
@@ -183,6 +303,10 @@ def main(argv=None):
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic of the product kernel measured with rocprofv3 counters")
+    ap.add_argument("--table5", action="store_true",
+                    help="only run the pages' Table 5 comparison set over the GPT-3 FFN widths "
+                         "and print it as one JSON line")
+    ap.add_argument("--table5-rows", type=int, default=2048, help="rows of X (tokens) for --table5")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (5 times) and exit; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -206,6 +330,12 @@ def main(argv=None):
             torch.bitwise_not(src, out=dst)   # elementwise: reads n bytes, writes n bytes
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+        return 0
+    if args.table5:
+        rows = run_table5(i8, torch, dev, args.table5_rows, args.steps)
+        print(json.dumps({"table5": rows, "pages_table5": TABLE5_PAGES,
+                          "note": "raw matmul of X [s, d] x W [d, 4d], inputs resident; "
+                                  "speed-up = FP16 library GEMM time / variant time"}), flush=True)
         return 0
     w = get_config(args.workload)
     _log(f"[bench] prefill workload {w.name}: s={w.s} h={w.h} o={w.o}")
@@ -252,6 +382,9 @@ def main(argv=None):
             "avg_launch_ms": round(pre["gemm_ms"], 5),
         },
         "pct_int8_peak_effective": round(100 * tops / INT8_PEAK_TOPS, 2),
+        "step_ms_percentiles": pre["pct"],
+        "step_ms_weights_from_hbm": {"ms": round(pre["cold_ms"], 5), "weight_copies_rotated": pre["copies"]},
+        "table5_comparison": pre["table5"],
         "weight_conversion": {"ms": round(pre["conv_ms"], 4),
                               "GB_per_s": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1)},
     }
