@@ -88,7 +88,9 @@ def step_percentiles(torch, n, fn):
 
 def table5_set(i8, torch, X, W, Wq, c_w, alpha, n, ws=None):
     """The pages' Table 5 comparison set on one layer (raw matmul time, inputs
-    resident): the FP16 GEMM of the vendor library (torch.matmul -> hipBLASLt),
+    resident): the FP16 GEMM of the vendor library (torch.matmul -> hipBLASLt)
+    and the library's own dense fp16 kernel (i8mm_fp16_gemm, weights packed at
+    load time),
     the int8 product alone ("Int8 without overhead": the same main loop with an
     int32 store, and the fused product with no outlier columns), vector-wise
     quantisation only (forward at alpha = inf: no decomposition) and the full
@@ -103,6 +105,9 @@ def table5_set(i8, torch, X, W, Wq, c_w, alpha, n, ws=None):
     Cf = torch.empty((s, o), dtype=torch.float16, device=dev)
     Ci = torch.empty((s, o), dtype=torch.int32, device=dev)
     t_fp16 = timed_ms(torch, n, lambda: torch.matmul(X, W, out=Cf))
+    Wp = i8.pack_fp16_weights(W)          # load time for the library's own fp16 baseline
+    t_fp16_own = timed_ms(torch, n, lambda: i8.fp16_gemm(X, Wp, C=Cf))
+    del Wp
     t_llm = timed_ms(torch, n, lambda: i8.forward(X, Wq, c_w, W, alpha, workspace=ws, C=C))
     t_vec = timed_ms(torch, n, lambda: i8.forward(X, Wq, c_w, W, float("inf"), workspace=ws, C=C))
     # the forward at alpha = inf left Xq / c_x for the no-outlier product in the workspace
@@ -113,12 +118,17 @@ def table5_set(i8, torch, X, W, Wq, c_w, alpha, n, ws=None):
     r = lambda t: round(t_fp16 / t, 3)
     return {
         "fp16_library_ms": round(t_fp16, 5),
+        "fp16_own_ms": round(t_fp16_own, 5),
+        "fp16_own_tflops": round(2.0 * s * h * o / (t_fp16_own * 1e-3) / 1e12, 1),
         "int8_gemm_i32_ms": round(t_i32, 5),
         "int8_product_no_outliers_ms": round(t_fused0, 5),
         "vectorwise_only_ms": round(t_vec, 5),
         "llm_int8_ms": round(t_llm, 5),
         "speedup_vs_fp16": {"int8_without_overhead": r(min(t_i32, t_fused0)), "vectorwise_only": r(t_vec),
                             "llm_int8": r(t_llm)},
+        "speedup_vs_own_fp16": {"int8_without_overhead": round(t_fp16_own / min(t_i32, t_fused0), 3),
+                                "vectorwise_only": round(t_fp16_own / t_vec, 3),
+                                "llm_int8": round(t_fp16_own / t_llm, 3)},
     }
 
 

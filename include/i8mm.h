@@ -183,6 +183,28 @@ i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq,
                                int64_t s, int64_t h, int64_t o, int32_t* C_i32,
                                hipStream_t stream);
 
+/*
+ * Dense fp16 baseline, load-time packing: W fp16 [h, o] -> Wp fp16 in the
+ * fp16 panel layout [h / 32][o][32] (W[k, j] is element
+ * (k / 32) * o * 32 + j * 32 + k % 32 of Wp; 2 * h * o bytes).
+ *
+ * [DIGEST] "Runtime Performance (Appendix D)": Table 5 reports every variant
+ * as a speed-up over the FP16 matrix multiply of the same layer; this and
+ * i8mm_fp16_gemm provide that baseline with the library's own kernels.
+ * Shape limits as above, plus 2 * h * o < 2^31.
+ */
+i8mm_status i8mm_pack_fp16_weights(const uint16_t* W, int64_t h, int64_t o, uint16_t* Wp, hipStream_t stream);
+
+/*
+ * Dense fp16 product C = fp16(X W), fp16 MFMA with fp32 accumulation, one
+ * round-to-nearest-even rounding per output ([DIGEST] "Runtime Performance
+ * (Appendix D)", the FP16 baseline of Table 5). The same main loop as the
+ * int8 product, run on 2-byte elements.
+ * X: [s, h] fp16; Wp: from i8mm_pack_fp16_weights; C: [s, o] fp16 (written).
+ */
+i8mm_status i8mm_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, int64_t h, int64_t o, uint16_t* C,
+                           hipStream_t stream);
+
 /* Bytes at the start of the forward workspace that hold the cross-block
  * accumulator of the detection (the outlier mask being ORed together, or,
  * for inputs of at most 64 rows, the per-row maxima). */

@@ -28,6 +28,8 @@ __all__ = [
     "outlier_matmul",
     "int8_gemm_i32",
     "forward",
+    "pack_fp16_weights",
+    "fp16_gemm",
     "forward_workspace",
     "forward_workspace_views",
     "x_o_stride",
@@ -214,6 +216,33 @@ def int8_gemm_i32(Xq: torch.Tensor, Wq: torch.Tensor, C: Optional[torch.Tensor] 
         _dev(Xq, "Xq", torch.int8), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)), s, h, o,
         _dev(C, "C", torch.int32, (s, o)), _stream(Xq))
     _check(st, "int8_gemm_i32")
+    return C
+
+
+def pack_fp16_weights(W: torch.Tensor, Wp: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Load-time packing for the dense fp16 baseline: W fp16 [h, o] -> Wp fp16
+    [h/32, o, 32] (W[k, j] at Wp[k // 32, j, k % 32])."""
+    h, o = W.shape
+    if h % 32 != 0:
+        raise ValueError(f"h must be a multiple of 64 (got {h})")
+    shape = (h // 32, o, 32)
+    if Wp is None:
+        Wp = torch.empty(shape, dtype=torch.float16, device=W.device)
+    st = _lib.i8mm_pack_fp16_weights(_dev(W, "W", torch.float16), h, o, _dev(Wp, "Wp", torch.float16, shape),
+                                     _stream(W))
+    _check(st, "pack_fp16_weights")
+    return Wp
+
+
+def fp16_gemm(X: torch.Tensor, Wp: torch.Tensor, C: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense fp16 baseline C fp16 [s, o] = fp16(X W) (fp32 accumulation) from packed Wp."""
+    s, h = X.shape
+    o = Wp.shape[1]
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.float16, device=X.device)
+    st = _lib.i8mm_fp16_gemm(_dev(X, "X", torch.float16), _dev(Wp, "Wp", torch.float16, (h // 32, o, 32)),
+                             s, h, o, _dev(C, "C", torch.float16, (s, o)), _stream(X))
+    _check(st, "fp16_gemm")
     return C
 
 

@@ -34,6 +34,9 @@ bool valid_o(int64_t o) { return o >= 64 && o % 64 == 0 && o <= (int64_t(1) << 3
 // only) through 32-bit buffer offsets.
 bool valid_w_extent(int64_t h, int64_t o) { return h * o < (int64_t(1) << 31); }
 
+// The dense fp16 product addresses Wp (2 h o bytes) with 32-bit offsets.
+bool valid_fp16_extent(int64_t h, int64_t o) { return 2 * h * o < (int64_t(1) << 31); }
+
 i8mm_status check_device() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
@@ -166,6 +169,23 @@ i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t s, in
     if (i8mm_status d = check_device()) return d;
     return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::Int32, Xq, nullptr, nullptr, 0, nullptr, nullptr, Wq,
                                            nullptr, nullptr, s, h, o, C_i32, stream));
+}
+
+i8mm_status i8mm_pack_fp16_weights(const uint16_t* W, int64_t h, int64_t o, uint16_t* Wp, hipStream_t stream) {
+    if (!W || !Wp) return I8MM_EINVAL;
+    if (!valid_shape_sh(1, h) || !valid_o(o) || !valid_fp16_extent(h, o)) return I8MM_EINVAL;
+    if (!aligned16(W) || !aligned16(Wp)) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_pack_fp16_panels(W, h, o, Wp, stream));
+}
+
+i8mm_status i8mm_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, int64_t h, int64_t o, uint16_t* C,
+                           hipStream_t stream) {
+    if (!X || !Wp || !C) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_fp16_extent(h, o)) return I8MM_EINVAL;
+    if (!aligned16(X) || !aligned16(Wp) || !aligned16(C)) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_fp16_gemm(X, Wp, s, h, o, C, stream));
 }
 
 size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h) {

@@ -30,6 +30,8 @@
 // outlier product on top with fp16 MFMA (fp32 accumulate) and rounds once
 // to fp16.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -161,7 +163,9 @@ constexpr int kOutRow = 136;
 constexpr int kOutWave = 32 * kOutRow;          // halves per wavefront
 constexpr int kMaxOnceSlices = 5;               // extra slices staged at once
 
-// Prefill main loop: both operand tiles reach LDS through direct-to-LDS
+// Prefill main loop (also the dense fp16 product, MODE Fp16Dense: the same
+// byte geometry with 2-byte elements, see launch_fp16_gemm): both operand
+// tiles reach LDS through direct-to-LDS
 // buffer loads, double buffered in four separate arrays (A0/A1 weights,
 // B0/B1 activations) so that the compiler's wait tracking for these loads
 // can tell the buffer being filled from the one being read. A stage's
@@ -172,7 +176,7 @@ constexpr int kMaxOnceSlices = 5;               // extra slices staged at once
 template <GemmOut MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
-                    int64_t s, int64_t h, int64_t o,
+                    int64_t s, int64_t h /* reduction bytes per row */, int64_t o,
                     const float* __restrict__ c_x, const float* __restrict__ c_w,
                     const uint16_t* __restrict__ X_O, int64_t ldo,
                     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out,
@@ -254,7 +258,9 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         }
     }
 
-    v16i acc[4][4];
+    constexpr bool dense16 = MODE == GemmOut::Fp16Dense;
+    using Acc = std::conditional_t<dense16, v16f, v16i>;
+    Acc acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -278,12 +284,20 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 #pragma unroll
         for (int i = 0; i < 4; ++i) b[i] = B[offB[kk] + 256 * i];
     };
+    // A sub-step is 32 reduction bytes per row: 32 int8 codes for
+    // v_mfma_i32_32x32x32_i8, or 16 fp16 values for v_mfma_f32_32x32x16_f16,
+    // whose lane fragments sit in the same 16-byte slots.
     auto mma = [&](const v4i* a, const v4i* b) {
 #pragma unroll
         for (int ob = 0; ob < 4; ++ob)
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb)
-                acc[ob][sb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ob], b[sb], acc[ob][sb], 0, 0, 0);
+            for (int sb = 0; sb < 4; ++sb) {
+                if constexpr (dense16)
+                    acc[ob][sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a[ob]),
+                                                                         __builtin_bit_cast(v8h, b[sb]), acc[ob][sb], 0, 0, 0);
+                else
+                    acc[ob][sb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[ob], b[sb], acc[ob][sb], 0, 0, 0);
+            }
     };
     // One sub-step's order: MFMAs interleaved with the next sub-step's LDS
     // reads and with this part's loads.
@@ -348,7 +362,37 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 
     // Lane layout of a 32x32 accumulator: register r holds
     // D[o = 8 (r / 4) + 4 (lane / 32) + r % 4][s = lane % 32].
-    if constexpr (MODE == GemmOut::Int32) {
+    if constexpr (dense16) {
+        // fp32 accumulators rounded once to fp16, staged per 32-row block and
+        // written as full 256-byte rows.
+        uint16_t* C = static_cast<uint16_t*>(Cout);
+        __syncthreads();   // every wavefront is done with the stage buffers
+        uint16_t* out_st = wid < 3 ? reinterpret_cast<uint16_t*>(A1) + wid * kOutWave : reinterpret_cast<uint16_t*>(B1);
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const v16f& f = acc[ob][sb];
+                    const uint32_t lo = float_to_half_bits(f[4 * g]) |
+                                        (static_cast<uint32_t>(float_to_half_bits(f[4 * g + 1])) << 16);
+                    const uint32_t hi = float_to_half_bits(f[4 * g + 2]) |
+                                        (static_cast<uint32_t>(float_to_half_bits(f[4 * g + 3])) << 16);
+                    *reinterpret_cast<uint2*>(out_st + r32 * kOutRow + ob * 32 + 8 * g + 4 * khalf) =
+                        make_uint2(lo, hi);
+                }
+            }
+            const int64_t gcol = o0 + wo * 128 + (lane & 15) * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 4 * i + (lane >> 4);
+                const v4i v = *reinterpret_cast<const v4i*>(out_st + row * kOutRow + (lane & 15) * 8);
+                const int64_t grow = s0 + ws * 128 + sb * 32 + row;
+                if (grow < s && gcol < o) *reinterpret_cast<v4i*>(C + grow * o + gcol) = v;
+            }
+        }
+    } else if constexpr (MODE == GemmOut::Int32) {
         int32_t* C = static_cast<int32_t*>(Cout);
 #pragma unroll
         for (int ob = 0; ob < 4; ++ob)
@@ -672,6 +716,16 @@ hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                                            clear, clear_words);
     return launch_mode<GemmOut::Mixed>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, s, h, o, C, stream,
                                        clear, clear_words);
+}
+
+hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, int64_t h, int64_t o, uint16_t* C,
+                            hipStream_t stream) {
+    // Rows of X and the 64-byte panels of Wp hold 2 h reduction bytes.
+    const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
+    hipLaunchKernelGGL((k_gemm_prefill<GemmOut::Fp16Dense>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
+                       reinterpret_cast<const int8_t*>(X), reinterpret_cast<const int8_t*>(Wp), s, 2 * h, o,
+                       nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, C, nullptr, 0);
+    return hipGetLastError();
 }
 
 hipError_t launch_outlier_matmul(const uint16_t* X_O, int64_t ldo, const int32_t* idx, const int32_t* n_out,

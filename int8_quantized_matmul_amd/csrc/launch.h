@@ -31,7 +31,7 @@ hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
 // mode: product variant of the shared int8 main loop. `clear` (optional):
 // clear_words uint32 words that the first block zeroes (the forward path's
 // accumulator, whose readers have finished by then).
-enum class GemmOut { Mixed = 0, Int32 = 1 };
+enum class GemmOut { Mixed = 0, Int32 = 1, Fp16Dense = 2 };
 
 hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                             const uint16_t* X_O, int64_t ldo,
@@ -39,6 +39,13 @@ hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                             const int8_t* Wq, const float* c_w, const uint16_t* W,
                             int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
                             uint32_t* clear = nullptr, int clear_words = 0);
+
+// Dense fp16 product C = fp16(X W) with fp32 accumulation; Wp is W in the
+// fp16 panel layout [h / 32][o][32] (see launch_pack_fp16_panels).
+hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, int64_t h, int64_t o, uint16_t* C,
+                            hipStream_t stream);
+
+hipError_t launch_pack_fp16_panels(const uint16_t* W, int64_t h, int64_t o, uint16_t* Wp, hipStream_t stream);
 
 hipError_t launch_outlier_matmul(const uint16_t* X_O, int64_t ldo,
                                  const int32_t* idx, const int32_t* n_out,

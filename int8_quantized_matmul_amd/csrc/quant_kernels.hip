@@ -533,6 +533,30 @@ __global__ __launch_bounds__(256) void k_quant_cols(const uint16_t* __restrict__
     }
 }
 
+// ---------------------------------------------------------------------------
+// Load-time packing of fp16 W [h, o] for the dense fp16 product into the
+// fp16 panel layout Wp [h / 32][o][32] (W[k, j] at element
+// (k / 32) o 32 + 32 j + k % 32): the same 64-byte run per column and panel
+// as the int8 layout, holding 32 reduction rows. One block per (64-column
+// strip, 32-row panel); the 32 x 64 tile is transposed through LDS and
+// written as the strip's contiguous 4 KiB of the panel.
+__global__ __launch_bounds__(256) void k_pack_fp16_panels(const uint16_t* __restrict__ W, int64_t o,
+                                                          uint16_t* __restrict__ Wp) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[64][40];   // [column][row], rows padded to 80 bytes
+    const int t = threadIdx.x;
+    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 64;
+    const int64_t p = blockIdx.y;
+    const int row = t >> 3, ch = t & 7;
+    const uint4 v = load_chunk(W + (p * 32 + row) * o + j0 + ch * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        tile[ch * 8 + e][row] = static_cast<uint16_t>(word_of(v, e >> 1) >> ((e & 1) * 16));
+    __syncthreads();
+    const int col = t >> 2, seg = t & 3;
+    *reinterpret_cast<uint4*>(Wp + (p * o + j0 + col) * 32 + seg * 8) =
+        *reinterpret_cast<const uint4*>(&tile[col][seg * 8]);
+}
+
 }  // namespace
 
 namespace {
@@ -632,6 +656,12 @@ hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, floa
     hipError_t e = launch_detect_into(X, s, h, alpha, acc, stream);
     if (e != hipSuccess) return e;
     return launch_rows(X, s, h, acc, mask, idx, n_out, Xq, c_x, X_O, ldo, stream);
+}
+
+hipError_t launch_pack_fp16_panels(const uint16_t* W, int64_t h, int64_t o, uint16_t* Wp, hipStream_t stream) {
+    hipLaunchKernelGGL(k_pack_fp16_panels, dim3(static_cast<unsigned>(o / 64), static_cast<unsigned>(h / 32)),
+                       dim3(256), 0, stream, W, o, Wp);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,

@@ -42,6 +42,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 __all__ = [
+    "fp16_matmul",
     "outlier_columns",
     "mask_from_indices",
     "row_scales",
@@ -232,6 +233,23 @@ def int8_mixed_matmul(Xq: np.ndarray, c_x: np.ndarray, X_O: np.ndarray, idx: np.
         Ci = int8_matmul_i32(Xq, Wq_t[j0:j1], col_chunk=col_chunk)
         CO = outlier_matmul(X_O, W_f16[:, j0:j1], idx)
         C[:, j0:j1] = dequantize_and_add(Ci, c_x, c_w[j0:j1], CO)
+    return C
+
+
+def fp16_matmul(X_f16: np.ndarray, W_f16: np.ndarray, col_chunk: int = 4096) -> np.ndarray:
+    """The FP16 baseline of [DIGEST] "Runtime Performance (Appendix D)"
+    (Table 5 reports every variant as a speed-up over the FP16 matrix
+    multiply of the same layer): C = fp16(X W), the product taken in float64
+    and rounded once to fp16 (round to nearest even).
+
+    Each float64 product of two fp16 values is exact; the sum over h is
+    rounded in float64, far below one fp16 ulp of the result.
+    """
+    Xd = X_f16.astype(np.float64)
+    o = W_f16.shape[1]
+    C = np.empty((X_f16.shape[0], o), np.float16)
+    for j0 in range(0, o, col_chunk):
+        C[:, j0:j0 + col_chunk] = (Xd @ W_f16[:, j0:j0 + col_chunk].astype(np.float64)).astype(np.float16)
     return C
 
 

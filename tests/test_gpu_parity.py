@@ -220,3 +220,45 @@ def test_bad_arguments_raise():
         i8.detect_outlier_cols(X)
     with pytest.raises(ValueError):
         i8.detect_outlier_cols(torch.zeros((4, 64), dtype=torch.float32, device=DEV))
+
+
+# Dense fp16 baseline (Table 5's FP16 reference): packing is a pure layout
+# change (exact); the product is checked against the oracle's fp16(X W).
+FP16 = [(1, 64, 64), (17, 192, 320), (40, 64, 320), (300, 1088, 448), (513, 384, 768), (16, 1024, 512)]
+
+
+@pytest.mark.parametrize("s,h,o", FP16, ids=[f"s{c[0]}h{c[1]}o{c[2]}" for c in FP16])
+def test_fp16_gemm_matches_oracle(s, h, o):
+    rng = np.random.default_rng(s + h + o)
+    X = rng.standard_normal((s, h)).astype(np.float16)
+    W = (rng.standard_normal((h, o)) * 0.02).astype(np.float16)
+    Xd, Wd = T(X), T(W)
+    say(f"  launch: fp16 pack + gemm s={s} h={h} o={o}")
+    Wp = i8.pack_fp16_weights(Wd)
+    C = i8.fp16_gemm(Xd, Wp)
+    torch.cuda.synchronize()
+    assert np.array_equal(H(Wp).transpose(1, 0, 2).reshape(o, h), W.T)
+    check_C(C, oracle.fp16_matmul(X, W))
+    C2 = i8.fp16_gemm(Xd, Wp)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2)
+
+
+def test_fp16_gemm_full_size_sampled():
+    """The 2048 x 4096 x 16384 layer of the prefill benchmark, sampled rows x
+    columns against the oracle."""
+    s, h, o = 2048, 4096, 16384
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    Xd = torch.randn((s, h), generator=g, device=DEV).half()
+    Wd = (0.02 * torch.randn((h, o), generator=g, device=DEV)).half()
+    say("  launch: fp16 pack + gemm 2048x4096x16384")
+    Wp = i8.pack_fp16_weights(Wd)
+    C = i8.fp16_gemm(Xd, Wp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, s - 1], rng.choice(s, 30, replace=False)]))
+    cols = np.unique(np.concatenate([[0, o - 1], rng.choice(o, 200, replace=False)]))
+    X, W = H(Xd), H(Wd)
+    ref = oracle.fp16_matmul(X[rows], W[:, cols])
+    check_C(C.index_select(0, torch.from_numpy(rows).to(DEV)).index_select(1, torch.from_numpy(cols).to(DEV)), ref)

@@ -367,3 +367,31 @@ def test_generator_plants_exact_outlier_sets():
         inp = make_inputs(get_config(name), with_W=False)
         _, idx, _ = oracle.outlier_columns(inp["X"], 6.0)
         assert idx.tolist() == sorted(inp["planted"].tolist())
+
+
+@pytest.mark.parametrize("seed,s,h,o", [(11, 3, 64, 8), (12, 5, 128, 4), (13, 2, 192, 6)])
+def test_fp16_baseline_is_exact_product_rounded_once(seed, s, h, o):
+    """The FP16 baseline of Table 5 ([DIGEST] 'Runtime Performance (Appendix
+    D)'): fp16_matmul equals the exact rational product X W rounded once to
+    fp16 (round to nearest even, written from the IEEE definition)."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((s, h)).astype(np.float16)
+    W = (rng.standard_normal((h, o)) * 0.05).astype(np.float16)
+    got = oracle.fp16_matmul(X, W)
+    Xf, Wf = rational.to_fractions(X), rational.to_fractions(W)
+    for i in range(s):
+        for j in range(o):
+            exact = sum(Xf[i][k] * Wf[k][j] for k in range(h))
+            assert Fraction(float(got[i, j])) == rational.fl16(exact), (i, j)
+
+
+def test_fp16_baseline_equals_full_decomposition():
+    """With alpha = 0 every column is an outlier and the decomposition is the
+    plain fp16 product: forward(alpha=0) and fp16_matmul agree bit for bit
+    (two independent routes through the oracle)."""
+    rng = np.random.default_rng(14)
+    X = rng.standard_normal((9, 320)).astype(np.float16)
+    W = (rng.standard_normal((320, 40)) * 0.02).astype(np.float16)
+    a = oracle.fp16_matmul(X, W, col_chunk=16)
+    b = oracle.forward(X, W, alpha=0.0)["C"]
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
