@@ -190,11 +190,13 @@ def run_prefill(i8, torch, w, steps, warmup, dev):
 
     cold_ms = timed_ms(torch, steps, cold_step, warmup=copies)
     del sets
+    # without a resident fp16 W: outlier rows rebuilt from the int8 codes
+    w8_ms = timed_ms(torch, steps, lambda: i8.forward(X, Wq, c_w, None, w.alpha, workspace=ws, C=C))
     # the step's intermediates again for anything that reads them later
     step()
     torch.cuda.synchronize()
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out,
-                inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies)
+                inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies, w8_ms=w8_ms)
 
 
 def run_decode(i8, torch, w, steps, warmup, dev):
@@ -222,7 +224,8 @@ def run_decode(i8, torch, w, steps, warmup, dev):
         v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
     n_out = int(v["n_out"].cpu()[0])
     weight_bytes = h * o + 2 * n_out * o + 4 * o
-    return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes)
+    w8_ms = timed_ms(torch, steps, lambda: i8.forward(X, Wq, c_w, None, w.alpha, workspace=ws, C=C))
+    return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, w8_ms=w8_ms)
 
 
 # The pages' Table 5 (raw matmul of the first FFN layer of GPT-3 models, X [s, d]
@@ -395,6 +398,7 @@ def main(argv=None):
         "step_ms_percentiles": pre["pct"],
         "step_ms_weights_from_hbm": {"ms": round(pre["cold_ms"], 5), "weight_copies_rotated": pre["copies"]},
         "table5_comparison": pre["table5"],
+        "without_fp16_weights": _w8_entry(pre["w8_ms"], h, o, pre["step_ms"]),
         "weight_conversion": {"ms": round(pre["conv_ms"], 4),
                               "GB_per_s": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1)},
     }
@@ -413,6 +417,7 @@ def main(argv=None):
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "product_kernel_ms": round(dec["gemm_ms"], 5),
             "product_kernel_weight_GB_per_s": round(gbs_gemm, 1),
+            "without_fp16_weights": _w8_entry(dec["w8_ms"], wd.h, wd.o, dec["step_ms"]),
         }
 
     if not args.no_cpu_baseline:
@@ -420,6 +425,15 @@ def main(argv=None):
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def _w8_entry(ms, h, o, step_ms):
+    """The step with no resident fp16 W (outlier rows rebuilt from Wq / c_w)
+    and the weight bytes each storage keeps resident."""
+    return {"ms_per_step": round(ms, 5), "vs_with_fp16_weights": round(ms / step_ms, 3),
+            "resident_weight_bytes": h * o + 4 * o,
+            "resident_weight_bytes_with_fp16_W": 3 * h * o + 4 * o,
+            "memory_reduction_vs_fp16_weights": round(2 * h * o / (h * o + 4 * o), 3)}
 
 
 def _kernel_sha():

@@ -148,8 +148,13 @@ i8mm_status i8mm_quantize_rowwise(const uint16_t* X, int64_t s, int64_t h,
  *
  * Xq: [s, h] int8; c_x: [s] fp32; X_O: [s, ldo] fp16 (ldo as above);
  * idx, n_out: as from i8mm_detect_outlier_cols; Wq: panel layout (above);
- * c_w: [o] fp32; W: [h, o] fp16 (the original weights);
- * C: [s, o] fp16 (written).
+ * c_w: [o] fp32; C: [s, o] fp16 (written).
+ * W: [h, o] fp16, the original weights, or NULL when no fp16 copy of W is
+ * kept: the outlier rows are then rebuilt from the int8 codes,
+ * W[k, j] = fp16(W_i8[k, j] / c_w[j]) (one IEEE division, one rounding), so
+ * only Wq and c_w stay resident: about half the weight memory, the saving
+ * the pages measure on BLOOM-176B ([DIGEST] "Executive Summary"; [PY]
+ * "第二件武器：混合精度分解"); the outlier product then sees the 8-bit weights.
  */
 i8mm_status i8mm_int8_mixed_matmul(const int8_t* Xq, const float* c_x,
                                    const uint16_t* X_O, int64_t ldo,
@@ -230,8 +235,8 @@ size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h);
  * workspace may be reused for any shape whose size fits. Calls that share a
  * workspace must not overlap. After completion the workspace holds the
  * intermediates at the offsets given by i8mm_forward_workspace_layout.
- * X: [s, h] fp16; Wq: panel layout (above); c_w: [o] fp32; W: [h, o] fp16;
- * C: [s, o] fp16 (written).
+ * X: [s, h] fp16; Wq: panel layout (above); c_w: [o] fp32; W: [h, o] fp16
+ * or NULL (as for i8mm_int8_mixed_matmul); C: [s, o] fp16 (written).
  */
 i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
                          const int8_t* Wq, const float* c_w, const uint16_t* W,

@@ -138,7 +138,7 @@ i8mm_status i8mm_int8_mixed_matmul(const int8_t* Xq, const float* c_x, const uin
                                    const int32_t* idx, const int32_t* n_out,
                                    const int8_t* Wq, const float* c_w, const uint16_t* W,
                                    int64_t s, int64_t h, int64_t o, uint16_t* C, hipStream_t stream) {
-    if (!Xq || !c_x || !X_O || !idx || !n_out || !Wq || !c_w || !W || !C) return I8MM_EINVAL;
+    if (!Xq || !c_x || !X_O || !idx || !n_out || !Wq || !c_w || !C) return I8MM_EINVAL;   // W may be null
     if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
     if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
     if (!aligned16(Xq) || !aligned16(c_x) || !aligned16(X_O) || !aligned16(idx) || !aligned16(n_out) ||
@@ -206,7 +206,7 @@ i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[7
 i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
                          const int8_t* Wq, const float* c_w, const uint16_t* W,
                          void* workspace, uint16_t* C, hipStream_t stream) {
-    if (!X || !Wq || !c_w || !W || !workspace || !C) return I8MM_EINVAL;
+    if (!X || !Wq || !c_w || !workspace || !C) return I8MM_EINVAL;   // W may be null
     if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
     if (std::isnan(alpha) || alpha < 0.0f) return I8MM_EINVAL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;

@@ -96,22 +96,57 @@ __device__ __forceinline__ void stage_outlier_slice(int kb, int n, int wid, int 
                                                     int64_t s, int64_t o, int64_t ldo,
                                                     const int32_t* __restrict__ idx,
                                                     __amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rX,
-                                                    uint16_t* dst) {
+                                                    uint16_t* dst, bool with_w = true) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int j = wid + 4 * q;                 // wave-uniform, 0..7
-        const int k0 = kb * 16 + 2 * j;            // rows k0 (lanes 0-31) and k0 + 1 (lanes 32-63)
-        const int id0 = idx[k0], id1 = idx[k0 + 1];
-        const int k = k0 + (lane >> 5);
-        const int64_t col = o0 + (lane & 31) * 8;
-        const bool okW = k < n && col < o;
-        const uint32_t vW = okW ? static_cast<uint32_t>(((lane >> 5) ? id1 : id0) * o * 2 + (lane & 31) * 16)
-                                : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, LDS_PTR(dst + j * 512), 16, vW, 0, 0, 0);
+        if (with_w) {
+            const int k0 = kb * 16 + 2 * j;        // rows k0 (lanes 0-31) and k0 + 1 (lanes 32-63)
+            const int id0 = idx[k0], id1 = idx[k0 + 1];
+            const int k = k0 + (lane >> 5);
+            const int64_t col = o0 + (lane & 31) * 8;
+            const bool okW = k < n && col < o;
+            const uint32_t vW = okW ? static_cast<uint32_t>(((lane >> 5) ? id1 : id0) * o * 2 + (lane & 31) * 16)
+                                    : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, LDS_PTR(dst + j * 512), 16, vW, 0, 0, 0);
+        }
         const int r = 32 * j + (lane >> 1);
         const uint32_t vX = s0 + r < s ? static_cast<uint32_t>(r * ldo * 2 + (kb * 16 + (lane & 1) * 8) * 2)
                                        : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, LDS_PTR(dst + kSlice + j * 512), 16, vX, 0, 0, 0);
+    }
+}
+
+// An outlier row's weight W[k, j] when no fp16 copy of W is resident: the
+// int8 code of the panel layout times the column's reciprocal scale
+// inv_cw = 1 / c_w[j] (to 1 ulp), rounded once to fp16 - within one fp16
+// ulp of the rounded quotient code / c_w, and exact whenever the
+// quantisation of the column was (power-of-two c_w, codes reproducing W).
+__device__ __forceinline__ uint16_t dequantized_weight(const int8_t* __restrict__ Wq, float inv_cw, int64_t k,
+                                                       int64_t j, int64_t o) {
+    const int q = Wq[(k >> 6) * o * 64 + j * 64 + (k & 63)];
+    return float_to_half_bits(static_cast<float>(q) * inv_cw);
+}
+
+// The W part of slice kb rebuilt from the int8 codes, written directly in
+// the transposed layout of transpose_w_slice (column t of the tile holds
+// its 16 rows idx[16 kb .. 16 kb + 15] as two 16-byte halves). Thread t
+// owns column o0 + t; rows past |O| and columns past o are zero.
+__device__ __forceinline__ void stage_w8_slice(int kb, int n, int64_t o0, int64_t o,
+                                               const int32_t* __restrict__ idx, const int8_t* __restrict__ Wq,
+                                               const float* __restrict__ c_w, uint16_t* dst) {
+    const int t = threadIdx.x;
+    const int64_t j = o0 + t;
+    const bool col_ok = j < o;
+    const float inv_cw = __builtin_amdgcn_rcpf(col_ok ? c_w[j] : 1.0f);
+    const int sw = (t >> 3) & 1;
+    // A rolled loop with 2-byte LDS writes keeps this small: it is inlined
+    // into every output block of the epilogue's rounds path.
+#pragma unroll 1
+    for (int e = 0; e < 16; ++e) {
+        const int k = kb * 16 + e;
+        const uint16_t w = col_ok && k < n ? dequantized_weight(Wq, inv_cw, idx[k], j, o) : static_cast<uint16_t>(0);
+        dst[(t * 2 + ((e >> 3) ^ sw)) * 8 + (e & 7)] = w;
     }
 }
 
@@ -239,13 +274,17 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     // loads complete under the main loop.
     int n_o = 0;
     constexpr bool mixed = MODE == GemmOut::Mixed;
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(mixed ? W + o0 : nullptr, mixed ? static_cast<uint32_t>((h * o - o0) * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(mixed && W ? W + o0 : nullptr,
+                                                mixed && W ? static_cast<uint32_t>((h * o - o0) * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(mixed ? X_O + s0 * ldo : nullptr,
                                                 mixed ? static_cast<uint32_t>(s_rows * ldo * 2) : 0u);
     float cx_pf[4], cw_pf[2];
+    // Without a resident fp16 W (W null) the outlier rows are rebuilt from
+    // the int8 codes in the epilogue; only their X part is staged here.
+    const bool w8 = W == nullptr;
     if constexpr (mixed) {
         n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
-        if (n_o > 0) stage_outlier_slice(0, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, olds);
+        if (n_o > 0) stage_outlier_slice(0, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, olds, !w8);
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             const int64_t srow = s0 + ws * 128 + sb * 32 + r32;
@@ -425,14 +464,18 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         float* invw = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(B1) + kOutWave) + wid * 128;
         const int nsl = (n_o + 15) / 16;
         const bool once = nsl <= 1 + kMaxOnceSlices;
-        if (once)
-            for (int q = 1; q < nsl; ++q) stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q));
+        if (once) {
+            for (int q = 1; q < nsl; ++q)
+                stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q), !w8);
+            if (w8)
+                for (int q = 0; q < nsl; ++q) stage_w8_slice(q, n_o, o0, o, idx, Wq, c_w, q ? slice_at(q) : olds);
+        }
         // 1 / c_w of the wave's 128 columns (reciprocals to 1 ulp)
 #pragma unroll
         for (int i = 0; i < 2; ++i) invw[lane + 64 * i] = __builtin_amdgcn_rcpf(cw_pf[i]);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (once) {
+        if (once && !w8) {
             // W parts transposed once, so that both MFMA operands are 16-byte reads
             if (nsl > 0) transpose_w_slice(olds);
             for (int q = 1; q < nsl; ++q) transpose_w_slice(slice_at(q));
@@ -459,17 +502,23 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     if (nsl > 0) f = apply_outlier_slice_t(olds, wo, ws, sb, ob, r32, khalf, f);
                     for (int q = 1; q < nsl; ++q) f = apply_outlier_slice_t(slice_at(q), wo, ws, sb, ob, r32, khalf, f);
                 } else {
-                    // more than 96 outlier columns: further slices in rounds
-                    f = apply_outlier_slice(olds, wo, ws, sb, ob, r32, khalf, f);
-                    for (int rb = 1; rb < nsl; rb += kMaxOnceSlices) {
+                    // more than 96 outlier columns: slices in rounds (slice 0
+                    // from olds when the fp16 rows were staged there; rebuilt
+                    // rows arrive already transposed)
+                    if (!w8) f = apply_outlier_slice(olds, wo, ws, sb, ob, r32, khalf, f);
+                    for (int rb = w8 ? 0 : 1; rb < nsl; rb += kMaxOnceSlices) {
                         const int re = rb + kMaxOnceSlices < nsl ? rb + kMaxOnceSlices : nsl;
                         __syncthreads();
-                        for (int q = rb; q < re; ++q)
-                            stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q - rb + 1));
+                        for (int q = rb; q < re; ++q) {
+                            stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q - rb + 1),
+                                                !w8);
+                            if (w8) stage_w8_slice(q, n_o, o0, o, idx, Wq, c_w, slice_at(q - rb + 1));
+                        }
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                         __syncthreads();
                         for (int q = rb; q < re; ++q)
-                            f = apply_outlier_slice(slice_at(q - rb + 1), wo, ws, sb, ob, r32, khalf, f);
+                            f = w8 ? apply_outlier_slice_t(slice_at(q - rb + 1), wo, ws, sb, ob, r32, khalf, f)
+                                   : apply_outlier_slice(slice_at(q - rb + 1), wo, ws, sb, ob, r32, khalf, f);
                     }
                 }
                 // Round once to fp16 and stage in this wavefront's LDS area
@@ -511,7 +560,8 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 __device__ __forceinline__ void outlier_operands_16(int kb, int n, int lane, int64_t ocol0, int64_t srow0,
                                                     int64_t s, int64_t o, const uint16_t* __restrict__ X_O,
                                                     int64_t ldo, const int32_t* __restrict__ idx,
-                                                    const uint16_t* __restrict__ W, v8h& wa, v8h& xb) {
+                                                    const uint16_t* __restrict__ W, const int8_t* __restrict__ Wq,
+                                                    const float* __restrict__ c_w, v8h& wa, v8h& xb) {
     int id[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) id[j] = idx[kb * 32 + j];     // uniform address: scalar loads
@@ -519,13 +569,16 @@ __device__ __forceinline__ void outlier_operands_16(int kb, int n, int lane, int
     const int kbase = kb * 32 + 8 * g;
     const int64_t ocol = ocol0 + (lane & 15);
     const bool col_ok = ocol < o;
+    // without a resident fp16 W the rows are rebuilt from the int8 codes
+    const float inv_cw = __builtin_amdgcn_rcpf(W == nullptr && col_ok ? c_w[ocol] : 1.0f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const bool ok = col_ok && kbase + e < n;
         const int sel = g == 0 ? id[e] : g == 1 ? id[8 + e] : g == 2 ? id[16 + e] : id[24 + e];
         const int row = ok ? sel : 0;
-        const uint16_t bits = W[static_cast<int64_t>(row) * o + (col_ok ? ocol : 0)];
-        wa[e] = __builtin_bit_cast(_Float16, ok ? bits : static_cast<uint16_t>(0));
+        uint16_t bits = 0;
+        if (ok) bits = W != nullptr ? W[static_cast<int64_t>(row) * o + ocol] : dequantized_weight(Wq, inv_cw, row, ocol, o);
+        wa[e] = __builtin_bit_cast(_Float16, bits);
     }
     const int64_t srow = srow0 + (lane & 15);
     const bool rok = srow < s;
@@ -539,14 +592,15 @@ __device__ __forceinline__ void outlier_operands_16(int kb, int n, int lane, int
 __device__ __forceinline__ v4f outlier_tile_16x16(v4f f, int lane, int64_t ocol0, int64_t srow0, int64_t s,
                                                    int64_t o, const uint16_t* __restrict__ X_O, int64_t ldo,
                                                    const int32_t* __restrict__ idx, int n,
-                                                   const uint16_t* __restrict__ W, const v8h* first) {
+                                                   const uint16_t* __restrict__ W, const int8_t* __restrict__ Wq,
+                                                   const float* __restrict__ c_w, const v8h* first) {
     for (int kb = 0; kb * 32 < n; ++kb) {
         v8h wa, xb;
         if (kb == 0 && first != nullptr) {
             wa = first[0];
             xb = first[1];
         } else {
-            outlier_operands_16(kb, n, lane, ocol0, srow0, s, o, X_O, ldo, idx, W, wa, xb);
+            outlier_operands_16(kb, n, lane, ocol0, srow0, s, o, X_O, ldo, idx, W, Wq, c_w, wa, xb);
         }
         f = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, xb, f, 0, 0, 0);
     }
@@ -593,7 +647,7 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     if constexpr (MODE == GemmOut::Mixed) {
         n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
         if (wid < NT && n_o > 0)
-            outlier_operands_16(0, n_o, lane, obase + wid * 16, 0, s, o, X_O, ldo, idx, W, pre[0], pre[1]);
+            outlier_operands_16(0, n_o, lane, obase + wid * 16, 0, s, o, X_O, ldo, idx, W, Wq, c_w, pre[0], pre[1]);
     }
 
     const int64_t nsteps = h / 64;
@@ -656,7 +710,7 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
         v4f f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
-        f = outlier_tile_16x16(f, lane, obase + nt * 16, 0, s, o, X_O, ldo, idx, n_o, W, pre);
+        f = outlier_tile_16x16(f, lane, obase + nt * 16, 0, s, o, X_O, ldo, idx, n_o, W, Wq, c_w, pre);
         if (srow < s) {
             const uint32_t lo = float_to_half_bits(f[0]) | (static_cast<uint32_t>(float_to_half_bits(f[1])) << 16);
             const uint32_t hi = float_to_half_bits(f[2]) | (static_cast<uint32_t>(float_to_half_bits(f[3])) << 16);
@@ -681,7 +735,7 @@ __global__ __launch_bounds__(256) void k_outlier_only(const uint16_t* __restrict
     const int r16 = lane & 15, g = lane >> 4;
     const int64_t srow = ts_i * 16 + r16;
     v4f f = {0.f, 0.f, 0.f, 0.f};
-    f = outlier_tile_16x16(f, lane, to_i * 16, ts_i * 16, s, o, X_O, ldo, idx, n_out[0], W, nullptr);
+    f = outlier_tile_16x16(f, lane, to_i * 16, ts_i * 16, s, o, X_O, ldo, idx, n_out[0], W, nullptr, nullptr, nullptr);
     const int64_t ocol = to_i * 16 + 4 * g;
     if (srow < s) *reinterpret_cast<v4f*>(C_O + srow * o + ocol) = f;
 }

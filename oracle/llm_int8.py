@@ -43,6 +43,7 @@ import numpy as np
 
 __all__ = [
     "fp16_matmul",
+    "dequantized_outlier_rows",
     "outlier_columns",
     "mask_from_indices",
     "row_scales",
@@ -221,17 +222,34 @@ def dequantize_and_add(C_i32: np.ndarray, c_x: np.ndarray, c_w: np.ndarray,
     return C.astype(np.float16)
 
 
+def dequantized_outlier_rows(Wq_t: np.ndarray, c_w: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Outlier rows W^O when no fp16 copy of W is kept (a storage variant; the
+    pages' Step 3 uses the original fp16 rows, [DIGEST] "The Full LLM.int8()
+    Algorithm"): W^O[k, j] = fl16(W_i8[idx[k], j] / c_w[j]), the int8 code
+    divided by its column scale (quotient in float64), rounded to fp16.
+    Only the int8 weights and their scales then stay resident, the memory
+    saving of [DIGEST] "Executive Summary" (1.96x on BLOOM-176B)."""
+    idx = np.asarray(idx, dtype=np.int64)
+    q = Wq_t[:, idx].T.astype(F64)                        # [|O|, o]
+    return (q / c_w.astype(F64)[None, :]).astype(np.float16)
+
+
 def int8_mixed_matmul(Xq: np.ndarray, c_x: np.ndarray, X_O: np.ndarray, idx: np.ndarray,
-                      Wq_t: np.ndarray, c_w: np.ndarray, W_f16: np.ndarray,
+                      Wq_t: np.ndarray, c_w: np.ndarray, W_f16: Optional[np.ndarray],
                       col_chunk: int = 4096) -> np.ndarray:
-    """Steps 3-5 given the quantised operands: C fp16 [s, o]."""
+    """Steps 3-5 given the quantised operands: C fp16 [s, o]. With W_f16 None
+    the outlier rows come from dequantized_outlier_rows (no resident fp16 W)."""
     s = Xq.shape[0]
     o = Wq_t.shape[0]
     C = np.empty((s, o), dtype=np.float16)
     for j0 in range(0, o, col_chunk):
         j1 = min(o, j0 + col_chunk)
         Ci = int8_matmul_i32(Xq, Wq_t[j0:j1], col_chunk=col_chunk)
-        CO = outlier_matmul(X_O, W_f16[:, j0:j1], idx)
+        if W_f16 is None:
+            rows = dequantized_outlier_rows(Wq_t[j0:j1], c_w[j0:j1], idx).astype(F64)
+            CO = np.asarray(X_O, dtype=np.float16).astype(F64) @ rows
+        else:
+            CO = outlier_matmul(X_O, W_f16[:, j0:j1], idx)
         C[:, j0:j1] = dequantize_and_add(Ci, c_x, c_w[j0:j1], CO)
     return C
 
@@ -255,17 +273,20 @@ def fp16_matmul(X_f16: np.ndarray, W_f16: np.ndarray, col_chunk: int = 4096) -> 
 
 def forward(X_f16: np.ndarray, W_f16: np.ndarray, alpha: float = 6.0,
             Wq_t: Optional[np.ndarray] = None, c_w: Optional[np.ndarray] = None,
-            keep: bool = False) -> Dict[str, np.ndarray]:
+            keep: bool = False, fp16_weights: bool = True) -> Dict[str, np.ndarray]:
     """The whole procedure for one linear layer ([DIGEST] Steps 1-5 in order).
 
     If (Wq_t, c_w) are given they are the load-time conversion of W_f16;
-    otherwise it is done here. Returns a dict with C and the intermediates.
+    otherwise it is done here. With fp16_weights False the outlier product
+    uses dequantized_outlier_rows instead of the fp16 rows of W_f16 (the
+    storage variant without a resident fp16 W). Returns a dict with C and the
+    intermediates.
     """
     mask, idx, n_out = outlier_columns(X_f16, alpha)                 # Step 1
     Xq, c_x, X_O = quantize_rowwise(X_f16, idx)                       # Steps 2, 4
     if Wq_t is None or c_w is None:
         Wq_t, c_w = quantize_colwise_weights(W_f16)                   # Step 4 (load time)
-    C = int8_mixed_matmul(Xq, c_x, X_O, idx, Wq_t, c_w, W_f16)        # Steps 3, 4, 5
+    C = int8_mixed_matmul(Xq, c_x, X_O, idx, Wq_t, c_w, W_f16 if fp16_weights else None)   # Steps 3, 4, 5
     out = {"C": C, "mask": mask, "idx": idx, "n_out": np.int32(n_out),
            "Xq": Xq, "c_x": c_x, "X_O": X_O}
     if keep:

@@ -262,3 +262,44 @@ def test_fp16_gemm_full_size_sampled():
     X, W = H(Xd), H(Wd)
     ref = oracle.fp16_matmul(X[rows], W[:, cols])
     check_C(C.index_select(0, torch.from_numpy(rows).to(DEV)).index_select(1, torch.from_numpy(cols).to(DEV)), ref)
+
+
+# Without a resident fp16 W (W = None): outlier rows rebuilt from W_i8 / c_w.
+W8 = [(70, 768, 640, 6), (300, 1088, 448, 40), (600, 512, 768, 100), (8, 1024, 512, 3), (9, 12288, 128, 9)]
+
+
+@pytest.mark.parametrize("s,h,o,nout", W8, ids=[f"s{c[0]}h{c[1]}n{c[3]}" for c in W8])
+def test_forward_without_fp16_weights(s, h, o, nout):
+    inp = random_case(110 + s, s, h, o, nout, row_frac=0.5)
+    X, W = inp["X"], inp["W"]
+    Xd, Wd = T(X), T(W)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    ws = i8.forward_workspace(s, h, DEV)
+    say(f"  launch: forward without fp16 W s={s} h={h} o={o} |O|={nout}")
+    C = i8.forward(Xd, Wq, c_w, None, 6.0, workspace=ws)
+    torch.cuda.synchronize()
+    v = i8.forward_workspace_views(ws, s, h)
+    C2 = i8.int8_mixed_matmul(v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, None)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2)
+    assert not v["acc"].any()
+    check_C(C, oracle.forward(X, W, 6.0, fp16_weights=False)["C"])
+
+
+@pytest.mark.parametrize("s", [8, 300])
+def test_without_fp16_weights_is_exact_for_lossless_weights(s):
+    """When W_i8 / c_w reproduces W exactly, dropping the fp16 W changes nothing:
+    both storage variants give bit-identical C (decode and prefill kernels)."""
+    h, o = 512, 384
+    rng = np.random.default_rng(s)
+    q = rng.integers(-127, 128, size=(h, o))
+    q[rng.integers(0, h, size=o), np.arange(o)] = 127
+    W = (q * np.exp2(-rng.integers(5, 9, size=o))[None, :]).astype(np.float16)
+    X = random_case(120 + s, s, h, o, 5, row_frac=0.5)["X"]
+    Xd, Wd = T(X), T(W)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    say(f"  launch: lossless weights s={s}")
+    C1 = i8.forward(Xd, Wq, c_w, Wd, 6.0)
+    C2 = i8.forward(Xd, Wq, c_w, None, 6.0)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)

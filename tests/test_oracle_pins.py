@@ -395,3 +395,42 @@ def test_fp16_baseline_equals_full_decomposition():
     a = oracle.fp16_matmul(X, W, col_chunk=16)
     b = oracle.forward(X, W, alpha=0.0)["C"]
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def _lossless_weights(rng, h, o):
+    """W whose column-wise int8 quantisation is exact: per column an integer
+    code vector with max |q| = 127 times a power-of-two scale 2^-e, so
+    c_w = 2^e exactly and W_i8 / c_w == W."""
+    q = rng.integers(-127, 128, size=(h, o))
+    q[rng.integers(0, h, size=o), np.arange(o)] = 127
+    e = rng.integers(5, 9, size=o)
+    return (q * np.exp2(-e)[None, :]).astype(np.float16)
+
+
+def test_rebuilt_outlier_rows_equal_fp16_rows_when_lossless():
+    """Without a resident fp16 W the outlier rows are W_i8 / c_w; for weights
+    whose quantisation is lossless the two storage variants give the same
+    C bit for bit (a wrong row, column or scale in the rebuild would not)."""
+    rng = np.random.default_rng(21)
+    inp = random_case(21, 12, 256, 96, 4, row_frac=0.5)
+    W = _lossless_weights(rng, 256, 96)
+    Wq_t, c_w = oracle.quantize_colwise_weights(W)
+    assert np.array_equal((Wq_t.T.astype(np.float64) / c_w[None, :]).astype(np.float16), W)
+    a = oracle.forward(inp["X"], W, 6.0)
+    b = oracle.forward(inp["X"], W, 6.0, fp16_weights=False)
+    assert a["n_out"] == 4
+    assert np.array_equal(a["C"].view(np.uint16), b["C"].view(np.uint16))
+
+
+def test_rebuilt_outlier_rows_are_rounded_quotients():
+    """Each rebuilt weight is the exact quotient code / c_w rounded once to
+    fp16 (checked with rational arithmetic), for ordinary weights."""
+    rng = np.random.default_rng(22)
+    W = (rng.standard_normal((64, 24)) * 0.02).astype(np.float16)
+    Wq_t, c_w = oracle.quantize_colwise_weights(W)
+    idx = np.array([3, 17, 40, 63])
+    rows = oracle.dequantized_outlier_rows(Wq_t, c_w, idx)
+    for a, k in enumerate(idx):
+        for j in range(24):
+            exact = Fraction(int(Wq_t[j, k])) / Fraction(float(c_w[j]))
+            assert Fraction(float(rows[a, j])) == rational.fl16(exact)
