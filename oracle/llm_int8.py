@@ -207,18 +207,25 @@ def outlier_matmul(X_O: np.ndarray, W_f16: np.ndarray, idx: np.ndarray) -> np.nd
 
 
 def dequantize_and_add(C_i32: np.ndarray, c_x: np.ndarray, c_w: np.ndarray,
-                       C_O: Optional[np.ndarray]) -> np.ndarray:
+                       C_O: Optional[np.ndarray], bias: Optional[np.ndarray] = None) -> np.ndarray:
     """Step 4 last bullet and Step 5: C = S ⊙ C_i32 + C^O, S_ij = 1/(c_x_i c_w_j).
 
     [DIGEST] "The Full LLM.int8() Algorithm", Step 4 (dequantise with the
     outer product of the scales) and Step 5 (sum the two partial results);
     [PY] "第一件武器：向量级量化" (divide by c_x ⊗ c_w). Evaluated in float64
     and rounded once to fp16.
+
+    bias (fp16 [o], optional) is the linear layer's bias, which stays in
+    16 bit ([DIGEST] "Mixed-Precision Decomposition", memory accounting):
+    b_j is added to every row of column j in the same float64 sum, before
+    the single rounding.
     """
     denom = c_x.astype(F64)[:, None] * c_w.astype(F64)[None, :]   # exact
     C = C_i32.astype(F64) / denom
     if C_O is not None:
         C = C + C_O
+    if bias is not None:
+        C = C + np.asarray(bias, dtype=np.float16).astype(F64)[None, :]
     return C.astype(np.float16)
 
 
@@ -236,9 +243,10 @@ def dequantized_outlier_rows(Wq_t: np.ndarray, c_w: np.ndarray, idx: np.ndarray)
 
 def int8_mixed_matmul(Xq: np.ndarray, c_x: np.ndarray, X_O: np.ndarray, idx: np.ndarray,
                       Wq_t: np.ndarray, c_w: np.ndarray, W_f16: Optional[np.ndarray],
-                      col_chunk: int = 4096) -> np.ndarray:
+                      col_chunk: int = 4096, bias: Optional[np.ndarray] = None) -> np.ndarray:
     """Steps 3-5 given the quantised operands: C fp16 [s, o]. With W_f16 None
-    the outlier rows come from dequantized_outlier_rows (no resident fp16 W)."""
+    the outlier rows come from dequantized_outlier_rows (no resident fp16 W);
+    bias (fp16 [o]) is added as in dequantize_and_add."""
     s = Xq.shape[0]
     o = Wq_t.shape[0]
     C = np.empty((s, o), dtype=np.float16)
@@ -250,7 +258,7 @@ def int8_mixed_matmul(Xq: np.ndarray, c_x: np.ndarray, X_O: np.ndarray, idx: np.
             CO = np.asarray(X_O, dtype=np.float16).astype(F64) @ rows
         else:
             CO = outlier_matmul(X_O, W_f16[:, j0:j1], idx)
-        C[:, j0:j1] = dequantize_and_add(Ci, c_x, c_w[j0:j1], CO)
+        C[:, j0:j1] = dequantize_and_add(Ci, c_x, c_w[j0:j1], CO, None if bias is None else bias[j0:j1])
     return C
 
 
@@ -273,20 +281,23 @@ def fp16_matmul(X_f16: np.ndarray, W_f16: np.ndarray, col_chunk: int = 4096) -> 
 
 def forward(X_f16: np.ndarray, W_f16: np.ndarray, alpha: float = 6.0,
             Wq_t: Optional[np.ndarray] = None, c_w: Optional[np.ndarray] = None,
-            keep: bool = False, fp16_weights: bool = True) -> Dict[str, np.ndarray]:
+            keep: bool = False, fp16_weights: bool = True,
+            bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """The whole procedure for one linear layer ([DIGEST] Steps 1-5 in order).
 
     If (Wq_t, c_w) are given they are the load-time conversion of W_f16;
     otherwise it is done here. With fp16_weights False the outlier product
     uses dequantized_outlier_rows instead of the fp16 rows of W_f16 (the
-    storage variant without a resident fp16 W). Returns a dict with C and the
-    intermediates.
+    storage variant without a resident fp16 W). bias (fp16 [o], optional) is
+    the layer's bias, added before the single rounding of C. Returns a dict
+    with C and the intermediates.
     """
     mask, idx, n_out = outlier_columns(X_f16, alpha)                 # Step 1
     Xq, c_x, X_O = quantize_rowwise(X_f16, idx)                       # Steps 2, 4
     if Wq_t is None or c_w is None:
         Wq_t, c_w = quantize_colwise_weights(W_f16)                   # Step 4 (load time)
-    C = int8_mixed_matmul(Xq, c_x, X_O, idx, Wq_t, c_w, W_f16 if fp16_weights else None)   # Steps 3, 4, 5
+    C = int8_mixed_matmul(Xq, c_x, X_O, idx, Wq_t, c_w, W_f16 if fp16_weights else None,
+                          bias=bias)                                   # Steps 3, 4, 5
     out = {"C": C, "mask": mask, "idx": idx, "n_out": np.int32(n_out),
            "Xq": Xq, "c_x": c_x, "X_O": X_O}
     if keep:

@@ -66,10 +66,11 @@ def to_fractions(A) -> Matrix:
     return [[Fraction(float(v)) for v in row] for row in A]
 
 
-def brute_force(X, W, alpha: float) -> Tuple[List[int], List[Fraction], List[List[int]],
-                                              List[Fraction], List[List[int]], List[List[int]],
-                                              List[List[Fraction]]]:
-    """Return (O, c_x, Xq, c_w, Wq [h][o], C_i32, C) for fp16-valued X [s][h], W [h][o]."""
+def brute_force(X, W, alpha: float, bias=None) -> Tuple[List[int], List[Fraction], List[List[int]],
+                                                         List[Fraction], List[List[int]], List[List[int]],
+                                                         List[List[Fraction]]]:
+    """Return (O, c_x, Xq, c_w, Wq [h][o], C_i32, C) for fp16-valued X [s][h], W [h][o]
+    (and an optional fp16-valued bias [o], added to each row before rounding)."""
     Xf = to_fractions(X)
     Wf = to_fractions(W)
     s, h = len(Xf), len(Xf[0])
@@ -110,6 +111,8 @@ def brute_force(X, W, alpha: float) -> Tuple[List[int], List[Fraction], List[Lis
         for j in range(o):
             v = Fraction(C_i32[i][j]) / (c_x[i] * c_w[j])
             v += sum((Xf[i][k] * Wf[k][j] for k in O), Fraction(0))
+            if bias is not None:
+                v += Fraction(float(bias[j]))
             row.append(fl16(v))
         C.append(row)
     return O, c_x, Xq, c_w, Wq, C_i32, C

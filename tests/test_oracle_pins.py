@@ -434,3 +434,48 @@ def test_rebuilt_outlier_rows_are_rounded_quotients():
         for j in range(24):
             exact = Fraction(int(Wq_t[j, k])) / Fraction(float(c_w[j]))
             assert Fraction(float(rows[a, j])) == rational.fl16(exact)
+
+
+# ---------------------------------------------------------------- layer bias
+
+def test_bias_alone_with_zero_weights():
+    """W = 0 (every code 0, c_w = 1 by the zero-column convention): C is the
+    bias broadcast over the rows, bit for bit, whatever X holds (outlier
+    columns included). A bias dropped, doubled or indexed by row fails."""
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((6, 128)).astype(np.float16)
+    X[:, 5] = 9.0
+    W = np.zeros((128, 64), np.float16)
+    b = (rng.standard_normal(64) * 3).astype(np.float16)
+    out = oracle.forward(X, W, 6.0, bias=b)
+    assert out["n_out"] == 1
+    assert np.array_equal(out["C"].view(np.uint16), np.broadcast_to(b, (6, 64)).view(np.uint16))
+
+
+def test_bias_alpha_zero_is_textbook_linear_layer():
+    """alpha = 0 (no int8 part): C is the fp16-rounded float64 X W + b, the
+    textbook linear layer."""
+    rng = np.random.default_rng(32)
+    X = rng.standard_normal((20, 128)).astype(np.float16)
+    W = (rng.standard_normal((128, 80)) * 0.02).astype(np.float16)
+    b = rng.standard_normal(80).astype(np.float16)
+    out = oracle.forward(X, W, alpha=0.0, bias=b)
+    ref = (X.astype(np.float64) @ W.astype(np.float64) + b.astype(np.float64)[None, :]).astype(np.float16)
+    assert np.array_equal(out["C"].view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("seed,s,h,o,nout", [(40, 4, 64, 12, 2), (41, 6, 128, 8, 0)])
+def test_bias_exact_rational_bruteforce(seed, s, h, o, nout):
+    """With a bias, C agrees with the exact rational evaluation of every step
+    plus b_j, rounded once (within one fp16 ulp, almost always bit-equal)."""
+    inp = random_case(seed, s, h, o, nout, row_frac=0.5)
+    b = (np.random.default_rng(seed).standard_normal(o) * 0.5).astype(np.float16)
+    *_, C = rational.brute_force(inp["X"], inp["W"], 6.0, bias=b)
+    out = oracle.forward(inp["X"], inp["W"], 6.0, bias=b)
+    equal = 0
+    for i in range(s):
+        for j in range(o):
+            g = Fraction(float(out["C"][i, j]))
+            assert abs(g - C[i][j]) <= rational.ulp16(C[i][j])
+            equal += g == C[i][j]
+    assert equal >= s * o - 1
