@@ -7,8 +7,9 @@
  *   1. the outlier feature columns O = { j : max_i |X_ij| >= alpha };
  *   2. row-wise absmax int8 quantisation of X over the columns not in O;
  *   3. (once, at load time) column-wise absmax int8 quantisation of W;
- *   4. C = fp16( C_i32 / (c_x (x) c_w) + X[:, O] W[O, :] ), where C_i32 is the
- *      exact int8 x int8 -> int32 product over the columns not in O.
+ *   4. C = fp16( C_i32 / (c_x (x) c_w) + X[:, O] W[O, :] [+ bias] ), where
+ *      C_i32 is the exact int8 x int8 -> int32 product over the columns not
+ *      in O.
  *
  * Page tags used in the citations below:
  *   [DIGEST] "LLM.int8(): 8-bit Matrix Multiplication for Transformers at
@@ -145,6 +146,10 @@ i8mm_status i8mm_quantize_rowwise(const uint16_t* X, int64_t s, int64_t h,
  * in fp32 and rounded once to fp16 (round to nearest even). S is never
  * materialised. n_out is read on the device; only rows idx[0 .. n_out) of W
  * are read.
+ * With a layer bias b the result is C = fp16( C_i32 / (c_x (x) c_w) +
+ * X_O W[idx, :] + b ), b added in the same fp32 sum before the one rounding
+ * (biases stay in 16 bit: [DIGEST] "Mixed-Precision Decomposition", memory
+ * accounting).
  *
  * Xq: [s, h] int8; c_x: [s] fp32; X_O: [s, ldo] fp16 (ldo as above);
  * idx, n_out: as from i8mm_detect_outlier_cols; Wq: panel layout (above);
@@ -155,11 +160,13 @@ i8mm_status i8mm_quantize_rowwise(const uint16_t* X, int64_t s, int64_t h,
  * only Wq and c_w stay resident: about half the weight memory, the saving
  * the pages measure on BLOOM-176B ([DIGEST] "Executive Summary"; [PY]
  * "第二件武器：混合精度分解"); the outlier product then sees the 8-bit weights.
+ * bias: [o] fp16 (read), or NULL for none.
  */
 i8mm_status i8mm_int8_mixed_matmul(const int8_t* Xq, const float* c_x,
                                    const uint16_t* X_O, int64_t ldo,
                                    const int32_t* idx, const int32_t* n_out,
                                    const int8_t* Wq, const float* c_w, const uint16_t* W,
+                                   const uint16_t* bias,
                                    int64_t s, int64_t h, int64_t o, uint16_t* C,
                                    hipStream_t stream);
 
@@ -236,10 +243,11 @@ size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h);
  * workspace must not overlap. After completion the workspace holds the
  * intermediates at the offsets given by i8mm_forward_workspace_layout.
  * X: [s, h] fp16; Wq: panel layout (above); c_w: [o] fp32; W: [h, o] fp16
- * or NULL (as for i8mm_int8_mixed_matmul); C: [s, o] fp16 (written).
+ * or NULL, and bias: [o] fp16 or NULL (both as for i8mm_int8_mixed_matmul);
+ * C: [s, o] fp16 (written).
  */
 i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
-                         const int8_t* Wq, const float* c_w, const uint16_t* W,
+                         const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
                          void* workspace, uint16_t* C, hipStream_t stream);
 
 /*

@@ -178,11 +178,17 @@ def _weights_ptr(W: Optional[torch.Tensor], h: int, o: int) -> Optional[int]:
     return None if W is None else _dev(W, "W", torch.float16, (h, o))
 
 
+def _bias_ptr(bias: Optional[torch.Tensor], o: int) -> Optional[int]:
+    """Pointer of the fp16 layer bias [o], or None (no bias)."""
+    return None if bias is None else _dev(bias, "bias", torch.float16, (o,))
+
+
 def int8_mixed_matmul(Xq: torch.Tensor, c_x: torch.Tensor, X_O: torch.Tensor, idx: torch.Tensor,
                       n_out: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Optional[torch.Tensor],
-                      C: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """C fp16 [s, o] = fp16(C_i32 / (c_x ⊗ c_w) + X_O W[idx, :]). With W None no
-    fp16 copy of the weights is needed: W[idx, :] is rebuilt as fp16(W_i8 / c_w)."""
+                      C: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C fp16 [s, o] = fp16(C_i32 / (c_x ⊗ c_w) + X_O W[idx, :] [+ bias]). With W
+    None no fp16 copy of the weights is needed: W[idx, :] is rebuilt as
+    fp16(W_i8 / c_w). bias: fp16 [o] or None."""
     s, h = Xq.shape
     o = Wq.shape[1]
     if C is None:
@@ -191,7 +197,7 @@ def int8_mixed_matmul(Xq: torch.Tensor, c_x: torch.Tensor, X_O: torch.Tensor, id
         _dev(Xq, "Xq", torch.int8), _dev(c_x, "c_x", torch.float32, (s,)),
         _dev(X_O, "X_O", torch.float16), X_O.shape[1], _dev(idx, "idx", torch.int32),
         _dev(n_out, "n_out", torch.int32, (1,)), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)),
-        _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o),
+        _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o), _bias_ptr(bias, o),
         s, h, o, _dev(C, "C", torch.float16, (s, o)), _stream(Xq))
     _check(st, "int8_mixed_matmul")
     return C
@@ -286,9 +292,10 @@ def forward_workspace_views(workspace: torch.Tensor, s: int, h: int) -> Dict[str
 
 def forward(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Optional[torch.Tensor],
             alpha: float = 6.0, workspace: Optional[torch.Tensor] = None,
-            C: Optional[torch.Tensor] = None) -> torch.Tensor:
+            C: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole per-forward path: detect -> quantise rows -> decomposed product.
-    W is the resident fp16 weight matrix, or None (outlier rows rebuilt from Wq / c_w)."""
+    W is the resident fp16 weight matrix, or None (outlier rows rebuilt from
+    Wq / c_w); bias is the fp16 layer bias [o], or None."""
     s, h = X.shape
     o = Wq.shape[1]
     if workspace is None:
@@ -300,7 +307,7 @@ def forward(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Optional[to
         raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
     st = _lib.i8mm_forward(
         _dev(X, "X", torch.float16), s, h, o, float(alpha), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)),
-        _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o),
+        _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o), _bias_ptr(bias, o),
         _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
     _check(st, "forward")
     return C

@@ -137,16 +137,18 @@ i8mm_status i8mm_quantize_rowwise(const uint16_t* X, int64_t s, int64_t h,
 i8mm_status i8mm_int8_mixed_matmul(const int8_t* Xq, const float* c_x, const uint16_t* X_O, int64_t ldo,
                                    const int32_t* idx, const int32_t* n_out,
                                    const int8_t* Wq, const float* c_w, const uint16_t* W,
+                                   const uint16_t* bias,
                                    int64_t s, int64_t h, int64_t o, uint16_t* C, hipStream_t stream) {
-    if (!Xq || !c_x || !X_O || !idx || !n_out || !Wq || !c_w || !C) return I8MM_EINVAL;   // W may be null
+    // W and bias may be null
+    if (!Xq || !c_x || !X_O || !idx || !n_out || !Wq || !c_w || !C) return I8MM_EINVAL;
     if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
     if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
     if (!aligned16(Xq) || !aligned16(c_x) || !aligned16(X_O) || !aligned16(idx) || !aligned16(n_out) ||
-        !aligned16(Wq) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
+        !aligned16(Wq) || !aligned16(c_w) || !aligned16(W) || !aligned16(bias) || !aligned16(C))
         return I8MM_EINVAL;
     if (i8mm_status d = check_device()) return d;
     return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W,
-                                           s, h, o, C, stream));
+                                           bias, s, h, o, C, stream));
 }
 
 i8mm_status i8mm_outlier_matmul(const uint16_t* X_O, int64_t ldo, const int32_t* idx, const int32_t* n_out,
@@ -168,7 +170,7 @@ i8mm_status i8mm_int8_gemm_i32(const int8_t* Xq, const int8_t* Wq, int64_t s, in
     if (!aligned16(Xq) || !aligned16(Wq) || !aligned16(C_i32)) return I8MM_EINVAL;
     if (i8mm_status d = check_device()) return d;
     return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::Int32, Xq, nullptr, nullptr, 0, nullptr, nullptr, Wq,
-                                           nullptr, nullptr, s, h, o, C_i32, stream));
+                                           nullptr, nullptr, nullptr, s, h, o, C_i32, stream));
 }
 
 i8mm_status i8mm_pack_fp16_weights(const uint16_t* W, int64_t h, int64_t o, uint16_t* Wp, hipStream_t stream) {
@@ -204,13 +206,14 @@ i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[7
 }
 
 i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
-                         const int8_t* Wq, const float* c_w, const uint16_t* W,
+                         const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
                          void* workspace, uint16_t* C, hipStream_t stream) {
-    if (!X || !Wq || !c_w || !workspace || !C) return I8MM_EINVAL;   // W may be null
+    if (!X || !Wq || !c_w || !workspace || !C) return I8MM_EINVAL;   // W and bias may be null
     if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
     if (std::isnan(alpha) || alpha < 0.0f) return I8MM_EINVAL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
-    if (!aligned16(X) || !aligned16(Wq) || !aligned16(c_w) || !aligned16(W) || !aligned16(C))
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(c_w) || !aligned16(W) || !aligned16(bias) ||
+        !aligned16(C))
         return I8MM_EINVAL;
     if (i8mm_status d = check_device()) return d;
     size_t off[7], total;
@@ -228,8 +231,8 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
     hipError_t e = i8mm::launch_forward_prologue(X, s, h, alpha, acc, mask, idx, n_out, Xq, c_x, X_O, ldo, stream,
                                                  &clear_words);
     if (e != hipSuccess) return I8MM_ELAUNCH;
-    e = i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, s, h, o, C,
-                               stream, clear_words > 0 ? acc : nullptr, clear_words);
+    e = i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s, h, o,
+                               C, stream, clear_words > 0 ? acc : nullptr, clear_words);
     return launched(e);
 }
 

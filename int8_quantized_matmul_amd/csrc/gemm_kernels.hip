@@ -18,8 +18,9 @@
 //
 // Two main loops share the epilogue structure:
 //  * k_gemm_prefill: 256x256 output tile per 256-thread block, K step 128
-//    (two panels), LDS double buffering with a register-staged global
-//    prefetch, v_mfma_i32_32x32x32_i8, 2x2 waves of 128x128.
+//    (two panels), both operands double buffered in LDS through
+//    direct-to-LDS buffer loads, v_mfma_i32_32x32x32_i8, 2x2 waves of
+//    128x128.
 //  * k_gemm_decode (s <= 16): weight streaming. Four wavefronts per 16*NT
 //    output columns split K and read their panels of Wq straight from HBM
 //    into the MFMA operand registers with non-temporal loads
@@ -27,8 +28,8 @@
 //    register batches in flight.
 // The fused epilogue converts the int32 accumulator to fp32, multiplies by
 // 1/c_x_i * 1/c_w_j (S is never materialised), then accumulates the fp16
-// outlier product on top with fp16 MFMA (fp32 accumulate) and rounds once
-// to fp16.
+// outlier product on top with fp16 MFMA (fp32 accumulate), adds the
+// optional layer bias and rounds once to fp16.
 
 #include <type_traits>
 
@@ -215,7 +216,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     const float* __restrict__ c_x, const float* __restrict__ c_w,
                     const uint16_t* __restrict__ X_O, int64_t ldo,
                     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out,
-                    const uint16_t* __restrict__ W, void* __restrict__ Cout,
+                    const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ Cout,
                     uint32_t* __restrict__ clear, int clear_words) {
     __shared__ v4i A0[kBuf], A1[kBuf], B0[kBuf], B1[kBuf];
     __shared__ __attribute__((aligned(16))) uint16_t olds[2 * kSlice];
@@ -452,8 +453,8 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         uint16_t* C = static_cast<uint16_t*>(Cout);
         __syncthreads();   // every wavefront is done with the stage buffers
         // Epilogue LDS: extra outlier slices q = 1, 2 in A0, 3, 4 in B0 and
-        // 5 in B1; output staging of waves 0-2 in A1 and of wave 3 in B1,
-        // followed there by 1 / c_w.
+        // 5 in B1; output staging of waves 0-2 in A1, followed there by the
+        // bias, and of wave 3 in B1, followed there by 1 / c_w.
         auto slice_at = [&](int q) -> uint16_t* {   // q = 1 .. kMaxOnceSlices
             uint16_t* base = q <= 2 ? reinterpret_cast<uint16_t*>(A0)
                            : q <= 4 ? reinterpret_cast<uint16_t*>(B0)
@@ -462,6 +463,19 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         };
         uint16_t* out_st = wid < 3 ? reinterpret_cast<uint16_t*>(A1) + wid * kOutWave : reinterpret_cast<uint16_t*>(B1);
         float* invw = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(B1) + kOutWave) + wid * 128;
+        float* bsl = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(A1) + 3 * kOutWave) + wid * 128;
+        // The layer bias of the wave's 128 columns (fp16 -> fp32, exact),
+        // fetched under the outlier staging below.
+        // Range-checked loads with no branch around them (columns past o, or
+        // no bias at all, read zero), so the wait for them falls at their use.
+        const bool has_bias = bias != nullptr;
+        const __amdgpu_buffer_rsrc_t rBias = make_rsrc(bias, has_bias ? static_cast<uint32_t>(2 * o) : 0u);
+        uint16_t bias_bits[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t col = static_cast<uint32_t>(o0 + wo * 128 + lane + 64 * i);
+            bias_bits[i] = __builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(rBias, 2 * col, 0, 0));
+        }
         const int nsl = (n_o + 15) / 16;
         const bool once = nsl <= 1 + kMaxOnceSlices;
         if (once) {
@@ -473,6 +487,10 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         // 1 / c_w of the wave's 128 columns (reciprocals to 1 ulp)
 #pragma unroll
         for (int i = 0; i < 2; ++i) invw[lane + 64 * i] = __builtin_amdgcn_rcpf(cw_pf[i]);
+        if (has_bias) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) bsl[lane + 64 * i] = half_bits_to_float(bias_bits[i]);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (once && !w8) {
@@ -519,6 +537,15 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                         for (int q = rb; q < re; ++q)
                             f = w8 ? apply_outlier_slice_t(slice_at(q - rb + 1), wo, ws, sb, ob, r32, khalf, f)
                                    : apply_outlier_slice(slice_at(q - rb + 1), wo, ws, sb, ob, r32, khalf, f);
+                    }
+                }
+                // The layer bias, in the same fp32 sum before the rounding.
+                if (has_bias) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const v4f bv = *reinterpret_cast<const v4f*>(bsl + ob * 32 + 8 * g + 4 * khalf);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) f[4 * g + e] += bv[e];
                     }
                 }
                 // Round once to fp16 and stage in this wavefront's LDS area
@@ -620,7 +647,8 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
                                                      const uint16_t* __restrict__ X_O, int64_t ldo,
                                                      const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ n_out,
-                                                     const uint16_t* __restrict__ W, void* __restrict__ Cout,
+                                                     const uint16_t* __restrict__ W,
+                                                     const uint16_t* __restrict__ bias, void* __restrict__ Cout,
                                                      uint32_t* __restrict__ clear, int clear_words) {
     __shared__ v4i red[kDecodeSplit][NT][64];
     if (blockIdx.x == 0)
@@ -644,10 +672,13 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     // outlier operands now, so the loads complete under the K loop.
     int n_o = 0;
     v8h pre[2];
+    uint2 bias4 = make_uint2(0u, 0u);   // the layer bias of this lane's 4 output columns
     if constexpr (MODE == GemmOut::Mixed) {
         n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
         if (wid < NT && n_o > 0)
             outlier_operands_16(0, n_o, lane, obase + wid * 16, 0, s, o, X_O, ldo, idx, W, Wq, c_w, pre[0], pre[1]);
+        if (wid < NT && bias != nullptr)
+            bias4 = *reinterpret_cast<const uint2*>(bias + obase + wid * 16 + 4 * g);
     }
 
     const int64_t nsteps = h / 64;
@@ -711,6 +742,12 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
         f = outlier_tile_16x16(f, lane, obase + nt * 16, 0, s, o, X_O, ldo, idx, n_o, W, Wq, c_w, pre);
+        if (bias != nullptr) {
+            f[0] += half_bits_to_float(bias4.x & 0xffffu);
+            f[1] += half_bits_to_float(bias4.x >> 16);
+            f[2] += half_bits_to_float(bias4.y & 0xffffu);
+            f[3] += half_bits_to_float(bias4.y >> 16);
+        }
         if (srow < s) {
             const uint32_t lo = float_to_half_bits(f[0]) | (static_cast<uint32_t>(float_to_half_bits(f[1])) << 16);
             const uint32_t hi = float_to_half_bits(f[2]) | (static_cast<uint32_t>(float_to_half_bits(f[3])) << 16);
@@ -743,16 +780,17 @@ __global__ __launch_bounds__(256) void k_outlier_only(const uint16_t* __restrict
 template <GemmOut MODE>
 hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, int64_t ldo,
                        const int32_t* idx, const int32_t* n_out, const int8_t* Wq, const float* c_w,
-                       const uint16_t* W, int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
-                       uint32_t* clear, int clear_words) {
+                       const uint16_t* W, const uint16_t* bias, int64_t s, int64_t h, int64_t o, void* C,
+                       hipStream_t stream, uint32_t* clear, int clear_words) {
     if (s <= 16) {
         constexpr int NT = 2;
         hipLaunchKernelGGL((k_gemm_decode<MODE, NT>), dim3(static_cast<unsigned>(o / (16 * NT))), dim3(256), 0,
-                           stream, Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C, clear, clear_words);
+                           stream, Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear,
+                           clear_words);
     } else {
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
         hipLaunchKernelGGL((k_gemm_prefill<MODE>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
-                           Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, C, clear, clear_words);
+                           Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words);
     }
     return hipGetLastError();
 }
@@ -762,13 +800,13 @@ hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, 
 hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                             const uint16_t* X_O, int64_t ldo,
                             const int32_t* idx, const int32_t* n_out,
-                            const int8_t* Wq, const float* c_w, const uint16_t* W,
+                            const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
                             int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
                             uint32_t* clear, int clear_words) {
     if (mode == GemmOut::Int32)
-        return launch_mode<GemmOut::Int32>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, s, h, o, C, stream,
+        return launch_mode<GemmOut::Int32>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, nullptr, s, h, o, C, stream,
                                            clear, clear_words);
-    return launch_mode<GemmOut::Mixed>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, s, h, o, C, stream,
+    return launch_mode<GemmOut::Mixed>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s, h, o, C, stream,
                                        clear, clear_words);
 }
 
@@ -778,7 +816,7 @@ hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, in
     const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
     hipLaunchKernelGGL((k_gemm_prefill<GemmOut::Fp16Dense>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
                        reinterpret_cast<const int8_t*>(X), reinterpret_cast<const int8_t*>(Wp), s, 2 * h, o,
-                       nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, C, nullptr, 0);
+                       nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, C, nullptr, 0);
     return hipGetLastError();
 }
 

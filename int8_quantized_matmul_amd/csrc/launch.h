@@ -28,15 +28,17 @@ hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, floa
 hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
                                 int8_t* Wq, float* c_w, hipStream_t stream);
 
-// mode: product variant of the shared int8 main loop. `clear` (optional):
-// clear_words uint32 words that the first block zeroes (the forward path's
+// mode: product variant of the shared int8 main loop. W (Mixed only) may be
+// null: outlier rows rebuilt from Wq / c_w. bias (Mixed only, optional):
+// fp16 [o] added before the rounding. `clear` (optional): clear_words
+// uint32 words that the first block zeroes (the forward path's
 // accumulator, whose readers have finished by then).
 enum class GemmOut { Mixed = 0, Int32 = 1, Fp16Dense = 2 };
 
 hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                             const uint16_t* X_O, int64_t ldo,
                             const int32_t* idx, const int32_t* n_out,
-                            const int8_t* Wq, const float* c_w, const uint16_t* W,
+                            const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
                             int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
                             uint32_t* clear = nullptr, int clear_words = 0);
 

@@ -63,11 +63,13 @@ def test_quantize_rowwise_rejects_small_ldo():
 
 def test_mixed_matmul_and_gemm_reject():
     lib = _lib()
-    assert lib.i8mm_int8_mixed_matmul(P, P, P, 64, P, P, P, P, P, 4, 64, 64, None, None) == -1
-    assert lib.i8mm_int8_mixed_matmul(P, P, P, 32, P, P, P, P, P, 4, 64, 64, P, None) == -1
+    assert lib.i8mm_int8_mixed_matmul(P, P, P, 64, P, P, P, P, P, None, 4, 64, 64, None, None) == -1
+    assert lib.i8mm_int8_mixed_matmul(P, P, P, 32, P, P, P, P, P, None, 4, 64, 64, P, None) == -1
+    # a misaligned bias
+    assert lib.i8mm_int8_mixed_matmul(P, P, P, 64, P, P, P, P, P, MIS, 4, 64, 64, P, None) == -1
     assert lib.i8mm_int8_gemm_i32(P, P, 4, 64, 65, P, None) == -1
     # W larger than 32-bit byte offsets can address (h * o >= 2^31)
-    assert lib.i8mm_int8_mixed_matmul(P, P, P, 65536, P, P, P, P, P, 4, 65536, 32768, P, None) == -1
+    assert lib.i8mm_int8_mixed_matmul(P, P, P, 65536, P, P, P, P, P, None, 4, 65536, 32768, P, None) == -1
     assert lib.i8mm_int8_gemm_i32(P, P, 4, 65536, 32768, P, None) == -1
     assert lib.i8mm_outlier_matmul(P, 64, P, P, P, 4, 64, 64, MIS, None) == -1
 
@@ -75,7 +77,9 @@ def test_mixed_matmul_and_gemm_reject():
 def test_forward_rejects_unaligned_workspace():
     lib = _lib()
     ws = ctypes.c_void_p((1 << 20) + 16)
-    assert lib.i8mm_forward(P, 4, 64, 64, 6.0, P, P, P, ws, P, None) == -1
+    assert lib.i8mm_forward(P, 4, 64, 64, 6.0, P, P, P, None, ws, P, None) == -1
+    # a misaligned bias
+    assert lib.i8mm_forward(P, 4, 64, 64, 6.0, P, P, P, MIS, ctypes.c_void_p(1 << 20), P, None) == -1
 
 
 def test_forward_workspace_layout():

@@ -168,7 +168,9 @@ FWD = [(70, 768, 640, 6, 6.0), (16, 8192, 256, 7, 6.0), (17, 8192, 256, 7, 6.0),
        (64, 2048, 256, 7, 6.0), (65, 2048, 256, 7, 6.0), (300, 640, 576, 5, 6.0),
        (8, 16384, 128, 9, 6.0), (9, 12288, 128, 9, 6.0), (66, 16384, 128, 9, 6.0), (70, 20480, 128, 9, 6.0),
        (3, 133120, 64, 9, 6.0),
-       (40, 128, 192, 0, 0.0), (1100, 128, 192, 0, 0.0), (513, 384, 768, 40, 6.0), (2, 64, 64, 0, 6.0)]
+       (40, 128, 192, 0, 0.0), (1100, 128, 192, 0, 0.0), (513, 384, 768, 40, 6.0), (2, 64, 64, 0, 6.0),
+       (1, 16384, 128, 5, 6.0), (5, 8256, 192, 3, 6.0), (12, 8192, 256, 0, 6.0), (10, 4096, 128, 0, 0.0),
+       (16, 64, 64, 2, 6.0), (8, 12288, 256, 7, float("inf")), (7, 1024, 128, 64, 6.0)]
 
 
 @pytest.mark.parametrize("s,h,o,nout,alpha", FWD, ids=[f"s{c[0]}h{c[1]}n{c[3]}a{c[4]}" for c in FWD])
@@ -303,3 +305,44 @@ def test_without_fp16_weights_is_exact_for_lossless_weights(s):
     C2 = i8.forward(Xd, Wq, c_w, None, 6.0)
     torch.cuda.synchronize()
     assert torch.equal(C1, C2)
+
+
+# The layer bias (fp16 [o]) added in the epilogue before the one rounding:
+# decode and prefill kernels, fp16 W resident or rebuilt, the prefill
+# epilogue's single-pass (|O| <= 96) and multi-round outlier paths.
+BIAS = [(8, 1024, 512, 3, True), (8, 1024, 512, 3, False), (70, 768, 640, 6, True),
+        (300, 1088, 448, 100, True), (300, 1088, 448, 100, False), (17, 192, 320, 0, True)]
+
+
+@pytest.mark.parametrize("s,h,o,nout,fp16_w", BIAS, ids=[f"s{c[0]}h{c[1]}n{c[3]}{'w' if c[4] else 'q'}" for c in BIAS])
+def test_forward_with_bias(s, h, o, nout, fp16_w):
+    inp = random_case(130 + s + nout, s, h, o, nout, row_frac=0.5)
+    X, W = inp["X"], inp["W"]
+    b = (np.random.default_rng(s + o).standard_normal(o) * 0.5).astype(np.float16)
+    Xd, Wd, bd = T(X), T(W), T(b)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    ws = i8.forward_workspace(s, h, DEV)
+    say(f"  launch: forward with bias s={s} h={h} o={o} |O|={nout} fp16 W={fp16_w}")
+    C = i8.forward(Xd, Wq, c_w, Wd if fp16_w else None, 6.0, workspace=ws, bias=bd)
+    torch.cuda.synchronize()
+    v = i8.forward_workspace_views(ws, s, h)
+    C2 = i8.int8_mixed_matmul(v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w,
+                              Wd if fp16_w else None, bias=bd)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2)
+    check_C(C, oracle.forward(X, W, 6.0, fp16_weights=fp16_w, bias=b)["C"])
+
+
+@pytest.mark.parametrize("s", [5, 260])
+def test_bias_alone_with_zero_weights(s):
+    """W = 0: every row of C is the bias, bit for bit (a bias read at the wrong
+    column, or from the row index, cannot pass)."""
+    h, o = 256, 576
+    X = random_case(140 + s, s, h, o, 2, row_frac=0.5)["X"]
+    b = (np.random.default_rng(s).standard_normal(o) * 3).astype(np.float16)
+    Wd = torch.zeros((h, o), dtype=torch.float16, device=DEV)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    say(f"  launch: zero weights with bias s={s}")
+    C = i8.forward(T(X), Wq, c_w, Wd, 6.0, bias=T(b))
+    torch.cuda.synchronize()
+    assert np.array_equal(H(C).view(np.uint16), np.broadcast_to(b, (s, o)).view(np.uint16))
