@@ -5,4 +5,8 @@ import this package; the product path never does.
 """
 
 from .llm_int8 import *  # noqa: F401,F403
-from .llm_int8 import __all__  # noqa: F401
+from .llm_int8 import __all__ as _main_all
+from .variants import *  # noqa: F401,F403
+from .variants import __all__ as _variant_all
+
+__all__ = list(_main_all) + list(_variant_all)

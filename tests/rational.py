@@ -133,3 +133,48 @@ def ulp16(v: Fraction) -> Fraction:
 
 def as_fractions_1d(v: Sequence[float]) -> List[Fraction]:
     return [Fraction(float(x)) for x in v]
+
+
+def zeropoint_brute_force(X, W, alpha: float):
+    """Zeropoint vector-wise with the decomposition, every step in exact
+    rationals with IEEE rounding emulated (fl32 / fl16 above): returns
+    (O, nd_x, zp_x, Xq, nd_w, zp_w, Wq [h][o], C' [s][o], C [s][o]).
+    nd = fl32(254 / fl32(max - min)) (1 if max == min); zp = round(fl32(nd
+    min)) + 127; q = clamp(round(fl32(nd x)) - zp, -127, 127); C' is the sum
+    over the non-outlier columns of the shifted codes' products and
+    C = fl16(C' / (nd_x nd_w) + sum over O of X W)."""
+    Xf = to_fractions(X)
+    Wf = to_fractions(W)
+    s, h = len(Xf), len(Xf[0])
+    o = len(Wf[0])
+    a = Fraction(float(alpha)) if alpha != float("inf") else None
+    O = [j for j in range(h) if a is not None and any(abs(Xf[i][j]) >= a for i in range(s))]
+    reg = [j for j in range(h) if j not in set(O)]
+
+    def params(vals):
+        lo, hi = (min(vals), max(vals)) if vals else (Fraction(0), Fraction(0))
+        span = fl32(hi - lo)
+        nd = fl32(Fraction(254) / span) if span != 0 else Fraction(1)
+        return nd, half_away(fl32(nd * lo)) + 127
+
+    def code(x, nd, zp):
+        return max(-127, min(127, half_away(fl32(nd * x)) - zp))
+
+    nd_x, zp_x, Xq = [], [], []
+    for i in range(s):
+        nd, zp = params([Xf[i][j] for j in reg])
+        nd_x.append(nd)
+        zp_x.append(zp)
+        Xq.append([code(Xf[i][j], nd, zp) if j in reg else 0 for j in range(h)])
+    nd_w, zp_w = [], []
+    Wq = [[0] * o for _ in range(h)]
+    for j in range(o):
+        nd, zp = params([Wf[k][j] for k in range(h)])
+        nd_w.append(nd)
+        zp_w.append(zp)
+        for k in range(h):
+            Wq[k][j] = code(Wf[k][j], nd, zp)
+    Cp = [[sum((Xq[i][k] + zp_x[i]) * (Wq[k][j] + zp_w[j]) for k in reg) for j in range(o)] for i in range(s)]
+    C = [[fl16(Fraction(Cp[i][j]) / (nd_x[i] * nd_w[j]) + sum((Xf[i][k] * Wf[k][j] for k in O), Fraction(0)))
+          for j in range(o)] for i in range(s)]
+    return O, nd_x, zp_x, Xq, nd_w, zp_w, Wq, Cp, C
