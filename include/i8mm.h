@@ -217,6 +217,86 @@ i8mm_status i8mm_pack_fp16_weights(const uint16_t* W, int64_t h, int64_t o, uint
 i8mm_status i8mm_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, int64_t h, int64_t o, uint16_t* C,
                            hipStream_t stream);
 
+/*
+ * Quantiser variants of Table 1 ([DIGEST] "Quantization Primitives: Absmax
+ * and Zeropoint Quantization" and "Vector-wise Quantization": tensor-wise
+ * absmax, row-wise absmax with one tensor-wide constant for W, and zeropoint
+ * vector-wise; each with the mixed-precision decomposition, or without it
+ * when alpha = +inf). The absmax variants reuse i8mm_int8_mixed_matmul: a
+ * tensor-wise constant is written to every entry of c_x (or c_w), so the
+ * product's 1 / (c_x (x) c_w) applies it unchanged.
+ */
+
+/*
+ * Tensor-wise absmax for X: c = fl32(127 / m), m the largest |X_ij| over all
+ * rows and the columns not in O (c = 1 when m == 0). Arguments and outputs
+ * as for i8mm_quantize_rowwise; c_x[i] = c for every row.
+ */
+i8mm_status i8mm_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h,
+                                     const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
+                                     int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
+                                     hipStream_t stream);
+
+/*
+ * Tensor-wise absmax for W (load time; used by tensor-wise and row-wise
+ * quantisation): one constant c = fl32(127 / max_ij |W_ij|). Arguments and
+ * outputs as for i8mm_quantize_colwise_weights; c_w[j] = c for every column.
+ */
+i8mm_status i8mm_quantize_weights_tensorwise(const uint16_t* W, int64_t h, int64_t o,
+                                             int8_t* Wq, float* c_w, hipStream_t stream);
+
+/*
+ * Zeropoint quantisation of each row of X over the columns not in O
+ * ([DIGEST] "Quantization Primitives", zeropoint: nd = 2 * 127 / (max - min)
+ * and a zero point; [PY] the zero-point passage). With min and max over the
+ * row's non-outlier values:
+ *   nd = fl32(254 / fl32(max - min))   (1 when max == min),
+ *   zp = round(fl32(nd * min)) + 127   (the pages print the zero point as a
+ *        garbled product of X and min; this reading makes the codes fill
+ *        [-127, 127] with q + zp ~ nd * x),
+ *   q  = clamp(round(fl32(nd * x)) - zp, -127, 127), rounding half away.
+ * X, mask, idx, n_out, Xq (0 in the columns in O), X_O and ldo as for
+ * i8mm_quantize_rowwise. nd_x: [s] fp32, zp_x: [s] int32 (the zero point
+ * can leave int16 for one-signed rows), rowsum_x: [s] int32, the sum of the
+ * row's codes (all written).
+ */
+i8mm_status i8mm_quantize_rowwise_zeropoint(const uint16_t* X, int64_t s, int64_t h,
+                                            const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
+                                            int8_t* Xq, float* nd_x, int32_t* zp_x, int32_t* rowsum_x,
+                                            uint16_t* X_O, int64_t ldo, hipStream_t stream);
+
+/*
+ * Zeropoint quantisation of each column of W over all h rows (load time),
+ * as above. Wq: panel layout (above); nd_w: [o] fp32; zp_w: [o] int32;
+ * colsum_w: [o] int32, the sum of the column's h codes (all written).
+ */
+i8mm_status i8mm_quantize_colwise_weights_zeropoint(const uint16_t* W, int64_t h, int64_t o,
+                                                    int8_t* Wq, float* nd_w, int32_t* zp_w, int32_t* colsum_w,
+                                                    hipStream_t stream);
+
+/*
+ * The zeropoint vector-wise product with the decomposition ([DIGEST]
+ * "Quantization Primitives": the product of two zeropoint-quantised
+ * matrices expands into the int8 product and three correction terms;
+ * [PY] the same four-term expansion):
+ *   C' = sum over k not in O of (Xq_ik + zp_x_i)(Wq_kj + zp_w_j)
+ *      = C_i32 + zp_w_j (rowsum_x_i + (h - |O|) zp_x_i) + zp_x_i colsum'_j,
+ *   C  = fp16( C' / (nd_x_i nd_w_j) + X_O W[idx, :] [+ bias] ),
+ * where C_i32 = Xq W_i8 (the int8 MFMA main loop of the absmax product) and
+ * colsum'_j = colsum_w_j minus the codes of column j in the outlier rows
+ * (read on the device). The correction is exact for zero points below 2^17
+ * in magnitude (sums in fp64 or int64); beyond, it is rounded in fp64.
+ * Arguments as for i8mm_int8_mixed_matmul, with nd_x / nd_w in place of
+ * c_x / c_w and the zero points and code sums from the two calls above;
+ * W (the fp16 weights, for the outlier rows) must not be NULL; bias may be.
+ */
+i8mm_status i8mm_zeropoint_matmul(const int8_t* Xq, const float* nd_x, const int32_t* zp_x,
+                                  const int32_t* rowsum_x, const uint16_t* X_O, int64_t ldo,
+                                  const int32_t* idx, const int32_t* n_out,
+                                  const int8_t* Wq, const float* nd_w, const int32_t* zp_w,
+                                  const int32_t* colsum_w, const uint16_t* W, const uint16_t* bias,
+                                  int64_t s, int64_t h, int64_t o, uint16_t* C, hipStream_t stream);
+
 /* Bytes at the start of the forward workspace that hold the cross-block
  * accumulator of the detection (the outlier mask being ORed together, or,
  * for inputs of at most 64 rows, the per-row maxima). */

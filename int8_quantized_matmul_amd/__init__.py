@@ -30,6 +30,14 @@ __all__ = [
     "forward",
     "pack_fp16_weights",
     "fp16_gemm",
+    "quantize_tensorwise",
+    "quantize_weights_tensorwise",
+    "quantize_rowwise_zeropoint",
+    "quantize_colwise_weights_zeropoint",
+    "zeropoint_matmul",
+    "SCHEMES",
+    "quantize_weights",
+    "variant_forward",
     "forward_workspace",
     "forward_workspace_views",
     "x_o_stride",
@@ -256,6 +264,134 @@ def fp16_gemm(X: torch.Tensor, Wp: torch.Tensor, C: Optional[torch.Tensor] = Non
                              s, h, o, _dev(C, "C", torch.float16, (s, o)), _stream(X))
     _check(st, "fp16_gemm")
     return C
+
+
+# ---------------------------------------------------------------- quantiser variants (Table 1)
+
+def quantize_weights_tensorwise(W: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Tensor-wise absmax for W: (Wq int8 panels, c_w fp32 [o] all equal to the
+    one constant 127 / max |W|)."""
+    h, o = W.shape
+    Wq = torch.empty(weight_panels_shape(h, o), dtype=torch.int8, device=W.device)
+    c_w = torch.empty((o,), dtype=torch.float32, device=W.device)
+    st = _lib.i8mm_quantize_weights_tensorwise(_dev(W, "W", torch.float16), h, o, _dev(Wq, "Wq", torch.int8),
+                                               _dev(c_w, "c_w", torch.float32), _stream(W))
+    _check(st, "quantize_weights_tensorwise")
+    return Wq, c_w
+
+
+def quantize_tensorwise(X: torch.Tensor, mask: torch.Tensor, idx: torch.Tensor, n_out: torch.Tensor
+                        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Tensor-wise absmax for X over the non-outlier columns: (Xq, c_x [s] all
+    equal, X_O), laid out as by quantize_rowwise."""
+    s, h = X.shape
+    dev = X.device
+    ldo = x_o_stride(h)
+    Xq = torch.empty((s, h), dtype=torch.int8, device=dev)
+    c_x = torch.empty((s,), dtype=torch.float32, device=dev)
+    X_O = torch.empty((s, ldo), dtype=torch.float16, device=dev)
+    st = _lib.i8mm_quantize_tensorwise(
+        _dev(X, "X", torch.float16), s, h, _dev(mask, "mask", torch.int32), _dev(idx, "idx", torch.int32),
+        _dev(n_out, "n_out", torch.int32, (1,)), _dev(Xq, "Xq", torch.int8), _dev(c_x, "c_x", torch.float32),
+        _dev(X_O, "X_O", torch.float16), ldo, _stream(X))
+    _check(st, "quantize_tensorwise")
+    return Xq, c_x, X_O
+
+
+def quantize_colwise_weights_zeropoint(W: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor,
+                                                                 torch.Tensor]:
+    """Zeropoint quantisation of the columns of W (load time): (Wq int8 panels,
+    nd_w fp32 [o], zp_w int32 [o], colsum_w int32 [o])."""
+    h, o = W.shape
+    dev = W.device
+    Wq = torch.empty(weight_panels_shape(h, o), dtype=torch.int8, device=dev)
+    nd_w = torch.empty((o,), dtype=torch.float32, device=dev)
+    zp_w = torch.empty((o,), dtype=torch.int32, device=dev)
+    cs_w = torch.empty((o,), dtype=torch.int32, device=dev)
+    st = _lib.i8mm_quantize_colwise_weights_zeropoint(
+        _dev(W, "W", torch.float16), h, o, _dev(Wq, "Wq", torch.int8), _dev(nd_w, "nd_w", torch.float32),
+        _dev(zp_w, "zp_w", torch.int32), _dev(cs_w, "colsum_w", torch.int32), _stream(W))
+    _check(st, "quantize_colwise_weights_zeropoint")
+    return Wq, nd_w, zp_w, cs_w
+
+
+def quantize_rowwise_zeropoint(X: torch.Tensor, mask: torch.Tensor, idx: torch.Tensor, n_out: torch.Tensor
+                               ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Zeropoint quantisation of the rows of X over the non-outlier columns:
+    (Xq int8 [s, h], nd_x fp32 [s], zp_x int32 [s], rowsum_x int32 [s], X_O)."""
+    s, h = X.shape
+    dev = X.device
+    ldo = x_o_stride(h)
+    Xq = torch.empty((s, h), dtype=torch.int8, device=dev)
+    nd_x = torch.empty((s,), dtype=torch.float32, device=dev)
+    zp_x = torch.empty((s,), dtype=torch.int32, device=dev)
+    rs_x = torch.empty((s,), dtype=torch.int32, device=dev)
+    X_O = torch.empty((s, ldo), dtype=torch.float16, device=dev)
+    st = _lib.i8mm_quantize_rowwise_zeropoint(
+        _dev(X, "X", torch.float16), s, h, _dev(mask, "mask", torch.int32), _dev(idx, "idx", torch.int32),
+        _dev(n_out, "n_out", torch.int32, (1,)), _dev(Xq, "Xq", torch.int8), _dev(nd_x, "nd_x", torch.float32),
+        _dev(zp_x, "zp_x", torch.int32), _dev(rs_x, "rowsum_x", torch.int32), _dev(X_O, "X_O", torch.float16), ldo,
+        _stream(X))
+    _check(st, "quantize_rowwise_zeropoint")
+    return Xq, nd_x, zp_x, rs_x, X_O
+
+
+def zeropoint_matmul(Xq: torch.Tensor, nd_x: torch.Tensor, zp_x: torch.Tensor, rowsum_x: torch.Tensor,
+                     X_O: torch.Tensor, idx: torch.Tensor, n_out: torch.Tensor, Wq: torch.Tensor,
+                     nd_w: torch.Tensor, zp_w: torch.Tensor, colsum_w: torch.Tensor, W: torch.Tensor,
+                     C: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C fp16 [s, o] = fp16(C' / (nd_x ⊗ nd_w) + X_O W[idx, :] [+ bias]), C' the
+    product of the zero-point-shifted codes over the non-outlier columns."""
+    s, h = Xq.shape
+    o = Wq.shape[1]
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.float16, device=Xq.device)
+    st = _lib.i8mm_zeropoint_matmul(
+        _dev(Xq, "Xq", torch.int8), _dev(nd_x, "nd_x", torch.float32, (s,)), _dev(zp_x, "zp_x", torch.int32, (s,)),
+        _dev(rowsum_x, "rowsum_x", torch.int32, (s,)), _dev(X_O, "X_O", torch.float16), X_O.shape[1],
+        _dev(idx, "idx", torch.int32), _dev(n_out, "n_out", torch.int32, (1,)),
+        _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)), _dev(nd_w, "nd_w", torch.float32, (o,)),
+        _dev(zp_w, "zp_w", torch.int32, (o,)), _dev(colsum_w, "colsum_w", torch.int32, (o,)),
+        _dev(W, "W", torch.float16, (h, o)), _bias_ptr(bias, o), s, h, o, _dev(C, "C", torch.float16, (s, o)),
+        _stream(Xq))
+    _check(st, "zeropoint_matmul")
+    return C
+
+
+SCHEMES = ("tensor", "row", "vector", "zeropoint")
+
+
+def quantize_weights(W: torch.Tensor, scheme: str) -> Tuple[torch.Tensor, ...]:
+    """Load-time weights for one quantiser scheme: (Wq, c_w) for "tensor" and
+    "row" (one constant) and "vector" (per column); (Wq, nd_w, zp_w, colsum_w)
+    for "zeropoint"."""
+    if scheme in ("tensor", "row"):
+        return quantize_weights_tensorwise(W)
+    if scheme == "vector":
+        return quantize_colwise_weights(W)
+    if scheme == "zeropoint":
+        return quantize_colwise_weights_zeropoint(W)
+    raise ValueError(f"unknown scheme {scheme!r}; one of {SCHEMES}")
+
+
+def variant_forward(X: torch.Tensor, qw: Tuple[torch.Tensor, ...], W: torch.Tensor, scheme: str,
+                    alpha: float = 6.0, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One forward of a quantiser scheme (Table 1) as a sequence of C-ABI
+    calls: detection at alpha (inf: no decomposition), the scheme's row
+    quantiser, then its product. qw comes from quantize_weights(W, scheme)."""
+    mask, idx, n_out = detect_outlier_cols(X, alpha)
+    if scheme == "zeropoint":
+        Xq, nd_x, zp_x, rs_x, X_O = quantize_rowwise_zeropoint(X, mask, idx, n_out)
+        Wq, nd_w, zp_w, cs_w = qw
+        return zeropoint_matmul(Xq, nd_x, zp_x, rs_x, X_O, idx, n_out, Wq, nd_w, zp_w, cs_w, W, bias=bias)
+    if scheme == "tensor":
+        Xq, c_x, X_O = quantize_tensorwise(X, mask, idx, n_out)
+    elif scheme in ("row", "vector"):
+        Xq, c_x, X_O = quantize_rowwise(X, mask, idx, n_out)
+    else:
+        raise ValueError(f"unknown scheme {scheme!r}; one of {SCHEMES}")
+    Wq, c_w = qw
+    return int8_mixed_matmul(Xq, c_x, X_O, idx, n_out, Wq, c_w, W, bias=bias)
 
 
 def forward_workspace(s: int, h: int, device) -> torch.Tensor:

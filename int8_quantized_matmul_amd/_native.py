@@ -27,6 +27,13 @@ _SIGNATURES = {
     "i8mm_int8_gemm_i32": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_p, c_p]),
     "i8mm_pack_fp16_weights": (c_int, [c_p, c_i64, c_i64, c_p, c_p]),
     "i8mm_fp16_gemm": (c_int, [c_p, c_p, c_i64, c_i64, c_i64, c_p, c_p]),
+    "i8mm_quantize_tensorwise": (c_int, [c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_p]),
+    "i8mm_quantize_weights_tensorwise": (c_int, [c_p, c_i64, c_i64, c_p, c_p, c_p]),
+    "i8mm_quantize_rowwise_zeropoint": (c_int, [c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                                                c_p, c_i64, c_p]),
+    "i8mm_quantize_colwise_weights_zeropoint": (c_int, [c_p, c_i64, c_i64, c_p, c_p, c_p, c_p, c_p]),
+    "i8mm_zeropoint_matmul": (c_int, [c_p, c_p, c_p, c_p, c_p, c_i64, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                                      c_i64, c_i64, c_i64, c_p, c_p]),
     "i8mm_forward_workspace_bytes": (c_size, [c_i64, c_i64]),
     "i8mm_forward": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     "i8mm_forward_workspace_layout": (c_int, [c_i64, c_i64, ctypes.POINTER(c_size), ctypes.POINTER(c_i64)]),

@@ -190,6 +190,75 @@ i8mm_status i8mm_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, int
     return launched(i8mm::launch_fp16_gemm(X, Wp, s, h, o, C, stream));
 }
 
+i8mm_status i8mm_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h,
+                                     const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
+                                     int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo, hipStream_t stream) {
+    if (!X || !mask || !idx || !n_out || !Xq || !c_x || !X_O) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h)) return I8MM_EINVAL;
+    if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
+    if (!aligned16(X) || !aligned16(mask) || !aligned16(idx) || !aligned16(n_out) || !aligned16(Xq) ||
+        !aligned16(c_x) || !aligned16(X_O))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_quantize_tensorwise(X, s, h, mask, Xq, c_x, X_O, ldo, stream));
+}
+
+i8mm_status i8mm_quantize_weights_tensorwise(const uint16_t* W, int64_t h, int64_t o, int8_t* Wq, float* c_w,
+                                             hipStream_t stream) {
+    if (!W || !Wq || !c_w) return I8MM_EINVAL;
+    if (!valid_shape_sh(1, h) || !valid_o(o)) return I8MM_EINVAL;
+    if (!aligned16(W) || !aligned16(Wq) || !aligned16(c_w)) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_quantize_weights_tensorwise(W, h, o, Wq, c_w, stream));
+}
+
+i8mm_status i8mm_quantize_rowwise_zeropoint(const uint16_t* X, int64_t s, int64_t h,
+                                            const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
+                                            int8_t* Xq, float* nd_x, int32_t* zp_x, int32_t* rowsum_x,
+                                            uint16_t* X_O, int64_t ldo, hipStream_t stream) {
+    if (!X || !mask || !idx || !n_out || !Xq || !nd_x || !zp_x || !rowsum_x || !X_O) return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h)) return I8MM_EINVAL;
+    if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
+    if (!aligned16(X) || !aligned16(mask) || !aligned16(idx) || !aligned16(n_out) || !aligned16(Xq) ||
+        !aligned16(nd_x) || !aligned16(zp_x) || !aligned16(rowsum_x) || !aligned16(X_O))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_quantize_rows_zp(X, s, h, mask, Xq, nd_x, zp_x, rowsum_x, X_O, ldo, stream));
+}
+
+i8mm_status i8mm_quantize_colwise_weights_zeropoint(const uint16_t* W, int64_t h, int64_t o, int8_t* Wq,
+                                                    float* nd_w, int32_t* zp_w, int32_t* colsum_w,
+                                                    hipStream_t stream) {
+    if (!W || !Wq || !nd_w || !zp_w || !colsum_w) return I8MM_EINVAL;
+    if (!valid_shape_sh(1, h) || !valid_o(o)) return I8MM_EINVAL;
+    if (!aligned16(W) || !aligned16(Wq) || !aligned16(nd_w) || !aligned16(zp_w) || !aligned16(colsum_w))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_quantize_cols_zp(W, h, o, Wq, nd_w, zp_w, colsum_w, stream));
+}
+
+i8mm_status i8mm_zeropoint_matmul(const int8_t* Xq, const float* nd_x, const int32_t* zp_x,
+                                  const int32_t* rowsum_x, const uint16_t* X_O, int64_t ldo,
+                                  const int32_t* idx, const int32_t* n_out,
+                                  const int8_t* Wq, const float* nd_w, const int32_t* zp_w,
+                                  const int32_t* colsum_w, const uint16_t* W, const uint16_t* bias,
+                                  int64_t s, int64_t h, int64_t o, uint16_t* C, hipStream_t stream) {
+    // bias may be null
+    if (!Xq || !nd_x || !zp_x || !rowsum_x || !X_O || !idx || !n_out || !Wq || !nd_w || !zp_w || !colsum_w ||
+        !W || !C)
+        return I8MM_EINVAL;
+    if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
+    if (ldo < round_up(h, 32) || ldo % 8 != 0) return I8MM_EINVAL;
+    if (!aligned16(Xq) || !aligned16(nd_x) || !aligned16(zp_x) || !aligned16(rowsum_x) || !aligned16(X_O) ||
+        !aligned16(idx) || !aligned16(n_out) || !aligned16(Wq) || !aligned16(nd_w) || !aligned16(zp_w) ||
+        !aligned16(colsum_w) || !aligned16(W) || !aligned16(bias) || !aligned16(C))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_int8_gemm(i8mm::GemmOut::ZeroPoint, Xq, nd_x, X_O, ldo, idx, n_out, Wq, nd_w, W,
+                                           bias, s, h, o, C, stream, nullptr, 0,
+                                           i8mm::ZpArgs{zp_x, rowsum_x, zp_w, colsum_w}));
+}
+
 size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h) {
     if (!valid_shape_sh(s, h)) return 0;
     size_t off[7], total;

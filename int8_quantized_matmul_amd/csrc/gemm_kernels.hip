@@ -217,7 +217,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     const uint16_t* __restrict__ X_O, int64_t ldo,
                     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out,
                     const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ Cout,
-                    uint32_t* __restrict__ clear, int clear_words) {
+                    uint32_t* __restrict__ clear, int clear_words, ZpArgs zp) {
     __shared__ v4i A0[kBuf], A1[kBuf], B0[kBuf], B1[kBuf];
     __shared__ __attribute__((aligned(16))) uint16_t olds[2 * kSlice];
     if (blockIdx.x == 0)
@@ -274,7 +274,8 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     // and the scales of this wavefront's rows and columns to registers: the
     // loads complete under the main loop.
     int n_o = 0;
-    constexpr bool mixed = MODE == GemmOut::Mixed;
+    constexpr bool zpm = MODE == GemmOut::ZeroPoint;
+    constexpr bool mixed = MODE == GemmOut::Mixed || zpm;   // fused fp16 epilogue with outliers
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(mixed && W ? W + o0 : nullptr,
                                                 mixed && W ? static_cast<uint32_t>((h * o - o0) * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(mixed ? X_O + s0 * ldo : nullptr,
@@ -463,7 +464,12 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         };
         uint16_t* out_st = wid < 3 ? reinterpret_cast<uint16_t*>(A1) + wid * kOutWave : reinterpret_cast<uint16_t*>(B1);
         float* invw = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(B1) + kOutWave) + wid * 128;
-        float* bsl = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(A1) + 3 * kOutWave) + wid * 128;
+        // after the staging of waves 0-2 in A1: bias, then (zeropoint) zp_w
+        // and the column code sums over the non-outlier rows, 128 per wave
+        float* a1_tail = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(A1) + 3 * kOutWave);
+        float* bsl = a1_tail + wid * 128;
+        int* zpw_l = reinterpret_cast<int*>(a1_tail + 512) + wid * 128;
+        int* csw_l = reinterpret_cast<int*>(a1_tail + 1024) + wid * 128;
         // The layer bias of the wave's 128 columns (fp16 -> fp32, exact),
         // fetched under the outlier staging below.
         // Range-checked loads with no branch around them (columns past o, or
@@ -491,6 +497,22 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 #pragma unroll
             for (int i = 0; i < 2; ++i) bsl[lane + 64 * i] = half_bits_to_float(bias_bits[i]);
         }
+        if constexpr (zpm) {
+            // sum over k not in O of Wq_kj = the column's code sum minus the
+            // codes of the outlier rows (read from the panels)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int64_t col = o0 + wo * 128 + lane + 64 * i;
+                const bool ok = col < o;
+                int cs = ok ? zp.colsum_w[col] : 0;
+                for (int q = 0; q < n_o; ++q) {
+                    const int64_t k = idx[q];
+                    if (ok) cs -= Wq[(k >> 6) * o * 64 + col * 64 + (k & 63)];
+                }
+                zpw_l[lane + 64 * i] = ok ? zp.zp_w[col] : 0;
+                csw_l[lane + 64 * i] = cs;
+            }
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (once && !w8) {
@@ -503,17 +525,44 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             const float inv_x = __builtin_amdgcn_rcpf(cx_pf[sb]);
+            // zeropoint: zp_x of the lane's row and rowsum + (h - |O|) zp_x
+            double zx = 0.0, zr = 0.0;
+            if constexpr (zpm) {
+                const int64_t srow = s0 + ws * 128 + sb * 32 + r32;
+                if (srow < s) {
+                    const int z = zp.zp_x[srow];
+                    zx = static_cast<double>(z);
+                    zr = static_cast<double>(static_cast<int64_t>(zp.rowsum_x[srow]) + (h - n_o) * static_cast<int64_t>(z));
+                }
+            }
             if (!once) __syncthreads();   // the previous row block's rounds are done
 #pragma unroll
             for (int ob = 0; ob < 4; ++ob) {
-                // Dequantise: f = C_i32 * (1/c_x) * (1/c_w).
+                // Dequantise: f = C_i32 * (1/c_x) * (1/c_w); zeropoint:
+                // C' = C_i32 + zp_w (rowsum + (h - |O|) zp_x) + zp_x colsum'
+                // by two fp64 FMAs (exact while every term is below 2^53,
+                // i.e. for zero points below 2^17 in magnitude), times
+                // (1/nd_x) * (1/nd_w). fp64 rather than int64 keeps the
+                // accumulators in registers.
                 v16f f;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const v4f iw = *reinterpret_cast<const v4f*>(invw + ob * 32 + 8 * g + 4 * khalf);
+                    if constexpr (zpm) {
+                        const v4i zw = *reinterpret_cast<const v4i*>(zpw_l + ob * 32 + 8 * g + 4 * khalf);
+                        const v4i cw = *reinterpret_cast<const v4i*>(csw_l + ob * 32 + 8 * g + 4 * khalf);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        f[4 * g + e] = static_cast<float>(acc[ob][sb][4 * g + e]) * (inv_x * iw[e]);
+                        for (int e = 0; e < 4; ++e) {
+                            const double cp = __fma_rn(zx, static_cast<double>(cw[e]),
+                                                       __fma_rn(static_cast<double>(zw[e]), zr,
+                                                                static_cast<double>(acc[ob][sb][4 * g + e])));
+                            f[4 * g + e] = static_cast<float>(cp) * (inv_x * iw[e]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            f[4 * g + e] = static_cast<float>(acc[ob][sb][4 * g + e]) * (inv_x * iw[e]);
+                    }
                 }
                 // Outlier product X_O W[idx, :] on top (fp32 accumulate).
                 if (once) {
@@ -649,7 +698,7 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
                                                      const int32_t* __restrict__ n_out,
                                                      const uint16_t* __restrict__ W,
                                                      const uint16_t* __restrict__ bias, void* __restrict__ Cout,
-                                                     uint32_t* __restrict__ clear, int clear_words) {
+                                                     uint32_t* __restrict__ clear, int clear_words, ZpArgs zp) {
     __shared__ v4i red[kDecodeSplit][NT][64];
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
@@ -673,7 +722,7 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     int n_o = 0;
     v8h pre[2];
     uint2 bias4 = make_uint2(0u, 0u);   // the layer bias of this lane's 4 output columns
-    if constexpr (MODE == GemmOut::Mixed) {
+    if constexpr (MODE == GemmOut::Mixed || MODE == GemmOut::ZeroPoint) {
         n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
         if (wid < NT && n_o > 0)
             outlier_operands_16(0, n_o, lane, obase + wid * 16, 0, s, o, X_O, ldo, idx, W, Wq, c_w, pre[0], pre[1]);
@@ -739,8 +788,30 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
         const float inv_x = __builtin_amdgcn_rcpf(srow < s ? c_x[srow] : 1.0f);
         const v4f cw = *reinterpret_cast<const v4f*>(c_w + ocol);
         v4f f;
+        if constexpr (MODE == GemmOut::ZeroPoint) {
+            // C' = C_i32 + zp_w (rowsum + (h - |O|) zp_x) + zp_x colsum', exact
+            // in int64 (colsum' = the column's code sum over the non-outlier rows)
+            const int zx = srow < s ? zp.zp_x[srow] : 0;
+            const int64_t zr =
+                srow < s ? static_cast<int64_t>(zp.rowsum_x[srow]) + (h - n_o) * static_cast<int64_t>(zx) : 0;
+            const v4i zw = *reinterpret_cast<const v4i*>(zp.zp_w + ocol);
+            v4i cs = *reinterpret_cast<const v4i*>(zp.colsum_w + ocol);
+            for (int q = 0; q < n_o; ++q) {
+                const int64_t k = idx[q];
+                const int8_t* p = Wq + (k >> 6) * o * 64 + ocol * 64 + (k & 63);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+                for (int e = 0; e < 4; ++e) cs[e] -= p[e * 64];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t cp = static_cast<int64_t>(sum[e]) + static_cast<int64_t>(zw[e]) * zr +
+                                   static_cast<int64_t>(zx) * static_cast<int64_t>(cs[e]);
+                f[e] = static_cast<float>(cp) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+        }
         f = outlier_tile_16x16(f, lane, obase + nt * 16, 0, s, o, X_O, ldo, idx, n_o, W, Wq, c_w, pre);
         if (bias != nullptr) {
             f[0] += half_bits_to_float(bias4.x & 0xffffu);
@@ -781,16 +852,16 @@ template <GemmOut MODE>
 hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, int64_t ldo,
                        const int32_t* idx, const int32_t* n_out, const int8_t* Wq, const float* c_w,
                        const uint16_t* W, const uint16_t* bias, int64_t s, int64_t h, int64_t o, void* C,
-                       hipStream_t stream, uint32_t* clear, int clear_words) {
+                       hipStream_t stream, uint32_t* clear, int clear_words, ZpArgs zp) {
     if (s <= 16) {
         constexpr int NT = 2;
         hipLaunchKernelGGL((k_gemm_decode<MODE, NT>), dim3(static_cast<unsigned>(o / (16 * NT))), dim3(256), 0,
                            stream, Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear,
-                           clear_words);
+                           clear_words, zp);
     } else {
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
         hipLaunchKernelGGL((k_gemm_prefill<MODE>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
-                           Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words);
+                           Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp);
     }
     return hipGetLastError();
 }
@@ -802,12 +873,15 @@ hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                             const int32_t* idx, const int32_t* n_out,
                             const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
                             int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
-                            uint32_t* clear, int clear_words) {
+                            uint32_t* clear, int clear_words, ZpArgs zp) {
     if (mode == GemmOut::Int32)
         return launch_mode<GemmOut::Int32>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, nullptr, s, h, o, C, stream,
-                                           clear, clear_words);
+                                           clear, clear_words, ZpArgs{});
+    if (mode == GemmOut::ZeroPoint)
+        return launch_mode<GemmOut::ZeroPoint>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s, h, o, C,
+                                               stream, clear, clear_words, zp);
     return launch_mode<GemmOut::Mixed>(Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s, h, o, C, stream,
-                                       clear, clear_words);
+                                       clear, clear_words, ZpArgs{});
 }
 
 hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, int64_t h, int64_t o, uint16_t* C,
@@ -816,7 +890,7 @@ hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, in
     const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
     hipLaunchKernelGGL((k_gemm_prefill<GemmOut::Fp16Dense>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
                        reinterpret_cast<const int8_t*>(X), reinterpret_cast<const int8_t*>(Wp), s, 2 * h, o,
-                       nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, C, nullptr, 0);
+                       nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, C, nullptr, 0, ZpArgs{});
     return hipGetLastError();
 }
 

@@ -28,19 +28,47 @@ hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, floa
 hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
                                 int8_t* Wq, float* c_w, hipStream_t stream);
 
+// Tensor-wise absmax: one constant for all of X's non-outlier part (written
+// to every c_x[i]) or for all of W (every c_w[j]); same outputs otherwise.
+hipError_t launch_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h, const uint32_t* mask, int8_t* Xq,
+                                      float* c_x, uint16_t* X_O, int64_t ldo, hipStream_t stream);
+hipError_t launch_quantize_weights_tensorwise(const uint16_t* W, int64_t h, int64_t o, int8_t* Wq, float* c_w,
+                                              hipStream_t stream);
+
+// Zeropoint quantisation: rows of X over the non-outlier columns (codes,
+// nd_x, zp_x, code sums over the row, X_O gather) and columns of W at load
+// time (panel codes, nd_w, zp_w, code sums over the column).
+hipError_t launch_quantize_rows_zp(const uint16_t* X, int64_t s, int64_t h, const uint32_t* mask, int8_t* Xq,
+                                   float* nd_x, int32_t* zp_x, int32_t* rowsum_x, uint16_t* X_O, int64_t ldo,
+                                   hipStream_t stream);
+hipError_t launch_quantize_cols_zp(const uint16_t* W, int64_t h, int64_t o, int8_t* Wq, float* nd_w, int32_t* zp_w,
+                                   int32_t* colsum_w, hipStream_t stream);
+
 // mode: product variant of the shared int8 main loop. W (Mixed only) may be
 // null: outlier rows rebuilt from Wq / c_w. bias (Mixed only, optional):
 // fp16 [o] added before the rounding. `clear` (optional): clear_words
 // uint32 words that the first block zeroes (the forward path's
 // accumulator, whose readers have finished by then).
-enum class GemmOut { Mixed = 0, Int32 = 1, Fp16Dense = 2 };
+// ZeroPoint: the product of zeropoint codes, C' = sum over k not in O of
+// (Xq_ik + zp_x_i)(Wq_kj + zp_w_j), dequantised with 1 / (nd_x nd_w) (passed
+// as c_x, c_w) plus the fp16 outlier product; ZpArgs carries the zero points
+// and code sums (rowsum over the row's codes, colsum over all h codes of the
+// column).
+enum class GemmOut { Mixed = 0, Int32 = 1, Fp16Dense = 2, ZeroPoint = 3 };
+
+struct ZpArgs {
+    const int32_t* zp_x;
+    const int32_t* rowsum_x;
+    const int32_t* zp_w;
+    const int32_t* colsum_w;
+};
 
 hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
                             const uint16_t* X_O, int64_t ldo,
                             const int32_t* idx, const int32_t* n_out,
                             const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
                             int64_t s, int64_t h, int64_t o, void* C, hipStream_t stream,
-                            uint32_t* clear = nullptr, int clear_words = 0);
+                            uint32_t* clear = nullptr, int clear_words = 0, ZpArgs zp = ZpArgs{});
 
 // Dense fp16 product C = fp16(X W) with fp32 accumulation; Wp is W in the
 // fp16 panel layout [h / 32][o][32] (see launch_pack_fp16_panels).

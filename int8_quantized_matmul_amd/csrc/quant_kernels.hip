@@ -14,32 +14,12 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "quant_common.h"
 
 #include <cmath>
 
 namespace i8mm {
 namespace {
-
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-    return __builtin_bit_cast(uint32_t,
-                              __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
-}
-__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
-    return __builtin_bit_cast(uint32_t,
-                              __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
-}
-__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b) {   // lane-wise, modulo 2^16
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a) - __builtin_bit_cast(u16x2, b));
-}
-
-constexpr uint32_t kAbs2 = 0x7fff7fffu;     // clears the sign bits of both fp16 halves
-constexpr uint32_t kInfBits = 0x7c00u;      // +inf; larger |x| patterns are NaN
-
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int k) {
-    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-}
 
 // ---------------------------------------------------------------------------
 // Outlier test ([DIGEST] "The Full LLM.int8() Algorithm", Step 1: column j
@@ -68,47 +48,6 @@ __device__ __forceinline__ uint32_t detect_flags(const uint4& d, uint32_t span) 
 #pragma unroll
     for (int e = 0; e < 8; ++e) f |= (((word_of(d, e >> 1) >> ((e & 1) * 16)) & 0xffffu) <= span ? 1u : 0u) << e;
     return f;
-}
-
-// ---------------------------------------------------------------------------
-// Per-chunk row work ([DIGEST] Step 4; [TM] "Absmax INT8 quantization from
-// first principles").
-
-// The chunk with the values whose bit in `bits` is set replaced by +0.
-__device__ __forceinline__ uint4 chunk_clear(const uint4& v, uint32_t bits) {
-    auto keep = [&](int k) {
-        const uint32_t lo = (bits >> (2 * k)) & 1u ? 0u : 0x0000ffffu;
-        const uint32_t hi = (bits >> (2 * k + 1)) & 1u ? 0u : 0xffff0000u;
-        return lo | hi;
-    };
-    return make_uint4(v.x & keep(0), v.y & keep(1), v.z & keep(2), v.w & keep(3));
-}
-
-// Running packed maximum of the |x| bit patterns of a chunk.
-__device__ __forceinline__ uint32_t chunk_absmax_fold(const uint4& v, uint32_t m2) {
-    return pk_max_u16(pk_max_u16(m2, v.x & kAbs2),
-                      pk_max_u16(pk_max_u16(v.y & kAbs2, v.z & kAbs2), v.w & kAbs2));
-}
-
-// The larger of the two halves of a packed maximum, as a float.
-__device__ __forceinline__ float absmax_value(uint32_t m2) {
-    const uint32_t a = m2 & 0xffffu, b = m2 >> 16;
-    return half_bits_to_float(a > b ? a : b);
-}
-
-// The 8 quantised values of a chunk, packed bytewise.
-__device__ __forceinline__ uint2 chunk_quantize(const uint4& v, float sc) {
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int q = quantize_one(half_bits_to_float((word_of(v, e >> 1) >> ((e & 1) * 16)) & 0xffffu), sc);
-        packed[e >> 2] |= (static_cast<uint32_t>(q) & 0xffu) << ((e & 3) * 8);
-    }
-    return make_uint2(packed[0], packed[1]);
-}
-
-__device__ __forceinline__ uint4 load_chunk(const uint16_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -196,55 +135,6 @@ __global__ __launch_bounds__(1024) void k_compact(const uint32_t* __restrict__ m
     if (t == 0) n_out[0] = wsum[15];
 }
 
-// Exclusive prefix sum of the popcounts of mask words [0, nw) into pre[]
-// (LDS), for a block of `nthr` threads; returns |O|.
-__device__ __forceinline__ int block_mask_prefix(const uint32_t* smask, int* pre, int nw, int* wsum, int nthr) {
-    const int t = threadIdx.x, lane = t & 63, wid = t >> 6, nwav = nthr / 64;
-    const int per = (nw + nthr - 1) / nthr;
-    const int w0 = t * per;
-    const int w1 = w0 + per < nw ? w0 + per : nw;
-    int cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(smask[w]);
-    const int incl = wave_inclusive_scan(cnt, lane);
-    if (lane == 63) wsum[wid] = incl;
-    __syncthreads();
-    if (wid == 0) {
-        int v = lane < nwav ? wsum[lane] : 0;
-        v = wave_inclusive_scan(v, lane);
-        if (lane < nwav) wsum[lane] = v;
-    }
-    __syncthreads();
-    int run = (wid > 0 ? wsum[wid - 1] : 0) + incl - cnt;
-    for (int w = w0; w < w1; ++w) {
-        pre[w] = run;
-        run += __popc(smask[w]);
-    }
-    const int n = wsum[nwav - 1];
-    __syncthreads();
-    return n;
-}
-
-// Writes mask[], idx[0 .. n) and n_out from the LDS mask and its prefix.
-__device__ __forceinline__ void emit_outlier_set(const uint32_t* smask, const int* pre, int nw, int n,
-                                                 uint32_t* __restrict__ mask, int32_t* __restrict__ idx,
-                                                 int32_t* __restrict__ n_out, int nthr) {
-    for (int w = threadIdx.x; w < nw; w += nthr) {
-        uint32_t bits = smask[w];
-        if (mask) mask[w] = bits;
-        int r = pre[w];
-        while (bits) {
-            idx[r++] = w * 32 + (__ffs(bits) - 1);
-            bits &= bits - 1u;
-        }
-    }
-    if (threadIdx.x == 0) n_out[0] = n;
-}
-
-// Rank of outlier column j (bit j set) among the outlier columns.
-__device__ __forceinline__ int outlier_rank(const uint32_t* smask, const int* pre, int j) {
-    return pre[j >> 5] + __popc(smask[j >> 5] & ((1u << (j & 31)) - 1u));
-}
-
 // ---------------------------------------------------------------------------
 // Row-wise absmax quantisation over the non-outlier columns plus the gather
 // of the outlier columns ([DIGEST] "The Full LLM.int8() Algorithm", Steps 2
@@ -261,8 +151,14 @@ __device__ __forceinline__ int outlier_rank(const uint32_t* smask, const int* pr
 // lane), otherwise the second pass re-reads it (an L2 hit). If idx is
 // non-null, block 0 also writes the index list and |O| (and the mask to
 // `mask_out` if that is non-null).
+// SC selects where the scale comes from: Absmax (the row's own, written to
+// c_x), MaxOnly (only the row's absmax over the non-outlier columns is
+// written, as a float, to c_x; nothing else), or Given (c_x[i] already holds
+// the scale, e.g. one constant for the whole tensor, and is only read).
 // Dynamic LDS: nw mask words + nw prefix counts.
-template <int CPL>
+enum class RowScale { Absmax, MaxOnly, Given };
+
+template <int CPL, RowScale SC = RowScale::Absmax>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ X, int64_t s, int64_t h,
                                                     const uint32_t* __restrict__ src_mask,
                                                     uint32_t* __restrict__ mask_out, int32_t* __restrict__ idx,
@@ -300,6 +196,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
     auto split = [&](const uint4& v, int64_t c) {
         const uint32_t bits = bits_of(c);
         if (!bits) return v;
+        if constexpr (SC == RowScale::MaxOnly) return chunk_clear(v, bits);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             if ((bits >> e) & 1u)
@@ -322,8 +219,17 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m2 = pk_max_u16(m2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2), off, kWave)));
-    const float sc = absmax_scale(absmax_value(m2));
-    if (lane == 0) c_x[i] = sc;
+    if constexpr (SC == RowScale::MaxOnly) {
+        if (lane == 0) c_x[i] = absmax_value(m2);
+        return;
+    }
+    float sc;
+    if constexpr (SC == RowScale::Given) {
+        sc = c_x[i];
+    } else {
+        sc = absmax_scale(absmax_value(m2));
+        if (lane == 0) c_x[i] = sc;
+    }
 
     int8_t* qr = Xq + i * h;
     if constexpr (CPL > 0) {
@@ -472,6 +378,27 @@ __global__ __launch_bounds__(256) void k_small_quant(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// One absmax constant for a whole tensor ([DIGEST] "Quantization Primitives":
+// tensor-wise absmax, 127 over the tensor's largest magnitude) from the
+// per-row (or per-column) maxima m[0 .. n): c = fl32(127 / max m) (1 when
+// the max is 0) is written over m[0 .. n), so that a per-row (per-column)
+// quantiser reading its own entry applies the one constant. One block.
+__global__ __launch_bounds__(1024) void k_tensor_scale(float* __restrict__ m, int64_t n) {
+    __shared__ float wmax[16];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    float v = 0.0f;
+    for (int64_t i = t; i < n; i += 1024) v = fmaxf(v, m[i]);
+    v = wave_max(v);
+    if (lane == 0) wmax[wid] = v;
+    __syncthreads();
+    float mx = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) mx = fmaxf(mx, wmax[w]);
+    const float c = absmax_scale(mx);
+    for (int64_t i = t; i < n; i += 1024) m[i] = c;
+}
+
+// ---------------------------------------------------------------------------
 // Load-time column-wise quantisation of W [h, o] into the panel layout
 // Wq [h / 64][o][64] (W_i8[k, j] at (k / 64) o 64 + 64 j + k % 64)
 // ([DIGEST] "The Full LLM.int8() Algorithm", Step 4; "Why vector-wise
@@ -481,6 +408,9 @@ __global__ __launch_bounds__(256) void k_small_quant(const uint16_t* __restrict_
 // all h rows (thread = 8 columns x every 32nd row; one wavefront reads 8
 // rows x 128 bytes). Pass 2: 64x64 tiles are quantised, transposed through
 // LDS and written as the strip's contiguous 4 KiB of each panel.
+// SC as for k_quant_rows: MaxOnly writes the column absmax to c_w and stops
+// after pass 1; Given skips pass 1 and quantises with the scales in c_w.
+template <RowScale SC = RowScale::Absmax>
 __global__ __launch_bounds__(256) void k_quant_cols(const uint16_t* __restrict__ W, int64_t h, int64_t o,
                                                     int8_t* __restrict__ Wq, float* __restrict__ c_w) {
     __shared__ float red[32][65];
@@ -490,6 +420,10 @@ __global__ __launch_bounds__(256) void k_quant_cols(const uint16_t* __restrict__
     const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 64;
     const int cc = t & 7, rg = t >> 3;
 
+    if constexpr (SC == RowScale::Given) {
+        if (t < 64) scale[t] = c_w[j0 + t];
+        __syncthreads();
+    } else {
     float m[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) m[e] = 0.0f;
@@ -506,11 +440,17 @@ __global__ __launch_bounds__(256) void k_quant_cols(const uint16_t* __restrict__
     if (t < 64) {
         float mm = 0.0f;
         for (int g = 0; g < 32; ++g) mm = fmaxf(mm, red[g][t]);
-        const float sc = absmax_scale(mm);
-        scale[t] = sc;
-        c_w[j0 + t] = sc;
+        if constexpr (SC == RowScale::MaxOnly) {
+            c_w[j0 + t] = mm;
+        } else {
+            const float sc = absmax_scale(mm);
+            scale[t] = sc;
+            c_w[j0 + t] = sc;
+        }
     }
+    if constexpr (SC == RowScale::MaxOnly) return;
     __syncthreads();
+    }
 
     for (int64_t r0 = 0; r0 < h; r0 += 64) {
 #pragma unroll
@@ -666,8 +606,30 @@ hipError_t launch_pack_fp16_panels(const uint16_t* W, int64_t h, int64_t o, uint
 
 hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
                                 int8_t* Wq, float* c_w, hipStream_t stream) {
-    hipLaunchKernelGGL(k_quant_cols, dim3(static_cast<unsigned>(o / 64)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(k_quant_cols<RowScale::Absmax>, dim3(static_cast<unsigned>(o / 64)), dim3(256), 0, stream,
                        W, h, o, Wq, c_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h, const uint32_t* mask, int8_t* Xq,
+                                      float* c_x, uint16_t* X_O, int64_t ldo, hipStream_t stream) {
+    // row maxima into c_x, one constant over them, then the codes with it
+    const dim3 grid(static_cast<unsigned>((s + 3) / 4)), block(256);
+    const size_t dyn = static_cast<size_t>(2 * (h / 32) * 4);
+    hipLaunchKernelGGL((k_quant_rows<0, RowScale::MaxOnly>), grid, block, dyn, stream, X, s, h, mask, nullptr,
+                       nullptr, nullptr, Xq, c_x, X_O, ldo);
+    hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(1024), 0, stream, c_x, s);
+    hipLaunchKernelGGL((k_quant_rows<0, RowScale::Given>), grid, block, dyn, stream, X, s, h, mask, nullptr,
+                       nullptr, nullptr, Xq, c_x, X_O, ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_weights_tensorwise(const uint16_t* W, int64_t h, int64_t o, int8_t* Wq, float* c_w,
+                                              hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(o / 64)), block(256);
+    hipLaunchKernelGGL(k_quant_cols<RowScale::MaxOnly>, grid, block, 0, stream, W, h, o, Wq, c_w);
+    hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(1024), 0, stream, c_w, o);
+    hipLaunchKernelGGL(k_quant_cols<RowScale::Given>, grid, block, 0, stream, W, h, o, Wq, c_w);
     return hipGetLastError();
 }
 

@@ -108,3 +108,21 @@ def test_valid_call_without_gpu_reports_no_device():
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert _lib().i8mm_int8_gemm_i32(P, P, 1, 64, 64, P, None) == -2
+
+
+def test_variant_entry_points_reject():
+    """The quantiser variants validate like the main entry points."""
+    lib = _lib()
+    assert lib.i8mm_quantize_tensorwise(P, 4, 128, P, P, P, P, P, P, 96, None) == -1        # ldo < h
+    assert lib.i8mm_quantize_tensorwise(P, 4, 100, P, P, P, P, P, P, 128, None) == -1       # h % 64
+    assert lib.i8mm_quantize_weights_tensorwise(P, 64, 65, P, P, None) == -1
+    assert lib.i8mm_quantize_weights_tensorwise(P, 64, 64, MIS, P, None) == -1
+    assert lib.i8mm_quantize_rowwise_zeropoint(P, 4, 128, P, P, P, P, P, None, P, P, 128, None) == -1
+    assert lib.i8mm_quantize_rowwise_zeropoint(P, 4, 128, P, P, P, P, P, P, P, P, 132, None) == -1
+    assert lib.i8mm_quantize_colwise_weights_zeropoint(P, 64, 64, P, P, P, None, None) == -1
+    assert lib.i8mm_quantize_colwise_weights_zeropoint(P, 96, 64, P, P, P, P, None) == -1
+    # W is required by the zeropoint product; bias must be aligned
+    args = [P, P, P, P, P, 64, P, P, P, P, P, P]
+    assert lib.i8mm_zeropoint_matmul(*args, None, None, 4, 64, 64, P, None) == -1
+    assert lib.i8mm_zeropoint_matmul(*args, P, MIS, 4, 64, 64, P, None) == -1
+    assert lib.i8mm_zeropoint_matmul(*args, P, None, 4, 65536, 32768, P, None) == -1
