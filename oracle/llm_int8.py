@@ -232,13 +232,17 @@ def dequantize_and_add(C_i32: np.ndarray, c_x: np.ndarray, c_w: np.ndarray,
 def dequantized_outlier_rows(Wq_t: np.ndarray, c_w: np.ndarray, idx: np.ndarray) -> np.ndarray:
     """Outlier rows W^O when no fp16 copy of W is kept (a storage variant; the
     pages' Step 3 uses the original fp16 rows, [DIGEST] "The Full LLM.int8()
-    Algorithm"): W^O[k, j] = fl16(W_i8[idx[k], j] / c_w[j]), the int8 code
-    divided by its column scale (quotient in float64), rounded to fp16.
-    Only the int8 weights and their scales then stay resident, the memory
-    saving of [DIGEST] "Executive Summary" (1.96x on BLOOM-176B)."""
+    Algorithm"): the int8 code dequantised by multiplying back with the
+    inverse scale ([PY] "量化为什么会崩：一个尺度统治全局":
+    dequantisation multiplies back by 1/s), W^O[k, j] = fl16(fl32(W_i8[idx[k], j]
+    * fl32(1 / c_w[j]))): the reciprocal and the product each rounded to
+    fp32, the result rounded once to fp16. Only the int8 weights and their
+    scales then stay resident, the memory saving of [DIGEST] "Executive
+    Summary" (1.96x on BLOOM-176B)."""
     idx = np.asarray(idx, dtype=np.int64)
-    q = Wq_t[:, idx].T.astype(F64)                        # [|O|, o]
-    return (q / c_w.astype(F64)[None, :]).astype(np.float16)
+    q = Wq_t[:, idx].T.astype(F32)                        # [|O|, o], exact
+    inv = (F32(1.0) / np.asarray(c_w, dtype=F32)).astype(F32)
+    return (q * inv[None, :]).astype(F32).astype(np.float16)
 
 
 def int8_mixed_matmul(Xq: np.ndarray, c_x: np.ndarray, X_O: np.ndarray, idx: np.ndarray,

@@ -6,8 +6,8 @@ nothing on the product path may import, call or run it).
 "Vector-wise Quantization" (Table 1's hierarchy: tensor-wise absmax,
 row-wise absmax with one tensor-wide constant for W, vector-wise, and
 zeropoint vector-wise, each also with the mixed-precision decomposition);
-[PY] "零点量化的思路" passage (the four-term product on GPUs) and the
-paragraph on granularity (row-wise, vector-wise); [TM] "Absmax INT8
+[PY] "量化为什么会崩：一个尺度统治全局" (the zero point and the four-term product on GPUs;
+row-wise and vector-wise granularity); [TM] "Absmax INT8
 quantization from first principles".
 
 Every variant keeps the decomposition of the main path: the outlier columns
@@ -149,7 +149,7 @@ def zeropoint_product_i64(Xq: np.ndarray, zp_x: np.ndarray, Wq_t: np.ndarray, zp
     """C'_ij = sum over k not in O of (Xq_ik + zp_x_i)(Wq_kj + zp_w_j), exact
     in int64: the product of the zero-point-shifted codes ([DIGEST]
     "Quantization Primitives", the product of two zeropoint-quantised
-    matrices; [PY] "零点量化的思路"), taken as written, not expanded."""
+    matrices; [PY] "量化为什么会崩：一个尺度统治全局"), taken as written, not expanded."""
     h = Xq.shape[1]
     reg = _regular(h, idx)
     A = Xq[:, reg].astype(np.int64) + np.asarray(zp_x, dtype=np.int64)[:, None]

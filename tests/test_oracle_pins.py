@@ -422,9 +422,11 @@ def test_rebuilt_outlier_rows_equal_fp16_rows_when_lossless():
     assert np.array_equal(a["C"].view(np.uint16), b["C"].view(np.uint16))
 
 
-def test_rebuilt_outlier_rows_are_rounded_quotients():
-    """Each rebuilt weight is the exact quotient code / c_w rounded once to
-    fp16 (checked with rational arithmetic), for ordinary weights."""
+def test_rebuilt_outlier_rows_are_rounded_products_with_the_inverse_scale():
+    """Each rebuilt weight is fl16(fl32(code * fl32(1 / c_w))), every rounding
+    emulated from its IEEE definition with rational arithmetic, for ordinary
+    weights; and it lies within one fp16 ulp (plus the two fp32 roundings)
+    of the exact quotient code / c_w, i.e. of the dequantised value."""
     rng = np.random.default_rng(22)
     W = (rng.standard_normal((64, 24)) * 0.02).astype(np.float16)
     Wq_t, c_w = oracle.quantize_colwise_weights(W)
@@ -432,8 +434,11 @@ def test_rebuilt_outlier_rows_are_rounded_quotients():
     rows = oracle.dequantized_outlier_rows(Wq_t, c_w, idx)
     for a, k in enumerate(idx):
         for j in range(24):
-            exact = Fraction(int(Wq_t[j, k])) / Fraction(float(c_w[j]))
-            assert Fraction(float(rows[a, j])) == rational.fl16(exact)
+            q = Fraction(int(Wq_t[j, k]))
+            inv = rational.fl32(1 / Fraction(float(c_w[j])))
+            got = Fraction(float(rows[a, j]))
+            assert got == rational.fl16(rational.fl32(q * inv))
+            assert abs(got - q / Fraction(float(c_w[j]))) <= rational.ulp16(got) * (1 + Fraction(1, 1 << 20))
 
 
 # ---------------------------------------------------------------- layer bias

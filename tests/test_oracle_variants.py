@@ -158,7 +158,7 @@ def test_zeropoint_roundtrip_bound():
 
 def test_four_term_expansion_identity():
     """The pages' expansion ([DIGEST] "Quantization Primitives"; [PY]
-    "零点量化的思路"): (A + zp_a)(B + zp_b) = AB + A zp_b + zp_a B + zp_a zp_b,
+    "量化为什么会崩：一个尺度统治全局"): (A + zp_a)(B + zp_b) = AB + A zp_b + zp_a B + zp_a zp_b,
     summed over the non-outlier columns, evaluated term by term with Python
     integers, equals the oracle's product of the shifted codes."""
     inp = random_case(11, 5, 64, 9, 2, row_frac=0.6)
