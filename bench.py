@@ -211,11 +211,12 @@ def run_prefill(i8, torch, w, steps, warmup, dev):
     # without a resident fp16 W (outlier rows rebuilt from the int8 codes),
     # timed the same way as the step with W right beside it
     w8 = variant_ms(i8, torch, steps, X, Wq, c_w, W, w.alpha, ws, C)
+    quant = quantiser_variants(i8, torch, steps, X, W, w.alpha, w8["base"])
     # the step's intermediates again for anything that reads them later
     step()
     torch.cuda.synchronize()
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out,
-                inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies, w8=w8)
+                inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies, w8=w8, quant=quant)
 
 
 def run_decode(i8, torch, w, steps, warmup, dev):
@@ -245,7 +246,26 @@ def run_decode(i8, torch, w, steps, warmup, dev):
     n_out = int(v["n_out"].cpu()[0])
     weight_bytes = h * o + 2 * n_out * o + 4 * o
     w8 = variant_ms(i8, torch, steps, X, Wq, c_w, W, w.alpha, ws, C)
-    return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, w8=w8)
+    del Wq, c_w
+    quant = quantiser_variants(i8, torch, steps, X, W, w.alpha, w8["base"])
+    return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, w8=w8, quant=quant)
+
+
+def quantiser_variants(i8, torch, steps, X, W, alpha, fused_ms):
+    """Table 1's quantiser schemes on the same layer ([DIGEST] "Quantization
+    Primitives", "Vector-wise Quantization"): one forward of each, as the
+    sequence of C-ABI calls variant_forward makes (detection, the scheme's
+    row quantiser, its product; weights converted beforehand), average ms of
+    `steps` back-to-back forwards, with the one-call fused vector-wise
+    forward for reference."""
+    out = {}
+    for scheme in i8.SCHEMES:
+        qw = i8.quantize_weights(W, scheme)
+        out[scheme + "_ms"] = round(timed_ms(torch, steps, lambda: i8.variant_forward(X, qw, W, scheme, alpha)), 5)
+        del qw
+    out["vector_fused_forward_ms"] = round(fused_ms, 5)
+    out["zeropoint_vs_vector"] = round(out["zeropoint_ms"] / out["vector_ms"], 3)
+    return out
 
 
 def variant_ms(i8, torch, steps, X, Wq, c_w, W, alpha, ws, C):
@@ -437,6 +457,7 @@ def main(argv=None):
         "table5_comparison": pre["table5"],
         "without_fp16_weights": _w8_entry(pre["w8"], h, o),
         "with_bias": _bias_entry(pre["w8"]),
+        "quantiser_variants": pre["quant"],
         "weight_conversion": {"ms": round(pre["conv_ms"], 4),
                               "GB_per_s": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1)},
     }
@@ -457,6 +478,7 @@ def main(argv=None):
             "product_kernel_weight_GB_per_s": round(gbs_gemm, 1),
             "without_fp16_weights": _w8_entry(dec["w8"], wd.h, wd.o),
             "with_bias": _bias_entry(dec["w8"]),
+            "quantiser_variants": dec["quant"],
         }
 
     if not args.no_cpu_baseline:

@@ -155,8 +155,10 @@ i8mm_status i8mm_quantize_rowwise(const uint16_t* X, int64_t s, int64_t h,
  * idx, n_out: as from i8mm_detect_outlier_cols; Wq: panel layout (above);
  * c_w: [o] fp32; C: [s, o] fp16 (written).
  * W: [h, o] fp16, the original weights, or NULL when no fp16 copy of W is
- * kept: the outlier rows are then rebuilt from the int8 codes,
- * W[k, j] = fp16(W_i8[k, j] / c_w[j]) (one IEEE division, one rounding), so
+ * kept: the outlier rows are then rebuilt from the int8 codes by multiplying
+ * back with the inverse scale, W[k, j] = fl16(fl32(W_i8[k, j] * fl32(1 / c_w[j])))
+ * (IEEE round to nearest even at each step; [PY] "量化为什么会崩：一个尺度统治全局":
+ * dequantisation multiplies by 1/s), so
  * only Wq and c_w stay resident: about half the weight memory, the saving
  * the pages measure on BLOOM-176B ([DIGEST] "Executive Summary"; [PY]
  * "第二件武器：混合精度分解"); the outlier product then sees the 8-bit weights.
@@ -248,7 +250,7 @@ i8mm_status i8mm_quantize_weights_tensorwise(const uint16_t* W, int64_t h, int64
 /*
  * Zeropoint quantisation of each row of X over the columns not in O
  * ([DIGEST] "Quantization Primitives", zeropoint: nd = 2 * 127 / (max - min)
- * and a zero point; [PY] the zero-point passage). With min and max over the
+ * and a zero point; [PY] "量化为什么会崩：一个尺度统治全局"). With min and max over the
  * row's non-outlier values:
  *   nd = fl32(254 / fl32(max - min))   (1 when max == min),
  *   zp = round(fl32(nd * min)) + 127   (the pages print the zero point as a

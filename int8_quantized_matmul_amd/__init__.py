@@ -196,7 +196,7 @@ def int8_mixed_matmul(Xq: torch.Tensor, c_x: torch.Tensor, X_O: torch.Tensor, id
                       C: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C fp16 [s, o] = fp16(C_i32 / (c_x ⊗ c_w) + X_O W[idx, :] [+ bias]). With W
     None no fp16 copy of the weights is needed: W[idx, :] is rebuilt as
-    fp16(W_i8 / c_w). bias: fp16 [o] or None."""
+    fp16(W_i8 * fl32(1 / c_w)). bias: fp16 [o] or None."""
     s, h = Xq.shape
     o = Wq.shape[1]
     if C is None:

@@ -119,10 +119,12 @@ __device__ __forceinline__ void stage_outlier_slice(int kb, int n, int wid, int 
 }
 
 // An outlier row's weight W[k, j] when no fp16 copy of W is resident: the
-// int8 code of the panel layout times the column's reciprocal scale
-// inv_cw = 1 / c_w[j] (to 1 ulp), rounded once to fp16 - within one fp16
-// ulp of the rounded quotient code / c_w, and exact whenever the
-// quantisation of the column was (power-of-two c_w, codes reproducing W).
+// int8 code of the panel layout dequantised by multiplying back with the
+// column's inverse scale, fl16(fl32(q * inv_cw)), inv_cw = fl32(1 / c_w[j])
+// (correctly rounded: see inverse_scale). Exact whenever the quantisation of
+// the column was (power-of-two c_w, codes reproducing W).
+__device__ __forceinline__ float inverse_scale(float c) { return __fdiv_rn(1.0f, c); }
+
 __device__ __forceinline__ uint16_t dequantized_weight(const int8_t* __restrict__ Wq, float inv_cw, int64_t k,
                                                        int64_t j, int64_t o) {
     const int q = Wq[(k >> 6) * o * 64 + j * 64 + (k & 63)];
@@ -139,7 +141,7 @@ __device__ __forceinline__ void stage_w8_slice(int kb, int n, int64_t o0, int64_
     const int t = threadIdx.x;
     const int64_t j = o0 + t;
     const bool col_ok = j < o;
-    const float inv_cw = __builtin_amdgcn_rcpf(col_ok ? c_w[j] : 1.0f);
+    const float inv_cw = inverse_scale(col_ok ? c_w[j] : 1.0f);
     const int sw = (t >> 3) & 1;
     // A rolled loop with 2-byte LDS writes keeps this small: it is inlined
     // into every output block of the epilogue's rounds path.
@@ -646,7 +648,7 @@ __device__ __forceinline__ void outlier_operands_16(int kb, int n, int lane, int
     const int64_t ocol = ocol0 + (lane & 15);
     const bool col_ok = ocol < o;
     // without a resident fp16 W the rows are rebuilt from the int8 codes
-    const float inv_cw = __builtin_amdgcn_rcpf(W == nullptr && col_ok ? c_w[ocol] : 1.0f);
+    const float inv_cw = inverse_scale(W == nullptr && col_ok ? c_w[ocol] : 1.0f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const bool ok = col_ok && kbase + e < n;

@@ -6,7 +6,7 @@
 // Absmax and Zeropoint Quantization" (nd = 2 * 127 / (max - min), a zero
 // point, the four-term product) and "Vector-wise Quantization" (Table 1's
 // zeropoint vector-wise row); [PY] "LLM.int8() 完全拆解" (pinghaoyang.com.cn),
-// the zero-point passage.
+// "量化为什么会崩：一个尺度统治全局" (the zero point and the four-term product).
 //
 // Each row of X (over the columns not in O) and each column of W gets
 //   nd = fl32(254 / fl32(max - min))   (1 when max == min),

@@ -346,3 +346,26 @@ def test_bias_alone_with_zero_weights(s):
     C = i8.forward(T(X), Wq, c_w, Wd, 6.0, bias=T(b))
     torch.cuda.synchronize()
     assert np.array_equal(H(C).view(np.uint16), np.broadcast_to(b, (s, o)).view(np.uint16))
+
+
+@pytest.mark.parametrize("s,h", [(12, 256), (40, 64), (70, 256)])
+def test_rebuilt_outlier_rows_bit_exact(s, h):
+    """Without a resident fp16 W, at alpha = 0 (every column in O, Xq = 0)
+    and with one-hot rows of X, row i of C is the rebuilt weight row of its
+    one column, fl16(fl32(q * fl32(1 / c_w))), which must match the
+    oracle's bit for bit (decode kernel; prefill single-pass and
+    multi-round outlier epilogues)."""
+    o = 320
+    rng = np.random.default_rng(s + h)
+    W = (rng.standard_normal((h, o)) * 0.02).astype(np.float16)
+    cols = rng.choice(h, size=s, replace=s > h)
+    X = np.zeros((s, h), np.float16)
+    X[np.arange(s), cols] = 1.0
+    Wd = T(W)
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    say(f"  launch: one-hot rows, rebuilt outlier rows s={s} h={h}")
+    C = i8.forward(T(X), Wq, c_w, None, 0.0)
+    torch.cuda.synchronize()
+    Wq_t, cw_r = oracle.quantize_colwise_weights(W)
+    ref = oracle.dequantized_outlier_rows(Wq_t, cw_r, cols)
+    assert np.array_equal(H(C).view(np.uint16), ref.view(np.uint16))
