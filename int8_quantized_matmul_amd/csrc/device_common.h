@@ -34,18 +34,29 @@ __device__ __forceinline__ float absmax_scale(float m) {
     return m > 0.0f ? __fdiv_rn(127.0f, m) : 1.0f;
 }
 
-// One fp32 multiply, then round half away from zero, clamped to [-127, 127].
-// Rounding: the float-to-int conversion truncates, and adding the largest
-// float below 1/2 with v's sign first pushes exactly the ties and everything
-// above them past the next integer (checked for every fp32 value of
-// magnitude at most 256). Clamping the sum to [-127.5, 127.5] before the
-// truncation equals clamping the rounded value to [-127, 127]. With
-// c = fl32(127 / m) and |x| <= m, |fl32(x c)| < 127.5, so the clamp never
-// changes a code; it only keeps the conversion in range for other inputs.
+// One fp32 multiply, then round half away from zero. v = fl32(x c) is
+// taken as an FMA with a -0 addend, which is the rounded product exactly
+// (also for a zero product, whose sign it keeps) and lets an fp16 x enter
+// the multiply without a separate conversion. Rounding: the float-to-int
+// conversion truncates, and adding the largest float below 1/2 with v's
+// sign first pushes exactly the ties and everything above them past the
+// next integer (checked for every fp32 value of magnitude at most 256).
+// Every caller scales by c = fl32(127 / m) with |x| <= m (m the absmax of
+// the values of its row, column or tensor), so |v| <= 127 and the code is
+// in [-127, 127] without a clamp.
 __device__ __forceinline__ int quantize_one(float x, float c) {
-    const float v = __fmul_rn(x, c);
+    const float v = __builtin_fmaf(x, c, -0.0f);
     const float t = __fadd_rn(v, copysignf(0.49999997f, v));
-    return static_cast<int>(__builtin_amdgcn_fmed3f(t, -127.5f, 127.5f));
+    return static_cast<int>(t);
+}
+
+// The low bytes of four ints packed into one word, b0 lowest.
+__device__ __forceinline__ uint32_t pack_bytes(int b0, int b1, int b2, int b3) {
+    // v_perm_b32 selector bytes 0-3 pick bytes of the second operand, 4-7
+    // bytes of the first, 0x0c a zero byte
+    const uint32_t lo = __builtin_amdgcn_perm(static_cast<uint32_t>(b1), static_cast<uint32_t>(b0), 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(static_cast<uint32_t>(b3), static_cast<uint32_t>(b2), 0x04000c0cu);
+    return lo | hi;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -60,15 +60,46 @@ __device__ __forceinline__ float absmax_value(uint32_t m2) {
     return half_bits_to_float(a > b ? a : b);
 }
 
-// The 8 quantised values of a chunk, packed bytewise.
+// fl32(x c) for the fp16 value x in the low (HI = false) or high half of
+// word w: v_fma_mix_f32 widens the half exactly and rounds x c + 0 once,
+// which is the rounded product except that a zero product comes out +0
+// (round_code maps both zeros to code 0), in one instruction.
+template <bool HI>
+__device__ __forceinline__ float mul_half(uint32_t w, float c) {
+    float r;
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(c));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(c));
+    return r;
+}
+
+// round half away from zero of v = fl32(x c), as in quantize_one
+__device__ __forceinline__ int round_code(float v) {
+    return static_cast<int>(__fadd_rn(v, copysignf(0.49999997f, v)));
+}
+
+// The 8 quantised values of a chunk (quantize_one of each), packed bytewise.
 __device__ __forceinline__ uint2 chunk_quantize(const uint4& v, float sc) {
-    uint32_t packed[2] = {0u, 0u};
+    int q[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int q = quantize_one(half_bits_to_float((word_of(v, e >> 1) >> ((e & 1) * 16)) & 0xffffu), sc);
-        packed[e >> 2] |= (static_cast<uint32_t>(q) & 0xffu) << ((e & 3) * 8);
+    for (int k = 0; k < 4; ++k) {
+        q[2 * k] = round_code(mul_half<false>(word_of(v, k), sc));
+        q[2 * k + 1] = round_code(mul_half<true>(word_of(v, k), sc));
     }
-    return make_uint2(packed[0], packed[1]);
+    return make_uint2(pack_bytes(q[0], q[1], q[2], q[3]), pack_bytes(q[4], q[5], q[6], q[7]));
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero, so a ragged or absent row needs no branch around its loads (and
+// waits on later loads stay countable).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint4 load_chunk_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
 __device__ __forceinline__ uint4 load_chunk(const uint16_t* p) {

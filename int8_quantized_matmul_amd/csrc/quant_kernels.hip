@@ -158,57 +158,76 @@ __global__ __launch_bounds__(1024) void k_compact(const uint32_t* __restrict__ m
 // Dynamic LDS: nw mask words + nw prefix counts.
 enum class RowScale { Absmax, MaxOnly, Given };
 
-template <int CPL, RowScale SC = RowScale::Absmax>
+// WPR wavefronts share a row (4 / WPR rows per block; wavefront part q of a
+// row owns its chunks 64 (WPR p + q) + lane) and meet in LDS for the row
+// maximum, so that few rows still give the GPU enough wavefronts; WPR > 1
+// only with the row's own absmax and the row held in registers.
+template <int CPL, RowScale SC = RowScale::Absmax, int WPR = 1>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ X, int64_t s, int64_t h,
                                                     const uint32_t* __restrict__ src_mask,
                                                     uint32_t* __restrict__ mask_out, int32_t* __restrict__ idx,
                                                     int32_t* __restrict__ n_out,
                                                     int8_t* __restrict__ Xq, float* __restrict__ c_x,
                                                     uint16_t* __restrict__ X_O, int64_t ldo) {
+    static_assert(WPR == 1 || (SC == RowScale::Absmax && CPL > 0), "row split needs the row in registers");
     extern __shared__ uint32_t dyn[];
     __shared__ int wsum[4];
+    __shared__ uint32_t part_max[4];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int part = wid % WPR;
     const int nw = static_cast<int>(h / 32);
     uint32_t* smask = dyn;
     int* pre = reinterpret_cast<int*>(dyn + nw);
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + wid;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * (4 / WPR) + wid / WPR;
     const bool live = i < s;
     const uint16_t* xr = X + (live ? i : 0) * h;
     const int64_t nch = h / 8;
+    auto chunk_of = [&](int p) -> int64_t { return 64 * (WPR * p + part) + lane; };
 
+    // The mask words are loaded before the row, so that the prefix counts
+    // below wait only for them (vector-memory waits are in issue order) and
+    // run while the row is still in flight.
+    uint32_t mw = 0u;
+    if (t < nw) mw = src_mask[t];
     uint4 cache[CPL > 0 ? CPL : 1];
     if constexpr (CPL > 0) {
+        // chunks past the row, and every chunk of a row past s, read zero
+        const __amdgpu_buffer_rsrc_t rrow = range_rsrc(xr, live ? static_cast<uint32_t>(2 * h) : 0u);
 #pragma unroll
-        for (int p = 0; p < CPL; ++p) {
-            const int64_t c = lane + 64 * p;
-            if (live && c < nch) cache[p] = load_chunk(xr + c * 8);
-        }
+        for (int p = 0; p < CPL; ++p) cache[p] = load_chunk_rsrc(rrow, static_cast<uint32_t>(chunk_of(p) * 16));
     }
-    for (int w = t; w < nw; w += 256) smask[w] = src_mask[w];
+    if (t < nw) smask[t] = mw;
+    for (int w = t + 256; w < nw; w += 256) smask[w] = src_mask[w];   // h > 8192
     __syncthreads();
     const int n = block_mask_prefix(smask, pre, nw, wsum, 256);
     if (blockIdx.x == 0 && idx != nullptr) emit_outlier_set(smask, pre, nw, n, mask_out, idx, n_out, 256);
-    if (!live) return;
+    if constexpr (WPR == 1) {
+        if (!live) return;
+    }
 
     uint16_t* orow = X_O + i * ldo;
     auto bits_of = [&](int64_t c) { return (smask[c >> 2] >> ((c & 3) * 8)) & 0xffu; };
-    // Outlier values to X_O; the chunk comes back with them cleared.
+    // Outlier values to X_O; the chunk comes back with them cleared. The
+    // chunk's first outlier column takes rank pre[word] plus the set bits
+    // below it in its word, the next ones follow in order; the loop runs
+    // once per outlier column in the chunk (usually none).
     auto split = [&](const uint4& v, int64_t c) {
         const uint32_t bits = bits_of(c);
-        if (!bits) return v;
+        if (!bits || !live) return v;   // a row past s holds zeros (WPR > 1 only)
         if constexpr (SC == RowScale::MaxOnly) return chunk_clear(v, bits);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if ((bits >> e) & 1u)
-                orow[outlier_rank(smask, pre, static_cast<int>(c * 8 + e))] =
-                    static_cast<uint16_t>(word_of(v, e >> 1) >> ((e & 1) * 16));
+        const int w = static_cast<int>(c >> 2), sh = static_cast<int>(c & 3) * 8;
+        int rank = pre[w] + __popc(smask[w] & ((1u << sh) - 1u));
+        for (uint32_t b = bits; b; b &= b - 1u) {
+            const int e = __ffs(b) - 1;
+            orow[rank++] = static_cast<uint16_t>(word_of(v, e >> 1) >> ((e & 1) * 16));
+        }
         return chunk_clear(v, bits);
     };
     uint32_t m2 = 0;
     if constexpr (CPL > 0) {
 #pragma unroll
         for (int p = 0; p < CPL; ++p) {
-            const int64_t c = lane + 64 * p;
+            const int64_t c = chunk_of(p);
             if (c < nch) {
                 cache[p] = split(cache[p], c);
                 m2 = chunk_absmax_fold(cache[p], m2);
@@ -219,6 +238,13 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m2 = pk_max_u16(m2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2), off, kWave)));
+    if constexpr (WPR > 1) {
+        if (lane == 0) part_max[wid] = m2;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < WPR; ++q) m2 = pk_max_u16(m2, part_max[wid - part + q]);
+        if (!live) return;
+    }
     if constexpr (SC == RowScale::MaxOnly) {
         if (lane == 0) c_x[i] = absmax_value(m2);
         return;
@@ -228,14 +254,14 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
         sc = c_x[i];
     } else {
         sc = absmax_scale(absmax_value(m2));
-        if (lane == 0) c_x[i] = sc;
+        if (lane == 0 && part == 0) c_x[i] = sc;
     }
 
     int8_t* qr = Xq + i * h;
     if constexpr (CPL > 0) {
 #pragma unroll
         for (int p = 0; p < CPL; ++p) {
-            const int64_t c = lane + 64 * p;
+            const int64_t c = chunk_of(p);
             if (c < nch) *reinterpret_cast<uint2*>(qr + c * 8) = chunk_quantize(cache[p], sc);
         }
     } else {
@@ -244,7 +270,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
                 chunk_quantize(chunk_clear(load_chunk(xr + c * 8), bits_of(c)), sc);
     }
     const int npad = (n + 31) & ~31;
-    for (int k = n + lane; k < npad; k += 64) orow[k] = 0;
+    if (part == 0)
+        for (int k = n + lane; k < npad; k += 64) orow[k] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -532,18 +559,34 @@ hipError_t launch_detect_into(const uint16_t* X, int64_t s, int64_t h, float alp
 hipError_t launch_rows(const uint16_t* X, int64_t s, int64_t h, const uint32_t* src_mask, uint32_t* mask_out,
                        int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
                        hipStream_t stream) {
-    const int64_t per_lane = (h / 8 + 63) / 64;
-    const dim3 grid(static_cast<unsigned>((s + 3) / 4)), block(256);
+    // Wavefronts per row: enough for ~4096 wavefronts in all (4 per SIMD),
+    // as long as each still holds its part of the row in registers.
+    const int64_t nch = h / 8;
+    int wpr = s >= 4096 ? 1 : s >= 2048 ? 2 : 4;
+    while (wpr > 1 && (nch + 64 * wpr - 1) / (64 * wpr) > 16) wpr = wpr == 4 ? 1 : 4;
+    const int64_t per_lane = (nch + 64 * wpr - 1) / (64 * wpr);
+    const dim3 grid(static_cast<unsigned>((s + 4 / wpr - 1) / (4 / wpr))), block(256);
     const size_t dyn = static_cast<size_t>(2 * (h / 32) * 4);
-#define I8MM_QROWS(CPL)                                                                                     \
-    hipLaunchKernelGGL(k_quant_rows<CPL>, grid, block, dyn, stream, X, s, h, src_mask, mask_out, idx, n_out, \
-                       Xq, c_x, X_O, ldo)
-    if (per_lane <= 2) I8MM_QROWS(2);
-    else if (per_lane <= 4) I8MM_QROWS(4);
-    else if (per_lane <= 8) I8MM_QROWS(8);
-    else if (per_lane <= 16) I8MM_QROWS(16);
-    else if (per_lane <= 32) I8MM_QROWS(32);
-    else I8MM_QROWS(0);
+#define I8MM_QROWS(CPL, W)                                                                                     \
+    hipLaunchKernelGGL((k_quant_rows<CPL, RowScale::Absmax, W>), grid, block, dyn, stream, X, s, h, src_mask,   \
+                       mask_out, idx, n_out, Xq, c_x, X_O, ldo)
+#define I8MM_QROWS_W(W)                                  \
+    if (per_lane <= 2) I8MM_QROWS(2, W);                 \
+    else if (per_lane <= 4) I8MM_QROWS(4, W);            \
+    else if (per_lane <= 8) I8MM_QROWS(8, W);            \
+    else I8MM_QROWS(16, W);
+    if (wpr == 4) {
+        I8MM_QROWS_W(4)
+    } else if (wpr == 2) {
+        I8MM_QROWS_W(2)
+    } else if (per_lane <= 16) {
+        I8MM_QROWS_W(1)
+    } else if (per_lane <= 32) {
+        I8MM_QROWS(32, 1);
+    } else {
+        I8MM_QROWS(0, 1);
+    }
+#undef I8MM_QROWS_W
 #undef I8MM_QROWS
     return hipGetLastError();
 }
