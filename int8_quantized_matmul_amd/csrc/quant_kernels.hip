@@ -294,11 +294,14 @@ __global__ __launch_bounds__(256) void k_small_detect(const uint16_t* __restrict
     const int64_t col = static_cast<int64_t>(blockIdx.x) * kSlabCols + c * 8;
     const bool cok = col < h;
     if (t < kSlabCols / 32) smask[t] = 0u;
+    // rows past s fall past the resource and read zero; columns past h are
+    // sent out of range
+    const __amdgpu_buffer_rsrc_t rX = range_rsrc(X, static_cast<uint32_t>(2 * static_cast<int64_t>(s) * h));
     uint4 v[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g)
-        v[g] = cok && r + 16 * g < s ? load_chunk(X + static_cast<int64_t>(r + 16 * g) * h + col)
-                                     : make_uint4(0, 0, 0, 0);
+        v[g] = load_chunk_rsrc(rX, cok ? static_cast<uint32_t>(2 * (static_cast<int64_t>(r + 16 * g) * h + col))
+                                       : 0x80000000u);
     uint4 d = detect_init();
 #pragma unroll
     for (int g = 0; g < RG; ++g)
@@ -332,23 +335,36 @@ __global__ __launch_bounds__(256) void k_small_quant(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ X_O, int64_t ldo) {
     __shared__ int part[2][4];
     __shared__ float rscale[16 * RG];
+    __shared__ uint32_t slab[kSlabCols / 32];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6, c = t & 15, r = t >> 4;
     const int nw = h / 32;
     const int w0 = static_cast<int>(blockIdx.x) * (kSlabCols / 32);
     const int64_t col = static_cast<int64_t>(blockIdx.x) * kSlabCols + c * 8;
     const bool cok = col < h;
+    // The mask words (the first 512 into registers) and row maxima are
+    // loaded before the rows, so that waiting for them does not wait for
+    // the rows (vector-memory waits are in issue order).
+    const uint32_t mwa = t < nw ? mask[t] : 0u;
+    const uint32_t mwb = t + 256 < nw ? mask[t + 256] : 0u;
+    const uint32_t rm = t < s ? rowmax[t] : 0u;
+    const __amdgpu_buffer_rsrc_t rX = range_rsrc(X, static_cast<uint32_t>(2 * static_cast<int64_t>(s) * h));
     uint4 v[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g)
-        v[g] = cok && r + 16 * g < s ? load_chunk(X + static_cast<int64_t>(r + 16 * g) * h + col)
-                                     : make_uint4(0, 0, 0, 0);
-    // Outlier columns before this slab and in total.
+        v[g] = load_chunk_rsrc(rX, cok ? static_cast<uint32_t>(2 * (static_cast<int64_t>(r + 16 * g) * h + col))
+                                       : 0x80000000u);
+    // Outlier columns before this slab and in total; this slab's own words
+    // go to LDS for the ranks below.
     int before = 0, total = 0;
-    for (int w = t; w < nw; w += 256) {
-        const int p = __popc(mask[w]);
+    auto count = [&](int w, uint32_t word) {
+        const int p = __popc(word);
         total += p;
         before += w < w0 ? p : 0;
-    }
+        if (w >= w0 && w < w0 + kSlabCols / 32) slab[w - w0] = word;
+    };
+    if (t < nw) count(t, mwa);
+    if (t + 256 < nw) count(t + 256, mwb);
+    for (int w = t + 512; w < nw; w += 256) count(w, mask[w]);   // h > 16384
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         before += __shfl_xor(before, off, kWave);
@@ -358,7 +374,7 @@ __global__ __launch_bounds__(256) void k_small_quant(const uint16_t* __restrict_
         part[0][wid] = before;
         part[1][wid] = total;
     }
-    if (t < s) rscale[t] = absmax_scale(__uint_as_float(rowmax[t]));
+    if (t < s) rscale[t] = absmax_scale(__uint_as_float(rm));
     __syncthreads();
     before = part[0][0] + part[0][1] + part[0][2] + part[0][3];
     total = part[1][0] + part[1][1] + part[1][2] + part[1][3];
@@ -369,7 +385,7 @@ __global__ __launch_bounds__(256) void k_small_quant(const uint16_t* __restrict_
     int rank = before;
     uint32_t word = 0u;
     for (int j = 0; j <= q; ++j) {
-        word = w0 + j < nw ? mask[w0 + j] : 0u;
+        word = w0 + j < nw ? slab[j] : 0u;
         if (j < q) rank += __popc(word);
     }
     rank += __popc(word & ((1u << ((c & 3) * 8)) - 1u));
