@@ -58,21 +58,26 @@ def product_kernel_ms(i8, torch, n, launch):
     return e0.elapsed_time(e1) / n
 
 
-def settle(torch, fn, ms=25.0, max_calls=2000):
-    """Untimed back-to-back calls of fn until about `ms` of GPU time has
-    passed. After an idle spell the GPU's clocks take ~10 ms of continuous
-    work to come back up (steps run ~10 % slower meanwhile), so this runs
-    before the warm-up steps and the timed region measures steady state."""
-    torch.cuda.synchronize()
-    e0, e1 = _events(torch)
-    e0.record()
-    fn()
-    e1.record()
-    torch.cuda.synchronize()
-    one = max(e0.elapsed_time(e1), 1e-3)
-    for _ in range(min(max_calls, int(ms / one))):
-        fn()
-    torch.cuda.synchronize()
+def settle(torch, fn, window=20, tol=0.01, max_ms=300.0):
+    """Untimed back-to-back calls of fn until the GPU runs them at a steady
+    rate: windows of `window` calls are timed until two in a row agree
+    within `tol` (at most ~max_ms of GPU time). After an idle spell the
+    GPU's clocks take a while to come back up (the first ~10 ms of steps
+    run ~10 % slower), so this runs before the warm-up steps and the timed
+    region measures steady state."""
+    prev, spent = None, 0.0
+    while spent < max_ms:
+        e0, e1 = _events(torch)
+        e0.record()
+        for _ in range(window):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        spent += t
+        if prev is not None and abs(t - prev) <= tol * prev:
+            break
+        prev = t
 
 
 def timed_ms(torch, n, fn, warmup=3):

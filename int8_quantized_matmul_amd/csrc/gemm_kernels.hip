@@ -153,18 +153,20 @@ __device__ __forceinline__ void stage_w8_slice(int kb, int n, int64_t o0, int64_
     }
 }
 
-// f += X_O[., slice] W[slice, .] for the 32 x 32 block (sb, ob) of a
-// wave's 128 x 128 output, operands from a staged slice
-// (v_mfma_f32_32x32x16_f16; the lane holds k = 8 (lane / 32) + e of the
-// slice for its column / row).
-__device__ __forceinline__ v16f apply_outlier_slice(const uint16_t* sl, int wo, int ws, int sb, int ob, int r32,
-                                                    int khalf, v16f f) {
-    const v8h xb = *reinterpret_cast<const v8h*>(sl + kSlice + (ws * 128 + sb * 32 + r32) * 16 + 8 * khalf);
-    v8h wa;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        wa[e] = __builtin_bit_cast(_Float16, sl[(8 * khalf + e) * 256 + wo * 128 + ob * 32 + r32]);
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb, f, 0, 0, 0);
+// f + wa xb with v_mfma_f32_32x32x16_f16 in its VGPR form. The epilogue's
+// dequantised values live in VGPRs while the accumulators of the main loop
+// fill the AGPRs; left to the compiler, this MFMA takes its C operand and
+// result in AGPRs and every block's values make a round trip (and the
+// register shuffles cost ~5 % of the kernel). Written as asm, the wait
+// states the hardware needs around a VGPR-form MFMA are explicit: 2 after
+// VALU writes of its operands, and more than the 18 a 16-pass result needs
+// before anything reads (or overwrites) its registers.
+__device__ __forceinline__ v16f mfma_f16_vgpr(const v8h& wa, const v8h& xb, const v16f& f) {
+    v16f r;
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "=v"(r)
+                 : "v"(wa), "v"(xb), "v"(f));
+    return r;
 }
 
 // In-place transpose of the W part of a staged slice, [16 k][256 columns]
@@ -186,13 +188,46 @@ __device__ __forceinline__ void transpose_w_slice(uint16_t* sl) {
     __syncthreads();
 }
 
-// apply_outlier_slice on a transposed slice: both operands are one 16-byte read.
+// f += X_O[., slice] W[slice, .] for the 32 x 32 block (sb, ob) of a
+// wave's 128 x 128 output, operands from a staged slice whose W part is
+// transposed (both operands one 16-byte read; the lane holds k = 8
+// (lane / 32) + e of the slice for its column / row).
 __device__ __forceinline__ v16f apply_outlier_slice_t(const uint16_t* sl, int wo, int ws, int sb, int ob, int r32,
                                                       int khalf, v16f f) {
     const v8h xb = *reinterpret_cast<const v8h*>(sl + kSlice + (ws * 128 + sb * 32 + r32) * 16 + 8 * khalf);
     const int col = wo * 128 + ob * 32 + r32;
     const v8h wa = *reinterpret_cast<const v8h*>(sl + (col * 2 + (khalf ^ ((col >> 3) & 1))) * 8);
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(wa, xb, f, 0, 0, 0);
+    return mfma_f16_vgpr(wa, xb, f);
+}
+
+// The same for slice q with both operands read from global memory: the
+// slices past the ones staged in LDS (more than 96 outlier columns, far
+// beyond the handful the method meets), without staging or barriers.
+__device__ __forceinline__ v16f apply_outlier_slice_global(int q, int n, int64_t o0, int64_t s0, int64_t s, int64_t o,
+                                                           const uint16_t* __restrict__ X_O, int64_t ldo,
+                                                           const int32_t* __restrict__ idx,
+                                                           const uint16_t* __restrict__ W, const int8_t* __restrict__ Wq,
+                                                           const float* __restrict__ c_w, int wo, int ws, int sb, int ob,
+                                                           int r32, int khalf, v16f f) {
+    const int64_t col = o0 + wo * 128 + ob * 32 + r32;
+    const int64_t row = s0 + ws * 128 + sb * 32 + r32;
+    const int k0 = q * 16 + 8 * khalf;
+    const bool col_ok = col < o;
+    const float inv_cw = inverse_scale(W == nullptr && col_ok ? c_w[col] : 1.0f);
+    v8h wa;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int k = k0 + e;
+        const bool ok = col_ok && k < n;
+        const int64_t rk = ok ? idx[k] : 0;
+        uint16_t bits = 0;
+        if (ok) bits = W != nullptr ? W[rk * o + col] : dequantized_weight(Wq, inv_cw, rk, col, o);
+        wa[e] = __builtin_bit_cast(_Float16, bits);
+    }
+    // columns of X_O up to round_up(|O|, 32) hold the outliers and zeros
+    v8h xb = {};
+    if (row < s) xb = *reinterpret_cast<const v8h*>(X_O + row * ldo + k0);
+    return mfma_f16_vgpr(wa, xb, f);
 }
 
 // LDS staging of the fp16 output: each wavefront owns 32 rows x 128
@@ -484,14 +519,15 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             const uint32_t col = static_cast<uint32_t>(o0 + wo * 128 + lane + 64 * i);
             bias_bits[i] = __builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(rBias, 2 * col, 0, 0));
         }
+        // The first nst = min(nsl, 1 + kMaxOnceSlices) slices are staged in
+        // LDS (slice 0 in olds, before the K loop); any further ones are
+        // read from global memory block by block.
         const int nsl = (n_o + 15) / 16;
-        const bool once = nsl <= 1 + kMaxOnceSlices;
-        if (once) {
-            for (int q = 1; q < nsl; ++q)
-                stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q), !w8);
-            if (w8)
-                for (int q = 0; q < nsl; ++q) stage_w8_slice(q, n_o, o0, o, idx, Wq, c_w, q ? slice_at(q) : olds);
-        }
+        const int nst = nsl < 1 + kMaxOnceSlices ? nsl : 1 + kMaxOnceSlices;
+        for (int q = 1; q < nst; ++q)
+            stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q), !w8);
+        if (w8)
+            for (int q = 0; q < nst; ++q) stage_w8_slice(q, n_o, o0, o, idx, Wq, c_w, q ? slice_at(q) : olds);
         // 1 / c_w of the wave's 128 columns (reciprocals to 1 ulp)
 #pragma unroll
         for (int i = 0; i < 2; ++i) invw[lane + 64 * i] = __builtin_amdgcn_rcpf(cw_pf[i]);
@@ -517,10 +553,10 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (once && !w8) {
+        if (!w8) {
             // W parts transposed once, so that both MFMA operands are 16-byte reads
-            if (nsl > 0) transpose_w_slice(olds);
-            for (int q = 1; q < nsl; ++q) transpose_w_slice(slice_at(q));
+            if (nst > 0) transpose_w_slice(olds);
+            for (int q = 1; q < nst; ++q) transpose_w_slice(slice_at(q));
         }
         // One 32-row block at a time: a lane then holds 4-column runs of one
         // row across all 128 columns of the wave.
@@ -537,7 +573,6 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     zr = static_cast<double>(static_cast<int64_t>(zp.rowsum_x[srow]) + (h - n_o) * static_cast<int64_t>(z));
                 }
             }
-            if (!once) __syncthreads();   // the previous row block's rounds are done
 #pragma unroll
             for (int ob = 0; ob < 4; ++ob) {
                 // Dequantise: f = C_i32 * (1/c_x) * (1/c_w); zeropoint:
@@ -567,29 +602,11 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     }
                 }
                 // Outlier product X_O W[idx, :] on top (fp32 accumulate).
-                if (once) {
-                    if (nsl > 0) f = apply_outlier_slice_t(olds, wo, ws, sb, ob, r32, khalf, f);
-                    for (int q = 1; q < nsl; ++q) f = apply_outlier_slice_t(slice_at(q), wo, ws, sb, ob, r32, khalf, f);
-                } else {
-                    // more than 96 outlier columns: slices in rounds (slice 0
-                    // from olds when the fp16 rows were staged there; rebuilt
-                    // rows arrive already transposed)
-                    if (!w8) f = apply_outlier_slice(olds, wo, ws, sb, ob, r32, khalf, f);
-                    for (int rb = w8 ? 0 : 1; rb < nsl; rb += kMaxOnceSlices) {
-                        const int re = rb + kMaxOnceSlices < nsl ? rb + kMaxOnceSlices : nsl;
-                        __syncthreads();
-                        for (int q = rb; q < re; ++q) {
-                            stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q - rb + 1),
-                                                !w8);
-                            if (w8) stage_w8_slice(q, n_o, o0, o, idx, Wq, c_w, slice_at(q - rb + 1));
-                        }
-                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                        __syncthreads();
-                        for (int q = rb; q < re; ++q)
-                            f = w8 ? apply_outlier_slice_t(slice_at(q - rb + 1), wo, ws, sb, ob, r32, khalf, f)
-                                   : apply_outlier_slice(slice_at(q - rb + 1), wo, ws, sb, ob, r32, khalf, f);
-                    }
-                }
+                if (nst > 0) f = apply_outlier_slice_t(olds, wo, ws, sb, ob, r32, khalf, f);
+                for (int q = 1; q < nst; ++q) f = apply_outlier_slice_t(slice_at(q), wo, ws, sb, ob, r32, khalf, f);
+                for (int q = nst; q < nsl; ++q)
+                    f = apply_outlier_slice_global(q, n_o, o0, s0, s, o, X_O, ldo, idx, W, Wq, c_w, wo, ws, sb, ob, r32,
+                                                   khalf, f);
                 // The layer bias, in the same fp32 sum before the rounding.
                 if (has_bias) {
 #pragma unroll
