@@ -29,6 +29,16 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
+// Two fp32 values rounded to fp16 (to nearest even) and packed, lo in the
+// low half, by one v_cvt_pk_f16_f32 (checked bit-equal to converting each
+// value on its own, for every fp32 input). Being asm it also pins both
+// values as fp32, like float_to_half_bits.
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+    uint32_t r;
+    asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+    return r;
+}
+
 // fl32(127 / m) with an IEEE correctly rounded division; 1 when m == 0.
 __device__ __forceinline__ float absmax_scale(float m) {
     return m > 0.0f ? __fdiv_rn(127.0f, m) : 1.0f;

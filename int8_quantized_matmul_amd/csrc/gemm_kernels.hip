@@ -453,10 +453,8 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const v16f& f = acc[ob][sb];
-                    const uint32_t lo = float_to_half_bits(f[4 * g]) |
-                                        (static_cast<uint32_t>(float_to_half_bits(f[4 * g + 1])) << 16);
-                    const uint32_t hi = float_to_half_bits(f[4 * g + 2]) |
-                                        (static_cast<uint32_t>(float_to_half_bits(f[4 * g + 3])) << 16);
+                    const uint32_t lo = pack_half2(f[4 * g], f[4 * g + 1]);
+                    const uint32_t hi = pack_half2(f[4 * g + 2], f[4 * g + 3]);
                     *reinterpret_cast<uint2*>(out_st + r32 * kOutRow + ob * 32 + 8 * g + 4 * khalf) =
                         make_uint2(lo, hi);
                 }
@@ -621,10 +619,8 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                 // own reads below see these writes).
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const uint32_t lo = float_to_half_bits(f[4 * g]) |
-                                        (static_cast<uint32_t>(float_to_half_bits(f[4 * g + 1])) << 16);
-                    const uint32_t hi = float_to_half_bits(f[4 * g + 2]) |
-                                        (static_cast<uint32_t>(float_to_half_bits(f[4 * g + 3])) << 16);
+                    const uint32_t lo = pack_half2(f[4 * g], f[4 * g + 1]);
+                    const uint32_t hi = pack_half2(f[4 * g + 2], f[4 * g + 3]);
                     *reinterpret_cast<uint2*>(out_st + r32 * kOutRow + ob * 32 + 8 * g + 4 * khalf) =
                         make_uint2(lo, hi);
                 }
@@ -839,8 +835,8 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
             f[3] += half_bits_to_float(bias4.y >> 16);
         }
         if (srow < s) {
-            const uint32_t lo = float_to_half_bits(f[0]) | (static_cast<uint32_t>(float_to_half_bits(f[1])) << 16);
-            const uint32_t hi = float_to_half_bits(f[2]) | (static_cast<uint32_t>(float_to_half_bits(f[3])) << 16);
+            const uint32_t lo = pack_half2(f[0], f[1]);
+            const uint32_t hi = pack_half2(f[2], f[3]);
             *reinterpret_cast<uint2*>(C + srow * o + ocol) = make_uint2(lo, hi);
         }
     }
