@@ -161,12 +161,13 @@ __device__ __forceinline__ void stage_w8_slice(int kb, int n, int64_t o0, int64_
 // states the hardware needs around a VGPR-form MFMA are explicit: 2 after
 // VALU writes of its operands, and more than the 18 a 16-pass result needs
 // before anything reads (or overwrites) its registers.
-__device__ __forceinline__ v16f mfma_f16_vgpr(const v8h& wa, const v8h& xb, const v16f& f) {
-    v16f r;
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "=v"(r)
-                 : "v"(wa), "v"(xb), "v"(f));
-    return r;
+// The accumulator is one tied operand: a result that only partly overlaps
+// the C operand is not a valid encoding.
+__device__ __forceinline__ v16f mfma_f16_vgpr(const v8h& wa, const v8h& xb, v16f f) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(f)
+                 : "v"(wa), "v"(xb));
+    return f;
 }
 
 // In-place transpose of the W part of a staged slice, [16 k][256 columns]
@@ -257,6 +258,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     uint32_t* __restrict__ clear, int clear_words, ZpArgs zp) {
     __shared__ v4i A0[kBuf], A1[kBuf], B0[kBuf], B1[kBuf];
     __shared__ __attribute__((aligned(16))) uint16_t olds[2 * kSlice];
+    __shared__ __attribute__((aligned(16))) float scl[512];   // c_x of the tile's rows, then c_w of its columns
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
 
@@ -307,9 +309,6 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         }
     };
 
-    // The first slice of the outlier operands goes to its own LDS region,
-    // and the scales of this wavefront's rows and columns to registers: the
-    // loads complete under the main loop.
     int n_o = 0;
     constexpr bool zpm = MODE == GemmOut::ZeroPoint;
     constexpr bool mixed = MODE == GemmOut::Mixed || zpm;   // fused fp16 epilogue with outliers
@@ -317,24 +316,10 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                                                 mixed && W ? static_cast<uint32_t>((h * o - o0) * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(mixed ? X_O + s0 * ldo : nullptr,
                                                 mixed ? static_cast<uint32_t>(s_rows * ldo * 2) : 0u);
-    float cx_pf[4], cw_pf[2];
     // Without a resident fp16 W (W null) the outlier rows are rebuilt from
     // the int8 codes in the epilogue; only their X part is staged here.
     const bool w8 = W == nullptr;
-    if constexpr (mixed) {
-        n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
-        if (n_o > 0) stage_outlier_slice(0, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, olds, !w8);
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            const int64_t srow = s0 + ws * 128 + sb * 32 + r32;
-            cx_pf[sb] = srow < s ? c_x[srow] : 1.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t col = o0 + wo * 128 + lane + 64 * i;
-            cw_pf[i] = col < o ? c_w[col] : 1.0f;
-        }
-    }
+    if constexpr (mixed) n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
 
     constexpr bool dense16 = MODE == GemmOut::Fp16Dense;
     using Acc = std::conditional_t<dense16, v16f, v16i>;
@@ -428,6 +413,20 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 
     load_part(0, A0, B0, 0, 8);
     load_part(1, A1, B1, 0, 3);
+    // Behind the first operand loads: the first slice of the outlier
+    // operands to its own LDS region, and the row and column scales of the
+    // tile to LDS (direct-to-LDS, one dword per lane; entries past s or o
+    // read zero and are never used). Nothing of this is held in registers
+    // across the main loop.
+    if constexpr (mixed) {
+        if (n_o > 0) stage_outlier_slice(0, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, olds, !w8);
+        const __amdgpu_buffer_rsrc_t rcx = make_rsrc(c_x + s0, static_cast<uint32_t>(s_rows * 4));
+        const __amdgpu_buffer_rsrc_t rcw = make_rsrc(c_w + o0, static_cast<uint32_t>(o_rows * 4));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rcx, LDS_PTR(scl + 64 * wu), 4, static_cast<uint32_t>(4 * (64 * wu + lane)),
+                                                 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rcw, LDS_PTR(scl + 256 + 64 * wu), 4,
+                                                 static_cast<uint32_t>(4 * (64 * wu + lane)), 0, 0, 0);
+    }
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
     frags(A0, B0, 0, fa[0], fb[0]);
@@ -498,7 +497,9 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             return base + (q <= 4 ? ((q - 1) & 1) * 2 * kSlice : 0);
         };
         uint16_t* out_st = wid < 3 ? reinterpret_cast<uint16_t*>(A1) + wid * kOutWave : reinterpret_cast<uint16_t*>(B1);
-        float* invw = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(B1) + kOutWave) + wid * 128;
+        // 1 / c_x and 1 / c_w of the tile (reciprocals to 1 ulp), in place
+        float* inv_rows = scl + ws * 128;
+        float* invw = scl + 256 + wo * 128;
         // after the staging of waves 0-2 in A1: bias, then (zeropoint) zp_w
         // and the column code sums over the non-outlier rows, 128 per wave
         float* a1_tail = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(A1) + 3 * kOutWave);
@@ -526,9 +527,8 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q), !w8);
         if (w8)
             for (int q = 0; q < nst; ++q) stage_w8_slice(q, n_o, o0, o, idx, Wq, c_w, q ? slice_at(q) : olds);
-        // 1 / c_w of the wave's 128 columns (reciprocals to 1 ulp)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) invw[lane + 64 * i] = __builtin_amdgcn_rcpf(cw_pf[i]);
+        for (int i = 0; i < 2; ++i) scl[t + 256 * i] = __builtin_amdgcn_rcpf(scl[t + 256 * i]);
         if (has_bias) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) bsl[lane + 64 * i] = half_bits_to_float(bias_bits[i]);
@@ -557,10 +557,15 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             for (int q = 1; q < nst; ++q) transpose_w_slice(slice_at(q));
         }
         // One 32-row block at a time: a lane then holds 4-column runs of one
-        // row across all 128 columns of the wave.
+        // row across all 128 columns of the wave. Written once for the usual
+        // case (every outlier slice staged in LDS) and once with the slices
+        // past those read from global memory, so that the common path carries
+        // none of the other's registers (which pushed values to scratch, and
+        // each reload's wait then also waited for the previous block's stores).
+        auto blocks = [&](auto with_global) {
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
-            const float inv_x = __builtin_amdgcn_rcpf(cx_pf[sb]);
+            const float inv_x = inv_rows[sb * 32 + r32];
             // zeropoint: zp_x of the lane's row and rowsum + (h - |O|) zp_x
             double zx = 0.0, zr = 0.0;
             if constexpr (zpm) {
@@ -602,9 +607,10 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                 // Outlier product X_O W[idx, :] on top (fp32 accumulate).
                 if (nst > 0) f = apply_outlier_slice_t(olds, wo, ws, sb, ob, r32, khalf, f);
                 for (int q = 1; q < nst; ++q) f = apply_outlier_slice_t(slice_at(q), wo, ws, sb, ob, r32, khalf, f);
-                for (int q = nst; q < nsl; ++q)
-                    f = apply_outlier_slice_global(q, n_o, o0, s0, s, o, X_O, ldo, idx, W, Wq, c_w, wo, ws, sb, ob, r32,
-                                                   khalf, f);
+                if constexpr (decltype(with_global)::value)
+                    for (int q = nst; q < nsl; ++q)
+                        f = apply_outlier_slice_global(q, n_o, o0, s0, s, o, X_O, ldo, idx, W, Wq, c_w, wo, ws, sb, ob,
+                                                       r32, khalf, f);
                 // The layer bias, in the same fp32 sum before the rounding.
                 if (has_bias) {
 #pragma unroll
@@ -636,6 +642,11 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                 if (grow < s && gcol < o) *reinterpret_cast<v4i*>(C + grow * o + gcol) = v;
             }
         }
+        };
+        if (nsl > nst)
+            blocks(std::true_type{});
+        else
+            blocks(std::false_type{});
     }
 }
 
