@@ -189,16 +189,31 @@ __device__ __forceinline__ void transpose_w_slice(uint16_t* sl) {
     __syncthreads();
 }
 
-// f += X_O[., slice] W[slice, .] for the 32 x 32 block (sb, ob) of a
-// wave's 128 x 128 output, operands from a staged slice whose W part is
-// transposed (both operands one 16-byte read; the lane holds k = 8
-// (lane / 32) + e of the slice for its column / row).
-__device__ __forceinline__ v16f apply_outlier_slice_t(const uint16_t* sl, int wo, int ws, int sb, int ob, int r32,
-                                                      int khalf, v16f f) {
-    const v8h xb = *reinterpret_cast<const v8h*>(sl + kSlice + (ws * 128 + sb * 32 + r32) * 16 + 8 * khalf);
+// The two operands of a staged, transposed slice: the W part of the
+// lane's column in column block ob, and the X_O part of its row in row
+// block sb.
+__device__ __forceinline__ v8h slice_w_operand(const uint16_t* sl, int wo, int ob, int r32, int khalf) {
     const int col = wo * 128 + ob * 32 + r32;
-    const v8h wa = *reinterpret_cast<const v8h*>(sl + (col * 2 + (khalf ^ ((col >> 3) & 1))) * 8);
-    return mfma_f16_vgpr(wa, xb, f);
+    return *reinterpret_cast<const v8h*>(sl + (col * 2 + (khalf ^ ((col >> 3) & 1))) * 8);
+}
+
+__device__ __forceinline__ v8h slice_x_operand(const uint16_t* sl, int ws, int sb, int r32, int khalf) {
+    return *reinterpret_cast<const v8h*>(sl + kSlice + (ws * 128 + sb * 32 + r32) * 16 + 8 * khalf);
+}
+
+// f[ob] += wa[ob] xb for the four column blocks of one 32-row block: four
+// independent VGPR-form MFMAs back to back under one set of wait states
+// (2 before, for the VALU writes of f; more than the 18 a 16-pass result
+// needs after, before anything reads f).
+__device__ __forceinline__ void mfma4_f16_vgpr(const v8h (&wa)[4], const v8h& xb, v16f (&f)[4]) {
+    asm volatile("s_nop 1\n\t"
+                 "v_mfma_f32_32x32x16_f16 %0, %4, %8, %0\n\t"
+                 "v_mfma_f32_32x32x16_f16 %1, %5, %8, %1\n\t"
+                 "v_mfma_f32_32x32x16_f16 %2, %6, %8, %2\n\t"
+                 "v_mfma_f32_32x32x16_f16 %3, %7, %8, %3\n\t"
+                 "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3])
+                 : "v"(wa[0]), "v"(wa[1]), "v"(wa[2]), "v"(wa[3]), "v"(xb));
 }
 
 // The same for slice q with both operands read from global memory: the
@@ -563,6 +578,17 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         // none of the other's registers (which pushed values to scratch, and
         // each reload's wait then also waited for the previous block's stores).
         auto blocks = [&](auto with_global) {
+        // 1 / c_w of the lane's 64 columns and slice 0's W operands do not
+        // depend on the row block: read once.
+        v4f iwr[4][4];
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) iwr[ob][g] = *reinterpret_cast<const v4f*>(invw + ob * 32 + 8 * g + 4 * khalf);
+        v8h wa0[4] = {};
+        if (nst > 0)
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob) wa0[ob] = slice_w_operand(olds, wo, ob, r32, khalf);
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
             const float inv_x = inv_rows[sb * 32 + r32];
@@ -576,18 +602,18 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     zr = static_cast<double>(static_cast<int64_t>(zp.rowsum_x[srow]) + (h - n_o) * static_cast<int64_t>(z));
                 }
             }
+            // Dequantise the four column blocks: f = C_i32 * (1/c_x) *
+            // (1/c_w); zeropoint: C' = C_i32 + zp_w (rowsum + (h - |O|) zp_x)
+            // + zp_x colsum' by two fp64 FMAs (exact while every term is
+            // below 2^53, i.e. for zero points below 2^17 in magnitude), times
+            // (1/nd_x) * (1/nd_w). fp64 rather than int64 keeps the
+            // accumulators in registers.
+            v16f f[4];
 #pragma unroll
-            for (int ob = 0; ob < 4; ++ob) {
-                // Dequantise: f = C_i32 * (1/c_x) * (1/c_w); zeropoint:
-                // C' = C_i32 + zp_w (rowsum + (h - |O|) zp_x) + zp_x colsum'
-                // by two fp64 FMAs (exact while every term is below 2^53,
-                // i.e. for zero points below 2^17 in magnitude), times
-                // (1/nd_x) * (1/nd_w). fp64 rather than int64 keeps the
-                // accumulators in registers.
-                v16f f;
+            for (int ob = 0; ob < 4; ++ob)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const v4f iw = *reinterpret_cast<const v4f*>(invw + ob * 32 + 8 * g + 4 * khalf);
+                    const v4f iw = iwr[ob][g];
                     if constexpr (zpm) {
                         const v4i zw = *reinterpret_cast<const v4i*>(zpw_l + ob * 32 + 8 * g + 4 * khalf);
                         const v4i cw = *reinterpret_cast<const v4i*>(csw_l + ob * 32 + 8 * g + 4 * khalf);
@@ -596,28 +622,39 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                             const double cp = __fma_rn(zx, static_cast<double>(cw[e]),
                                                        __fma_rn(static_cast<double>(zw[e]), zr,
                                                                 static_cast<double>(acc[ob][sb][4 * g + e])));
-                            f[4 * g + e] = static_cast<float>(cp) * (inv_x * iw[e]);
+                            f[ob][4 * g + e] = static_cast<float>(cp) * (inv_x * iw[e]);
                         }
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            f[4 * g + e] = static_cast<float>(acc[ob][sb][4 * g + e]) * (inv_x * iw[e]);
+                            f[ob][4 * g + e] = static_cast<float>(acc[ob][sb][4 * g + e]) * (inv_x * iw[e]);
                     }
                 }
-                // Outlier product X_O W[idx, :] on top (fp32 accumulate).
-                if (nst > 0) f = apply_outlier_slice_t(olds, wo, ws, sb, ob, r32, khalf, f);
-                for (int q = 1; q < nst; ++q) f = apply_outlier_slice_t(slice_at(q), wo, ws, sb, ob, r32, khalf, f);
-                if constexpr (decltype(with_global)::value)
+            // Outlier product X_O W[idx, :] on top (fp32 accumulate), one
+            // staged slice at a time for all four column blocks.
+            if (nst > 0) mfma4_f16_vgpr(wa0, slice_x_operand(olds, ws, sb, r32, khalf), f);
+            for (int q = 1; q < nst; ++q) {
+                const uint16_t* sl = slice_at(q);
+                v8h wa[4];
+#pragma unroll
+                for (int ob = 0; ob < 4; ++ob) wa[ob] = slice_w_operand(sl, wo, ob, r32, khalf);
+                mfma4_f16_vgpr(wa, slice_x_operand(sl, ws, sb, r32, khalf), f);
+            }
+            if constexpr (decltype(with_global)::value)
+#pragma unroll
+                for (int ob = 0; ob < 4; ++ob)
                     for (int q = nst; q < nsl; ++q)
-                        f = apply_outlier_slice_global(q, n_o, o0, s0, s, o, X_O, ldo, idx, W, Wq, c_w, wo, ws, sb, ob,
-                                                       r32, khalf, f);
+                        f[ob] = apply_outlier_slice_global(q, n_o, o0, s0, s, o, X_O, ldo, idx, W, Wq, c_w, wo, ws, sb,
+                                                           ob, r32, khalf, f[ob]);
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob) {
                 // The layer bias, in the same fp32 sum before the rounding.
                 if (has_bias) {
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const v4f bv = *reinterpret_cast<const v4f*>(bsl + ob * 32 + 8 * g + 4 * khalf);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) f[4 * g + e] += bv[e];
+                        for (int e = 0; e < 4; ++e) f[ob][4 * g + e] += bv[e];
                     }
                 }
                 // Round once to fp16 and stage in this wavefront's LDS area
@@ -625,8 +662,8 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                 // own reads below see these writes).
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const uint32_t lo = pack_half2(f[4 * g], f[4 * g + 1]);
-                    const uint32_t hi = pack_half2(f[4 * g + 2], f[4 * g + 3]);
+                    const uint32_t lo = pack_half2(f[ob][4 * g], f[ob][4 * g + 1]);
+                    const uint32_t hi = pack_half2(f[ob][4 * g + 2], f[ob][4 * g + 3]);
                     *reinterpret_cast<uint2*>(out_st + r32 * kOutRow + ob * 32 + 8 * g + 4 * khalf) =
                         make_uint2(lo, hi);
                 }
