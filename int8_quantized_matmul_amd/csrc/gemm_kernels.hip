@@ -46,8 +46,12 @@ constexpr int kTK = 128;   // reduction bytes per LDS stage
 constexpr int kBuf = 256 * kTK / 16;   // v4i slots of one operand's stage buffer (32 KiB)
 
 // LDS layout of a stage buffer: 256 rows of 128 bytes; row r keeps its
-// 16-byte chunk c in slot 8 r + (c ^ (r & 7)), so that 8 consecutive rows
-// reading the same chunk hit 8 different 16-byte bank groups.
+// 16-byte chunk c in slot 8 r + (c ^ ((r / 2) & 7)). The LDS serves a
+// 16-byte read 16 lanes at a time from 64 banks (16 groups of 16 bytes, two
+// consecutive rows per bank row), so the 16 consecutive rows read at one
+// chunk hit 16 different groups. (With c ^ (r & 7), rows r and r + 8 met in
+// one group and every fragment read took twice as long: measured 1.6x less
+// read throughput for this access pattern.)
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
 // return zero, which pads ragged tiles without branches. Word 3 selects the
@@ -297,30 +301,36 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 
     // Load q (0..7) of wavefront w fills LDS rows 64 w + 8 q .. + 7 (one
     // KiB; lane i writes slot 8 r + i % 8 of row r = 64 w + 8 q + i / 8),
-    // so lane i fetches chunk c = (i % 8) ^ (i / 8) of its row: panel
+    // so lane i fetches chunk c = (i % 8) ^ ((r / 2) & 7) of its row, i.e.
+    // c0 = (i % 8) ^ (i / 16) for even q and c0 ^ 4 for odd q: panel
     // 2 kt + c / 4, bytes 16 (c % 4) of the row's 64 there. Rows past o
     // (whole wavefronts, as o_rows is a multiple of 64) and chunks past h
     // get the out-of-range offset.
     const int dr = lane >> 3;
-    const int c = (lane & 7) ^ dr;
-    const uint32_t vA = 64 * wu < o_rows
-                            ? static_cast<uint32_t>((64 * wu + dr) * 64 + (c & 3) * 16 + (c >> 2) * o * 64)
-                            : kOutOfRange;
+    const int c0 = (lane & 7) ^ (dr >> 1);
+    auto a_offset = [&](int c) {
+        return 64 * wu < o_rows ? static_cast<uint32_t>((64 * wu + dr) * 64 + (c & 3) * 16 + (c >> 2) * o * 64)
+                                : kOutOfRange;
+    };
+    const uint32_t vA[2] = {a_offset(c0), a_offset(c0 ^ 4)};
     uint32_t vB[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) vB[q] = static_cast<uint32_t>((64 * wu + 8 * q + dr) * h + c * 16);
+    for (int q = 0; q < 8; ++q)
+        vB[q] = static_cast<uint32_t>((64 * wu + 8 * q + dr) * h + (c0 ^ (4 * (q & 1))) * 16);
     const int64_t KT = (h + kTK - 1) / kTK;
     // Loads q in [q0, q1) of stage kt into (A, B).
     auto load_part = [&](int64_t kt, v4i* A, v4i* B, int q0, int q1) {
         const uint32_t k = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kt * kTK));
         const int64_t a0 = o0 * 64 + kt * kTK * o;
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq + (a0 < wq_bytes ? a0 : 0), bytes_left(wq_bytes, a0));
-        const uint32_t oob = (k + c * 16 < static_cast<uint32_t>(h)) ? 0u : kOutOfRange;
+        const uint32_t oob[2] = {(k + c0 * 16 < static_cast<uint32_t>(h)) ? 0u : kOutOfRange,
+                                 (k + (c0 ^ 4) * 16 < static_cast<uint32_t>(h)) ? 0u : kOutOfRange};
 #pragma unroll
         for (int q = q0; q < q1; ++q) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(A + (wu * 8 + q) * 64), 16, (vA | oob) + q * 512, 0,
-                                                     0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(B + (wu * 8 + q) * 64), 16, vB[q] | oob, k, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(A + (wu * 8 + q) * 64), 16,
+                                                     (vA[q & 1] | oob[q & 1]) + q * 512, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(B + (wu * 8 + q) * 64), 16, vB[q] | oob[q & 1], k, 0,
+                                                     0);
         }
     };
 
@@ -346,12 +356,12 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
-    // Fragment slots: the four rows a lane reads share r & 7 (= r32 & 7),
-    // so slot(row_i, chunk) = slot(row_0, chunk) + 256 i.
+    // Fragment slots: the four rows a lane reads share (r / 2) & 7
+    // (= (r32 / 2) & 7), so slot(row_i, chunk) = slot(row_0, chunk) + 256 i.
     int offA[4], offB[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        const int x = (kk * 2 + khalf) ^ (r32 & 7);
+        const int x = (kk * 2 + khalf) ^ ((r32 >> 1) & 7);
         offA[kk] = (wo * 128 + r32) * 8 + x;
         offB[kk] = (ws * 128 + r32) * 8 + x;
     }
@@ -379,17 +389,15 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     };
     // One sub-step's order: MFMAs interleaved with the next sub-step's LDS
     // reads and with this part's loads.
+    // At most one load every second MFMA (measured ~1 % faster than one
+    // per MFMA, and faster than one every third, which pushes the last
+    // loads of a stage too close to its wait).
     auto sched_sub = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+            if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+            if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
         }
     };
     // Stage kt from (Ac, Bc); stage kt + 1 sits in (An, Bn), of which loads
