@@ -328,6 +328,53 @@ def run_table5(i8, torch, dev, s, n):
     return rows
 
 
+def run_all_configs(i8, torch, dev, steps):
+    """The one-call forward step and the product kernel alone on every
+    configuration's seeded inputs (the parity tests' inputs), weights
+    converted beforehand: effective TOPS (2 s h o / step) for the prefill
+    shapes, weight bytes per second for the weight-streaming one."""
+    from workloads import CONFIGS, make_inputs
+    rows = []
+    for name, w in CONFIGS.items():
+        inp = make_inputs(w)
+        X = torch.from_numpy(inp["X"]).to(dev)
+        W = torch.from_numpy(inp["W"]).to(dev)
+        del inp
+        s, h, o = w.s, w.h, w.o
+        Wq, c_w = i8.quantize_colwise_weights(W)
+        ws = i8.forward_workspace(s, h, dev)
+        v = i8.forward_workspace_views(ws, s, h)
+        C = torch.empty((s, o), dtype=torch.float16, device=dev)
+
+        def step():
+            i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C)
+
+        settle(torch, step)
+        step_ms = timed_ms(torch, steps, step)
+        gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
+            v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
+        n_out = int(v["n_out"].cpu()[0])
+        row = {"workload": name, "s": s, "h": h, "o": o, "n_outliers": n_out, "outlier_row_frac": w.row_frac,
+               "step_ms": round(step_ms, 5), "product_kernel_ms": round(gemm_ms, 5)}
+        if w.decode:
+            wb = h * o + 2 * n_out * o + 4 * o
+            row["weight_GB_per_s"] = round(wb / (step_ms * 1e-3) / 1e9, 1)
+            row["pct_hbm_peak"] = round(100 * wb / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+            row["product_kernel_weight_GB_per_s"] = round(wb / (gemm_ms * 1e-3) / 1e9, 1)
+        else:
+            tops = 2.0 * s * h * o / (step_ms * 1e-3) / 1e12
+            gemm_tops = 2.0 * s * (h - n_out) * o / (gemm_ms * 1e-3) / 1e12
+            row["effective_TOPS"] = round(tops, 1)
+            row["pct_int8_peak"] = round(100 * tops / INT8_PEAK_TOPS, 2)
+            row["product_kernel_TOPS"] = round(gemm_tops, 1)
+            row["product_kernel_pct_peak"] = round(100 * gemm_tops / INT8_PEAK_TOPS, 2)
+        _log(f"[configs] {row}")
+        rows.append(row)
+        del X, W, Wq, c_w, ws, v, C
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(w, inputs, budget_s):
     """Time the CPU oracle (as it stands) on the same workload's inputs.
 
@@ -382,6 +429,9 @@ def main(argv=None):
                     help="only run the pages' Table 5 comparison set over the GPT-3 FFN widths "
                          "and print it as one JSON line")
     ap.add_argument("--table5-rows", type=int, default=2048, help="rows of X (tokens) for --table5")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="only time the one-call forward and the product kernel on every configuration "
+                         "(tiny, prefill, decode, QKV prefill, outlier-density sweep) and print one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (5 times) and exit; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -411,6 +461,11 @@ def main(argv=None):
         print(json.dumps({"table5": rows, "pages_table5": TABLE5_PAGES,
                           "note": "raw matmul of X [s, d] x W [d, 4d], inputs resident; "
                                   "speed-up = FP16 library GEMM time / variant time"}), flush=True)
+        return 0
+    if args.all_configs:
+        print(json.dumps({"all_configs": run_all_configs(i8, torch, dev, args.steps),
+                          "note": "one-call forward step (detect + quantise + product) and the product "
+                                  "kernel alone, weights converted beforehand, inputs resident"}), flush=True)
         return 0
     w = get_config(args.workload)
     _log(f"[bench] prefill workload {w.name}: s={w.s} h={w.h} o={w.o}")
