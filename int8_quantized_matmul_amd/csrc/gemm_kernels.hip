@@ -256,6 +256,29 @@ constexpr int kOutRow = 136;
 constexpr int kOutWave = 32 * kOutRow;          // halves per wavefront
 constexpr int kMaxOnceSlices = 5;               // extra slices staged at once
 
+// Writes a wavefront's staged 32 x 128 fp16 block (rows srow0 .. + 31 and
+// columns ocol0 .. + 127 of C) as full 256-byte rows: 16 lanes per row, 4
+// rows per store, with no branch: the stores take 32-bit
+// offsets from a buffer resource that starts at row srow0 and ends with row
+// s - 1, so rows past s fall outside it and columns past o get an
+// out-of-range offset (offsets stay below 64 o < 2^31 as h o < 2^31).
+__device__ __forceinline__ void store_staged_block(const uint16_t* out_st, uint16_t* C, int64_t srow0, int64_t ocol0,
+                                                   int64_t s, int64_t o, int lane) {
+    const int64_t rows = s - srow0;
+    const uint32_t bytes = rows <= 0 ? 0u : static_cast<uint32_t>((rows < 32 ? rows : 32) * o * 2);
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(C + (rows > 0 ? srow0 * o : 0), bytes);
+    const uint32_t o32 = static_cast<uint32_t>(o);
+    const uint32_t col = static_cast<uint32_t>(ocol0) + (lane & 15) * 8;
+    const bool col_ok = col < o32;
+    const uint32_t off0 = ((lane >> 4) * o32 + col) * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const v4i v = *reinterpret_cast<const v4i*>(out_st + (4 * i + (lane >> 4)) * kOutRow + (lane & 15) * 8);
+        const uint32_t off = col_ok ? off0 + static_cast<uint32_t>(i) * 8 * o32 : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rC, off, 0, 0);
+    }
+}
+
 // Prefill main loop (also the dense fp16 product, MODE Fp16Dense: the same
 // byte geometry with 2-byte elements, see launch_fp16_gemm): both operand
 // tiles reach LDS through direct-to-LDS
@@ -481,14 +504,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                         make_uint2(lo, hi);
                 }
             }
-            const int64_t gcol = o0 + wo * 128 + (lane & 15) * 8;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = 4 * i + (lane >> 4);
-                const v4i v = *reinterpret_cast<const v4i*>(out_st + row * kOutRow + (lane & 15) * 8);
-                const int64_t grow = s0 + ws * 128 + sb * 32 + row;
-                if (grow < s && gcol < o) *reinterpret_cast<v4i*>(C + grow * o + gcol) = v;
-            }
+            store_staged_block(out_st, C, s0 + ws * 128 + sb * 32, o0 + wo * 128, s, o, lane);
         }
     } else if constexpr (MODE == GemmOut::Int32) {
         int32_t* C = static_cast<int32_t*>(Cout);
@@ -512,17 +528,14 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         __syncthreads();   // every wavefront is done with the stage buffers
         // Epilogue LDS: extra outlier slices q = 1, 2 in A0, 3, 4 in B0 and
         // 5 in B1; output staging of waves 0-2 in A1, followed there by the
-        // bias, and of wave 3 in B1, followed there by 1 / c_w.
+        // bias and the zeropoint vectors, and of wave 3 in B1; the scales in
+        // their own array.
         auto slice_at = [&](int q) -> uint16_t* {   // q = 1 .. kMaxOnceSlices
             uint16_t* base = q <= 2 ? reinterpret_cast<uint16_t*>(A0)
                            : q <= 4 ? reinterpret_cast<uint16_t*>(B0)
                                     : reinterpret_cast<uint16_t*>(B1) + kOutWave + 1024;
             return base + (q <= 4 ? ((q - 1) & 1) * 2 * kSlice : 0);
         };
-        uint16_t* out_st = wid < 3 ? reinterpret_cast<uint16_t*>(A1) + wid * kOutWave : reinterpret_cast<uint16_t*>(B1);
-        // 1 / c_x and 1 / c_w of the tile (reciprocals to 1 ulp), in place
-        float* inv_rows = scl + ws * 128;
-        float* invw = scl + 256 + wo * 128;
         // after the staging of waves 0-2 in A1: bias, then (zeropoint) zp_w
         // and the column code sums over the non-outlier rows, 128 per wave
         float* a1_tail = reinterpret_cast<float*>(reinterpret_cast<uint16_t*>(A1) + 3 * kOutWave);
@@ -550,6 +563,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             stage_outlier_slice(q, n_o, wu, lane, o0, s0, s, o, ldo, idx, rW, rX, slice_at(q), !w8);
         if (w8)
             for (int q = 0; q < nst; ++q) stage_w8_slice(q, n_o, o0, o, idx, Wq, c_w, q ? slice_at(q) : olds);
+        // 1 / c_x and 1 / c_w of the tile (reciprocals to 1 ulp), in place
 #pragma unroll
         for (int i = 0; i < 2; ++i) scl[t + 256 * i] = __builtin_amdgcn_rcpf(scl[t + 256 * i]);
         if (has_bias) {
@@ -586,6 +600,18 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         // none of the other's registers (which pushed values to scratch, and
         // each reload's wait then also waited for the previous block's stores).
         auto blocks = [&](auto with_global) {
+        // The lane's indices are derived again here from an opaque copy of
+        // the thread index: left to the compiler, it computed them before
+        // the K loop and carried them (or spilled them) across it.
+        int te = static_cast<int>(threadIdx.x);
+        asm volatile("" : "+v"(te));
+        const int lane = te & 63, wid = te >> 6, wo = wid & 1, ws = wid >> 1, r32 = lane & 31, khalf = lane >> 5;
+        uint16_t* out_st = wid < 3 ? reinterpret_cast<uint16_t*>(A1) + wid * kOutWave : reinterpret_cast<uint16_t*>(B1);
+        const float* inv_rows = scl + ws * 128;
+        const float* invw = scl + 256 + wo * 128;
+        const float* bsl = a1_tail + wid * 128;
+        const int* zpw_l = reinterpret_cast<const int*>(a1_tail + 512) + wid * 128;
+        const int* csw_l = reinterpret_cast<const int*>(a1_tail + 1024) + wid * 128;
         // 1 / c_w of the lane's 64 columns and slice 0's W operands do not
         // depend on the row block: read once.
         v4f iwr[4][4];
@@ -676,16 +702,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                         make_uint2(lo, hi);
                 }
             }
-            // Write the 32 x 128 block as full 256-byte rows: 16 lanes per
-            // row, 4 rows per store instruction.
-            const int64_t gcol = o0 + wo * 128 + (lane & 15) * 8;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = 4 * i + (lane >> 4);
-                const v4i v = *reinterpret_cast<const v4i*>(out_st + row * kOutRow + (lane & 15) * 8);
-                const int64_t grow = s0 + ws * 128 + sb * 32 + row;
-                if (grow < s && gcol < o) *reinterpret_cast<v4i*>(C + grow * o + gcol) = v;
-            }
+            store_staged_block(out_st, C, s0 + ws * 128 + sb * 32, o0 + wo * 128, s, o, lane);
         }
         };
         if (nsl > nst)
