@@ -13,8 +13,9 @@
 // the A fragment of a 16x16x64 MFMA (16 columns x 64 reduction bytes) is one
 // contiguous KiB and a 256-column tile of one panel is 16 contiguous KiB.
 // The matrix core computes D[o][s] (W_i8 as the A operand), so each lane
-// ends up holding runs of 4 consecutive output columns of one row of C and
-// stores them as one 8-byte fp16 quad.
+// ends up holding runs of 4 consecutive output columns of one row of C: the
+// decode epilogue stores them as 8-byte fp16 quads, the prefill epilogue
+// regroups them through LDS into full 256-byte rows.
 //
 // Two main loops share the epilogue structure:
 //  * k_gemm_prefill: 256x256 output tile per 256-thread block, K step 128
@@ -54,7 +55,8 @@ constexpr int kBuf = 256 * kTK / 16;   // v4i slots of one operand's stage buffe
 // read throughput for this access pattern.)
 
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
-// return zero, which pads ragged tiles without branches. Word 3 selects the
+// return zero and stores there are dropped, which handles ragged tiles
+// without branches. Word 3 selects the
 // 32-bit data format that raw loads on gfx9-family parts expect.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),

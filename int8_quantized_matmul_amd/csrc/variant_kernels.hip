@@ -134,6 +134,129 @@ __global__ __launch_bounds__(256) void k_quant_rows_zp(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
+// The same with the row held in registers and split over WPR wavefronts
+// (4 / WPR rows per block; part q of a row owns its 8-column chunks
+// 64 (WPR p + q) + lane, p < CPL), as the absmax row quantiser does: X is
+// read once, the outlier values go to X_O straight from the registers, min
+// and max exclude the outlier columns, and the parts of a row meet in LDS
+// for min, max and the code sum. The codes are those of k_quant_rows_zp
+// (same zeropoint_of / zeropoint_code). Dynamic LDS: nw mask words + nw
+// prefix counts.
+template <int CPL, int WPR>
+__global__ __launch_bounds__(256) void k_quant_rows_zp_reg(const uint16_t* __restrict__ X, int64_t s, int64_t h,
+                                                           const uint32_t* __restrict__ mask,
+                                                           int8_t* __restrict__ Xq, float* __restrict__ nd_x,
+                                                           int32_t* __restrict__ zp_x, int32_t* __restrict__ rowsum_x,
+                                                           uint16_t* __restrict__ X_O, int64_t ldo) {
+    extern __shared__ uint32_t dyn[];
+    __shared__ int wsum[4];
+    __shared__ float part_lo[4], part_hi[4];
+    __shared__ int part_sum[4];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int part = wid % WPR;
+    const int nw = static_cast<int>(h / 32);
+    uint32_t* smask = dyn;
+    int* pre = reinterpret_cast<int*>(dyn + nw);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * (4 / WPR) + wid / WPR;
+    const bool live = i < s;
+    const uint16_t* xr = X + (live ? i : 0) * h;
+    const int64_t nch = h / 8;
+    auto chunk_of = [&](int p) -> int64_t { return 64 * (WPR * p + part) + lane; };
+
+    // mask words first, then the row (chunks past the row, and every chunk
+    // of a row past s, read zero)
+    uint32_t mw = 0u;
+    if (t < nw) mw = mask[t];
+    const __amdgpu_buffer_rsrc_t rrow = range_rsrc(xr, live ? static_cast<uint32_t>(2 * h) : 0u);
+    uint4 cache[CPL];
+#pragma unroll
+    for (int p = 0; p < CPL; ++p) cache[p] = load_chunk_rsrc(rrow, static_cast<uint32_t>(chunk_of(p) * 16));
+    if (t < nw) smask[t] = mw;
+    for (int w = t + 256; w < nw; w += 256) smask[w] = mask[w];   // h > 8192
+    __syncthreads();
+    const int n = block_mask_prefix(smask, pre, nw, wsum, 256);
+
+    uint16_t* orow = X_O + i * ldo;
+    auto bits_of = [&](int64_t c) { return (smask[c >> 2] >> ((c & 3) * 8)) & 0xffu; };
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < CPL; ++p) {
+        const int64_t c = chunk_of(p);
+        if (c >= nch) continue;
+        const uint32_t bits = bits_of(c);
+        if (bits && live) {
+            const int w = static_cast<int>(c >> 2), sh = static_cast<int>(c & 3) * 8;
+            int rank = pre[w] + __popc(smask[w] & ((1u << sh) - 1u));
+            for (uint32_t b = bits; b; b &= b - 1u) {
+                const int e = __ffs(b) - 1;
+                orow[rank++] = static_cast<uint16_t>(word_of(cache[p], e >> 1) >> ((e & 1) * 16));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (!((bits >> e) & 1u)) {
+                const float x = half_at(cache[p], e);
+                lo = fminf(lo, x);
+                hi = fmaxf(hi, x);
+            }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, kWave));
+        hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
+    }
+    if constexpr (WPR > 1) {
+        if (lane == 0) {
+            part_lo[wid] = lo;
+            part_hi[wid] = hi;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < WPR; ++q) {
+            lo = fminf(lo, part_lo[wid - part + q]);
+            hi = fmaxf(hi, part_hi[wid - part + q]);
+        }
+    }
+    if (lo > hi) lo = hi = 0.0f;   // every column is an outlier
+    const ZeroPoint z = zeropoint_of(lo, hi);
+
+    int8_t* qr = Xq + i * h;
+    int sum = 0;
+#pragma unroll
+    for (int p = 0; p < CPL; ++p) {
+        const int64_t c = chunk_of(p);
+        if (c >= nch) continue;
+        const uint32_t bits = bits_of(c);
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int q = (bits >> e) & 1u ? 0 : zeropoint_code(half_at(cache[p], e), z);
+            sum += q;
+            packed[e >> 2] |= (static_cast<uint32_t>(q) & 0xffu) << ((e & 3) * 8);
+        }
+        if (live) *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(packed[0], packed[1]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+    if constexpr (WPR > 1) {
+        if (lane == 0) part_sum[wid] = sum;
+        __syncthreads();
+        sum = 0;
+#pragma unroll
+        for (int q = 0; q < WPR; ++q) sum += part_sum[wid - part + q];
+    }
+    if (!live) return;
+    if (lane == 0 && part == 0) {
+        nd_x[i] = z.nd;
+        zp_x[i] = z.zp;
+        rowsum_x[i] = sum;
+    }
+    const int npad = (n + 31) & ~31;
+    if (part == 0)
+        for (int k = n + lane; k < npad; k += 64) orow[k] = 0;
+}
+
+// ---------------------------------------------------------------------------
 // Columns of W (load time) into the panel layout Wq [h / 64][o][64], as
 // k_quant_cols does for absmax: one 256-thread block per 64-column strip;
 // pass 1 takes min and max per column over all h rows, pass 2 quantises
@@ -222,8 +345,36 @@ hipError_t launch_quantize_rows_zp(const uint16_t* X, int64_t s, int64_t h, cons
                                    float* nd_x, int32_t* zp_x, int32_t* rowsum_x, uint16_t* X_O, int64_t ldo,
                                    hipStream_t stream) {
     const size_t dyn = static_cast<size_t>(2 * (h / 32) * 4);
-    hipLaunchKernelGGL(k_quant_rows_zp, dim3(static_cast<unsigned>((s + 3) / 4)), dim3(256), dyn, stream, X, s, h,
-                       mask, Xq, nd_x, zp_x, rowsum_x, X_O, ldo);
+    // Wavefronts per row as for the absmax row quantiser: ~4096 wavefronts
+    // in all while each holds at most 16 chunks of its row.
+    const int64_t nch = h / 8;
+    int wpr = s >= 4096 ? 1 : s >= 2048 ? 2 : 4;
+    while (wpr > 1 && (nch + 64 * wpr - 1) / (64 * wpr) > 16) wpr = wpr == 4 ? 1 : 4;
+    const int64_t per_lane = (nch + 64 * wpr - 1) / (64 * wpr);
+    if (per_lane > 16) {
+        // long rows: one wavefront per row reading it twice
+        hipLaunchKernelGGL(k_quant_rows_zp, dim3(static_cast<unsigned>((s + 3) / 4)), dim3(256), dyn, stream, X, s,
+                           h, mask, Xq, nd_x, zp_x, rowsum_x, X_O, ldo);
+        return hipGetLastError();
+    }
+    const dim3 grid(static_cast<unsigned>((s + 4 / wpr - 1) / (4 / wpr))), block(256);
+#define I8MM_ZPROWS(CPL, W)                                                                                      \
+    hipLaunchKernelGGL((k_quant_rows_zp_reg<CPL, W>), grid, block, dyn, stream, X, s, h, mask, Xq, nd_x, zp_x,    \
+                       rowsum_x, X_O, ldo)
+#define I8MM_ZPROWS_W(W)                                 \
+    if (per_lane <= 2) I8MM_ZPROWS(2, W);                \
+    else if (per_lane <= 4) I8MM_ZPROWS(4, W);           \
+    else if (per_lane <= 8) I8MM_ZPROWS(8, W);           \
+    else I8MM_ZPROWS(16, W);
+    if (wpr == 4) {
+        I8MM_ZPROWS_W(4)
+    } else if (wpr == 2) {
+        I8MM_ZPROWS_W(2)
+    } else {
+        I8MM_ZPROWS_W(1)
+    }
+#undef I8MM_ZPROWS_W
+#undef I8MM_ZPROWS
     return hipGetLastError();
 }
 

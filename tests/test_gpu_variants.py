@@ -129,3 +129,30 @@ def test_variants_with_bias(s):
         C = i8.variant_forward(Xd, i8.quantize_weights(Wd, scheme), Wd, scheme, bias=bd)
         torch.cuda.synchronize()
         check_C(C, oracle.variant_forward(X, W, scheme, bias=b))
+
+
+# (s, h): every launch shape of the zeropoint row quantiser, named by the
+# wavefronts per row and chunks per lane it picks (more rows, fewer
+# wavefronts per row; rows longer than 16 chunks per lane take the two-pass
+# kernel that reads each row twice).
+ZP_ROW_SHAPES = [(2048, 256, "W2 CPL2"), (2048, 4096, "W2 CPL4"), (2048, 8192, "W2 CPL8"),
+                 (4096, 256, "W1 CPL2"), (4096, 2048, "W1 CPL4"), (64, 8192, "W4 CPL4"),
+                 (16, 16384, "W4 CPL8"), (4, 32768, "W4 CPL16"), (3, 40960, "two-pass")]
+
+
+@pytest.mark.parametrize("s,h,label", ZP_ROW_SHAPES, ids=[c[2] for c in ZP_ROW_SHAPES])
+def test_zeropoint_rows_every_launch_shape(s, h, label):
+    inp = random_case(260 + s % 97 + h % 89, s, h, 64, 5, row_frac=0.5)
+    X = inp["X"].copy()
+    X[: s // 2] = np.abs(X[: s // 2])                  # one-signed rows
+    X[s // 2:] += np.float16(1.5)                       # shifted rows
+    say(f"  launch: zeropoint rows {label} s={s} h={h}")
+    mask, idx, n_out, idx_r = _gpu_detect(X, 6.0)
+    Xq, nd_x, zp_x, rs_x, X_O = i8.quantize_rowwise_zeropoint(T(X), mask, idx, n_out)
+    torch.cuda.synchronize()
+    Xq_r, ndx_r, zpx_r, XO_r = oracle.quantize_rowwise_zeropoint(X, idx_r)
+    assert np.array_equal(H(Xq), Xq_r), "zeropoint Xq differs"
+    assert np.array_equal(H(nd_x).view(np.uint32), ndx_r.view(np.uint32)), "nd_x differs"
+    assert np.array_equal(H(zp_x), zpx_r), "zp_x differs"
+    assert np.array_equal(H(rs_x), Xq_r.astype(np.int64).sum(axis=1)), "rowsum_x differs"
+    _check_XO(X_O, XO_r)
