@@ -161,7 +161,7 @@ enum class RowScale { Absmax, MaxOnly, Given };
 // WPR wavefronts share a row (4 / WPR rows per block; wavefront part q of a
 // row owns its chunks 64 (WPR p + q) + lane) and meet in LDS for the row
 // maximum, so that few rows still give the GPU enough wavefronts; WPR > 1
-// only with the row's own absmax and the row held in registers.
+// only with the row held in registers.
 template <int CPL, RowScale SC = RowScale::Absmax, int WPR = 1>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ X, int64_t s, int64_t h,
                                                     const uint32_t* __restrict__ src_mask,
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
                                                     int32_t* __restrict__ n_out,
                                                     int8_t* __restrict__ Xq, float* __restrict__ c_x,
                                                     uint16_t* __restrict__ X_O, int64_t ldo) {
-    static_assert(WPR == 1 || (SC == RowScale::Absmax && CPL > 0), "row split needs the row in registers");
+    static_assert(WPR == 1 || CPL > 0, "row split needs the row in registers");
     extern __shared__ uint32_t dyn[];
     __shared__ int wsum[4];
     __shared__ uint32_t part_max[4];
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
         if (!live) return;
     }
     if constexpr (SC == RowScale::MaxOnly) {
-        if (lane == 0) c_x[i] = absmax_value(m2);
+        if (lane == 0 && part == 0) c_x[i] = absmax_value(m2);
         return;
     }
     float sc;
@@ -673,8 +673,25 @@ hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
 hipError_t launch_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h, const uint32_t* mask, int8_t* Xq,
                                       float* c_x, uint16_t* X_O, int64_t ldo, hipStream_t stream) {
     // row maxima into c_x, one constant over them, then the codes with it
-    const dim3 grid(static_cast<unsigned>((s + 3) / 4)), block(256);
     const size_t dyn = static_cast<size_t>(2 * (h / 32) * 4);
+    const int64_t per_lane4 = (h / 8 + 255) / 256;   // chunks per lane with 4 wavefronts per row
+    if (s < 2048 && per_lane4 <= 16) {
+        // few rows: each row split over 4 wavefronts and held in registers
+        const dim3 grid(static_cast<unsigned>(s)), block(256);
+#define I8MM_TW(CPL)                                                                                         \
+    hipLaunchKernelGGL((k_quant_rows<CPL, RowScale::MaxOnly, 4>), grid, block, dyn, stream, X, s, h, mask,    \
+                       nullptr, nullptr, nullptr, Xq, c_x, X_O, ldo);                                         \
+    hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(1024), 0, stream, c_x, s);                              \
+    hipLaunchKernelGGL((k_quant_rows<CPL, RowScale::Given, 4>), grid, block, dyn, stream, X, s, h, mask,      \
+                       nullptr, nullptr, nullptr, Xq, c_x, X_O, ldo)
+        if (per_lane4 <= 2) { I8MM_TW(2); }
+        else if (per_lane4 <= 4) { I8MM_TW(4); }
+        else if (per_lane4 <= 8) { I8MM_TW(8); }
+        else { I8MM_TW(16); }
+#undef I8MM_TW
+        return hipGetLastError();
+    }
+    const dim3 grid(static_cast<unsigned>((s + 3) / 4)), block(256);
     hipLaunchKernelGGL((k_quant_rows<0, RowScale::MaxOnly>), grid, block, dyn, stream, X, s, h, mask, nullptr,
                        nullptr, nullptr, Xq, c_x, X_O, ldo);
     hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(1024), 0, stream, c_x, s);

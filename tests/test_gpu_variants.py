@@ -156,3 +156,24 @@ def test_zeropoint_rows_every_launch_shape(s, h, label):
     assert np.array_equal(H(zp_x), zpx_r), "zp_x differs"
     assert np.array_equal(H(rs_x), Xq_r.astype(np.int64).sum(axis=1)), "rowsum_x differs"
     _check_XO(X_O, XO_r)
+
+
+# (s, h): launch shapes of the tensor-wise row passes (row maxima, then codes
+# with the one constant): few rows split over 4 wavefronts with the row in
+# registers at 2 to 16 chunks per lane, otherwise one wavefront per row.
+TW_ROW_SHAPES = [(8, 1024, "W4 CPL2"), (64, 8192, "W4 CPL4"), (16, 16384, "W4 CPL8"), (4, 32768, "W4 CPL16"),
+                 (3, 40960, "one wavefront per row"), (2048, 256, "many rows")]
+
+
+@pytest.mark.parametrize("s,h,label", TW_ROW_SHAPES, ids=[c[2] for c in TW_ROW_SHAPES])
+def test_tensorwise_rows_every_launch_shape(s, h, label):
+    inp = random_case(270 + s % 97 + h % 89, s, h, 64, 5, row_frac=0.5)
+    X = inp["X"]
+    say(f"  launch: tensor-wise rows {label} s={s} h={h}")
+    mask, idx, n_out, idx_r = _gpu_detect(X, 6.0)
+    Xq, c_x, X_O = i8.quantize_tensorwise(T(X), mask, idx, n_out)
+    torch.cuda.synchronize()
+    Xq_r, cx_r, XO_r = oracle.quantize_tensorwise(X, idx_r)
+    assert np.array_equal(H(Xq), Xq_r), "tensor-wise Xq differs"
+    assert np.array_equal(H(c_x).view(np.uint32), cx_r.view(np.uint32)), "tensor-wise c_x differs"
+    _check_XO(X_O, XO_r)
