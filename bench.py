@@ -260,16 +260,31 @@ def quantiser_variants(i8, torch, steps, X, W, alpha, fused_ms):
     """Table 1's quantiser schemes on the same layer ([DIGEST] "Quantization
     Primitives", "Vector-wise Quantization"): one forward of each, as the
     sequence of C-ABI calls variant_forward makes (detection, the scheme's
-    row quantiser, its product; weights converted beforehand), average ms of
-    `steps` back-to-back forwards, with the one-call fused vector-wise
-    forward for reference."""
+    row quantiser, its product; weights converted beforehand) and as the
+    scheme's one-call forward, average ms of `steps` back-to-back forwards,
+    with the bench's own vector-wise step for reference."""
     out = {}
+    s, h = X.shape
+    ws = i8.forward_workspace(s, h, X.device, zeropoint=True)
+    C = torch.empty((s, W.shape[1]), dtype=torch.float16, device=X.device)
+    one_call = {}
     for scheme in i8.SCHEMES:
         qw = i8.quantize_weights(W, scheme)
         out[scheme + "_ms"] = round(timed_ms(torch, steps, lambda: i8.variant_forward(X, qw, W, scheme, alpha)), 5)
+        # the same scheme through its one-call forward (row- and vector-wise
+        # share i8mm_forward; they differ in the weights' constants)
+        if scheme == "tensor":
+            fn = lambda: i8.forward_tensorwise(X, qw[0], qw[1], W, alpha, workspace=ws, C=C)
+        elif scheme == "zeropoint":
+            fn = lambda: i8.forward_zeropoint(X, qw, W, alpha, workspace=ws, C=C)
+        else:
+            fn = lambda: i8.forward(X, qw[0], qw[1], W, alpha, workspace=ws, C=C)
+        one_call[scheme + "_ms"] = round(timed_ms(torch, steps, fn), 5)
         del qw
+    out["one_call"] = one_call
     out["vector_fused_forward_ms"] = round(fused_ms, 5)
     out["zeropoint_vs_vector"] = round(out["zeropoint_ms"] / out["vector_ms"], 3)
+    out["one_call_zeropoint_vs_vector"] = round(one_call["zeropoint_ms"] / one_call["vector_ms"], 3)
     return out
 
 

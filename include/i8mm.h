@@ -333,6 +333,47 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
                          void* workspace, uint16_t* C, hipStream_t stream);
 
 /*
+ * The same one-call forward with tensor-wise absmax for X ([DIGEST]
+ * "Quantization Primitives": one constant 127 / max |X| over the columns not
+ * in O; Table 1's tensor-wise row): detection, then the maxima of the rows,
+ * one constant over them and the codes with it, then the decomposed product,
+ * in five kernel launches. Arguments, workspace (same size and layout as
+ * i8mm_forward's; c_x holds the one constant in every entry) and errors as
+ * for i8mm_forward. With c_w from i8mm_quantize_weights_tensorwise this is
+ * Table 1's tensor-wise scheme; with column-wise c_w, tensor-wise X against
+ * vector-wise W.
+ */
+i8mm_status i8mm_forward_tensorwise(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                    const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                    void* workspace, uint16_t* C, hipStream_t stream);
+
+/*
+ * Bytes of device workspace that i8mm_forward_zeropoint needs for (s, h):
+ * i8mm_forward's workspace followed by zp_x [s] int32 and rowsum_x [s]
+ * int32, each 256-byte aligned. Returns 0 for invalid shapes.
+ */
+size_t i8mm_forward_zeropoint_workspace_bytes(int64_t s, int64_t h);
+
+/*
+ * The one-call forward of the zeropoint vector-wise scheme with the
+ * decomposition (Table 1's zeropoint rows; the product as for
+ * i8mm_zeropoint_matmul): detection, zeropoint row quantisation and gather,
+ * the zeropoint product, in three kernel launches. Weights from
+ * i8mm_quantize_colwise_weights_zeropoint (Wq, nd_w, zp_w, colsum_w); W
+ * (fp16, for the outlier rows) must not be NULL; bias may be. workspace:
+ * i8mm_forward_zeropoint_workspace_bytes(s, h) bytes, 256-byte aligned, its
+ * first I8MM_FORWARD_ACC_BYTES bytes zero before the first call and left
+ * zero again (the same workspace may serve i8mm_forward and the other
+ * one-call forwards). After completion it holds the intermediates at the
+ * offsets of i8mm_forward_workspace_layout (nd_x in place of c_x), then
+ * zp_x and rowsum_x. Errors as for i8mm_forward.
+ */
+i8mm_status i8mm_forward_zeropoint(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                   const int8_t* Wq, const float* nd_w, const int32_t* zp_w, const int32_t* colsum_w,
+                                   const uint16_t* W, const uint16_t* bias, void* workspace, uint16_t* C,
+                                   hipStream_t stream);
+
+/*
  * Byte offsets inside the forward workspace, in the order accumulator, mask,
  * idx, n_out, Xq, c_x, X_O (7 entries written to offsets[]), and the X_O row
  * stride (elements) in *ldo. Returns I8MM_EINVAL for bad shapes or null

@@ -28,6 +28,8 @@ __all__ = [
     "outlier_matmul",
     "int8_gemm_i32",
     "forward",
+    "forward_tensorwise",
+    "forward_zeropoint",
     "pack_fp16_weights",
     "fp16_gemm",
     "quantize_tensorwise",
@@ -394,10 +396,12 @@ def variant_forward(X: torch.Tensor, qw: Tuple[torch.Tensor, ...], W: torch.Tens
     return int8_mixed_matmul(Xq, c_x, X_O, idx, n_out, Wq, c_w, W, bias=bias)
 
 
-def forward_workspace(s: int, h: int, device) -> torch.Tensor:
-    """A zero-filled device workspace (uint8) for forward(). Its leading
-    accumulator must start at zero; forward() leaves it zero again."""
-    n = _lib.i8mm_forward_workspace_bytes(s, h)
+def forward_workspace(s: int, h: int, device, zeropoint: bool = False) -> torch.Tensor:
+    """A zero-filled device workspace (uint8) for forward() and
+    forward_tensorwise() (zeropoint=True: sized for forward_zeropoint(),
+    which also serves the others). Its leading accumulator must start at
+    zero; every one-call forward leaves it zero again."""
+    n = (_lib.i8mm_forward_zeropoint_workspace_bytes if zeropoint else _lib.i8mm_forward_workspace_bytes)(s, h)
     if n == 0:
         raise I8MMError(f"invalid shape for the forward workspace: s={s}, h={h}")
     return torch.zeros((n,), dtype=torch.uint8, device=device)
@@ -446,4 +450,53 @@ def forward(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Optional[to
         _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o), _bias_ptr(bias, o),
         _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
     _check(st, "forward")
+    return C
+
+
+def forward_tensorwise(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Optional[torch.Tensor],
+                       alpha: float = 6.0, workspace: Optional[torch.Tensor] = None,
+                       C: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """forward() with tensor-wise absmax for X (one constant over the columns
+    not in O): Table 1's tensor-wise scheme with weights from
+    quantize_weights_tensorwise (or quantize_weights(W, "tensor"))."""
+    s, h = X.shape
+    o = Wq.shape[1]
+    if workspace is None:
+        workspace = forward_workspace(s, h, X.device)
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.float16, device=X.device)
+    need = _lib.i8mm_forward_workspace_bytes(s, h)
+    if workspace.numel() < need or workspace.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
+    st = _lib.i8mm_forward_tensorwise(
+        _dev(X, "X", torch.float16), s, h, o, float(alpha), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)),
+        _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o), _bias_ptr(bias, o),
+        _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
+    _check(st, "forward_tensorwise")
+    return C
+
+
+def forward_zeropoint(X: torch.Tensor, qw: Tuple[torch.Tensor, ...], W: torch.Tensor, alpha: float = 6.0,
+                      workspace: Optional[torch.Tensor] = None, C: Optional[torch.Tensor] = None,
+                      bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The one-call forward of the zeropoint vector-wise scheme: qw = (Wq,
+    nd_w, zp_w, colsum_w) from quantize_weights(W, "zeropoint"); W (fp16) is
+    required for the outlier rows. The workspace must come from
+    forward_workspace(s, h, device, zeropoint=True) or be as large."""
+    s, h = X.shape
+    Wq, nd_w, zp_w, cs_w = qw
+    o = Wq.shape[1]
+    if workspace is None:
+        workspace = forward_workspace(s, h, X.device, zeropoint=True)
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.float16, device=X.device)
+    need = _lib.i8mm_forward_zeropoint_workspace_bytes(s, h)
+    if workspace.numel() < need or workspace.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
+    st = _lib.i8mm_forward_zeropoint(
+        _dev(X, "X", torch.float16), s, h, o, float(alpha), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)),
+        _dev(nd_w, "nd_w", torch.float32, (o,)), _dev(zp_w, "zp_w", torch.int32, (o,)),
+        _dev(cs_w, "colsum_w", torch.int32, (o,)), _dev(W, "W", torch.float16, (h, o)), _bias_ptr(bias, o),
+        _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
+    _check(st, "forward_zeropoint")
     return C

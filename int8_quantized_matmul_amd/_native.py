@@ -37,6 +37,10 @@ _SIGNATURES = {
     "i8mm_forward_workspace_bytes": (c_size, [c_i64, c_i64]),
     "i8mm_forward": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     "i8mm_forward_workspace_layout": (c_int, [c_i64, c_i64, ctypes.POINTER(c_size), ctypes.POINTER(c_i64)]),
+    "i8mm_forward_tensorwise": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
+    "i8mm_forward_zeropoint_workspace_bytes": (c_size, [c_i64, c_i64]),
+    "i8mm_forward_zeropoint": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                                       c_p]),
     "i8mm_version": (ctypes.c_char_p, []),
     "i8mm_status_string": (ctypes.c_char_p, [c_int]),
 }

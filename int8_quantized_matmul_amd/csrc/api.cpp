@@ -305,4 +305,77 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
     return launched(e);
 }
 
+i8mm_status i8mm_forward_tensorwise(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                    const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                    void* workspace, uint16_t* C, hipStream_t stream) {
+    if (!X || !Wq || !c_w || !workspace || !C) return I8MM_EINVAL;   // W and bias may be null
+    if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
+    if (std::isnan(alpha) || alpha < 0.0f) return I8MM_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(c_w) || !aligned16(W) || !aligned16(bias) ||
+        !aligned16(C))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    size_t off[7], total;
+    int64_t ldo;
+    forward_layout(s, h, off, &ldo, &total);
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* acc = reinterpret_cast<uint32_t*>(ws + off[0]);
+    int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[4]);
+    float* c_x = reinterpret_cast<float*>(ws + off[5]);
+    uint16_t* X_O = reinterpret_cast<uint16_t*>(ws + off[6]);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + off[2]);
+    int32_t* n_out = reinterpret_cast<int32_t*>(ws + off[3]);
+    int clear_words = 0;
+    hipError_t e = i8mm::launch_forward_prologue_variant(false, X, s, h, alpha, acc,
+                                                         reinterpret_cast<uint32_t*>(ws + off[1]), idx, n_out, Xq,
+                                                         c_x, nullptr, nullptr, X_O, ldo, stream, &clear_words);
+    if (e != hipSuccess) return I8MM_ELAUNCH;
+    e = i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s, h, o,
+                               C, stream, acc, clear_words);
+    return launched(e);
+}
+
+size_t i8mm_forward_zeropoint_workspace_bytes(int64_t s, int64_t h) {
+    if (!valid_shape_sh(s, h)) return 0;
+    size_t off[7], total;
+    int64_t ldo;
+    forward_layout(s, h, off, &ldo, &total);
+    return total + 2 * static_cast<size_t>(round_up(4 * s, 256));
+}
+
+i8mm_status i8mm_forward_zeropoint(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                   const int8_t* Wq, const float* nd_w, const int32_t* zp_w, const int32_t* colsum_w,
+                                   const uint16_t* W, const uint16_t* bias, void* workspace, uint16_t* C,
+                                   hipStream_t stream) {
+    if (!X || !Wq || !nd_w || !zp_w || !colsum_w || !W || !workspace || !C) return I8MM_EINVAL;   // bias may be null
+    if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
+    if (std::isnan(alpha) || alpha < 0.0f) return I8MM_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(nd_w) || !aligned16(zp_w) || !aligned16(colsum_w) ||
+        !aligned16(W) || !aligned16(bias) || !aligned16(C))
+        return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    size_t off[7], total;
+    int64_t ldo;
+    forward_layout(s, h, off, &ldo, &total);
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* acc = reinterpret_cast<uint32_t*>(ws + off[0]);
+    int8_t* Xq = reinterpret_cast<int8_t*>(ws + off[4]);
+    float* nd_x = reinterpret_cast<float*>(ws + off[5]);
+    uint16_t* X_O = reinterpret_cast<uint16_t*>(ws + off[6]);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + off[2]);
+    int32_t* n_out = reinterpret_cast<int32_t*>(ws + off[3]);
+    int32_t* zp_x = reinterpret_cast<int32_t*>(ws + total);
+    int32_t* rowsum_x = reinterpret_cast<int32_t*>(ws + total + round_up(4 * s, 256));
+    int clear_words = 0;
+    hipError_t e = i8mm::launch_forward_prologue_variant(true, X, s, h, alpha, acc,
+                                                         reinterpret_cast<uint32_t*>(ws + off[1]), idx, n_out, Xq,
+                                                         nd_x, zp_x, rowsum_x, X_O, ldo, stream, &clear_words);
+    if (e != hipSuccess) return I8MM_ELAUNCH;
+    e = i8mm::launch_int8_gemm(i8mm::GemmOut::ZeroPoint, Xq, nd_x, X_O, ldo, idx, n_out, Wq, nd_w, W, bias, s, h,
+                               o, C, stream, acc, clear_words, i8mm::ZpArgs{zp_x, rowsum_x, zp_w, colsum_w});
+    return launched(e);
+}
+
 }  // extern "C"

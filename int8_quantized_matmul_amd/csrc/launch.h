@@ -25,22 +25,38 @@ hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, floa
                                    uint32_t* mask, int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x,
                                    uint16_t* X_O, int64_t ldo, hipStream_t stream, int* clear_words);
 
+// The same for the tensor-wise (zeropoint = false; c_x receives the one
+// constant in every entry) or zeropoint (c_x receives nd_x; zp_x and
+// rowsum_x are written) row quantiser: detection into acc[0 .. h / 32),
+// then the scheme's row quantiser, whose first block writes the mask, the
+// index list and |O|.
+hipError_t launch_forward_prologue_variant(bool zeropoint, const uint16_t* X, int64_t s, int64_t h, float alpha,
+                                           uint32_t* acc, uint32_t* mask, int32_t* idx, int32_t* n_out, int8_t* Xq,
+                                           float* c_x, int32_t* zp_x, int32_t* rowsum_x, uint16_t* X_O, int64_t ldo,
+                                           hipStream_t stream, int* clear_words);
+
 hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
                                 int8_t* Wq, float* c_w, hipStream_t stream);
 
 // Tensor-wise absmax: one constant for all of X's non-outlier part (written
 // to every c_x[i]) or for all of W (every c_w[j]); same outputs otherwise.
+// If idx is non-null, the first pass also writes the index list and |O|
+// (and the mask to mask_out if that is non-null) from `mask`.
 hipError_t launch_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h, const uint32_t* mask, int8_t* Xq,
-                                      float* c_x, uint16_t* X_O, int64_t ldo, hipStream_t stream);
+                                      float* c_x, uint16_t* X_O, int64_t ldo, hipStream_t stream,
+                                      uint32_t* mask_out = nullptr, int32_t* idx = nullptr,
+                                      int32_t* n_out = nullptr);
 hipError_t launch_quantize_weights_tensorwise(const uint16_t* W, int64_t h, int64_t o, int8_t* Wq, float* c_w,
                                               hipStream_t stream);
 
 // Zeropoint quantisation: rows of X over the non-outlier columns (codes,
 // nd_x, zp_x, code sums over the row, X_O gather) and columns of W at load
 // time (panel codes, nd_w, zp_w, code sums over the column).
+// (idx, n_out, mask_out: as for launch_quantize_tensorwise.)
 hipError_t launch_quantize_rows_zp(const uint16_t* X, int64_t s, int64_t h, const uint32_t* mask, int8_t* Xq,
                                    float* nd_x, int32_t* zp_x, int32_t* rowsum_x, uint16_t* X_O, int64_t ldo,
-                                   hipStream_t stream);
+                                   hipStream_t stream, uint32_t* mask_out = nullptr, int32_t* idx = nullptr,
+                                   int32_t* n_out = nullptr);
 hipError_t launch_quantize_cols_zp(const uint16_t* W, int64_t h, int64_t o, int8_t* Wq, float* nd_w, int32_t* zp_w,
                                    int32_t* colsum_w, hipStream_t stream);
 

@@ -657,6 +657,21 @@ hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, floa
     return launch_rows(X, s, h, acc, mask, idx, n_out, Xq, c_x, X_O, ldo, stream);
 }
 
+hipError_t launch_forward_prologue_variant(bool zeropoint, const uint16_t* X, int64_t s, int64_t h, float alpha,
+                                           uint32_t* acc, uint32_t* mask, int32_t* idx, int32_t* n_out, int8_t* Xq,
+                                           float* c_x, int32_t* zp_x, int32_t* rowsum_x, uint16_t* X_O, int64_t ldo,
+                                           hipStream_t stream, int* clear_words) {
+    // Detection ORs the mask into acc[0 .. h / 32) (zero beforehand, cleared
+    // again by the product); the scheme's row quantiser reads it there and
+    // its block 0 writes the mask, the index list and |O|.
+    *clear_words = static_cast<int>(h / 32);
+    hipError_t e = launch_detect_into(X, s, h, alpha, acc, stream);
+    if (e != hipSuccess) return e;
+    if (zeropoint)
+        return launch_quantize_rows_zp(X, s, h, acc, Xq, c_x, zp_x, rowsum_x, X_O, ldo, stream, mask, idx, n_out);
+    return launch_quantize_tensorwise(X, s, h, acc, Xq, c_x, X_O, ldo, stream, mask, idx, n_out);
+}
+
 hipError_t launch_pack_fp16_panels(const uint16_t* W, int64_t h, int64_t o, uint16_t* Wp, hipStream_t stream) {
     hipLaunchKernelGGL(k_pack_fp16_panels, dim3(static_cast<unsigned>(o / 64), static_cast<unsigned>(h / 32)),
                        dim3(256), 0, stream, W, o, Wp);
@@ -671,7 +686,8 @@ hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
 }
 
 hipError_t launch_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h, const uint32_t* mask, int8_t* Xq,
-                                      float* c_x, uint16_t* X_O, int64_t ldo, hipStream_t stream) {
+                                      float* c_x, uint16_t* X_O, int64_t ldo, hipStream_t stream,
+                                      uint32_t* mask_out, int32_t* idx, int32_t* n_out) {
     // row maxima into c_x, one constant over them, then the codes with it
     const size_t dyn = static_cast<size_t>(2 * (h / 32) * 4);
     const int64_t per_lane4 = (h / 8 + 255) / 256;   // chunks per lane with 4 wavefronts per row
@@ -680,7 +696,7 @@ hipError_t launch_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h, c
         const dim3 grid(static_cast<unsigned>(s)), block(256);
 #define I8MM_TW(CPL)                                                                                         \
     hipLaunchKernelGGL((k_quant_rows<CPL, RowScale::MaxOnly, 4>), grid, block, dyn, stream, X, s, h, mask,    \
-                       nullptr, nullptr, nullptr, Xq, c_x, X_O, ldo);                                         \
+                       mask_out, idx, n_out, Xq, c_x, X_O, ldo);                                              \
     hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(1024), 0, stream, c_x, s);                              \
     hipLaunchKernelGGL((k_quant_rows<CPL, RowScale::Given, 4>), grid, block, dyn, stream, X, s, h, mask,      \
                        nullptr, nullptr, nullptr, Xq, c_x, X_O, ldo)
@@ -692,8 +708,8 @@ hipError_t launch_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h, c
         return hipGetLastError();
     }
     const dim3 grid(static_cast<unsigned>((s + 3) / 4)), block(256);
-    hipLaunchKernelGGL((k_quant_rows<0, RowScale::MaxOnly>), grid, block, dyn, stream, X, s, h, mask, nullptr,
-                       nullptr, nullptr, Xq, c_x, X_O, ldo);
+    hipLaunchKernelGGL((k_quant_rows<0, RowScale::MaxOnly>), grid, block, dyn, stream, X, s, h, mask, mask_out,
+                       idx, n_out, Xq, c_x, X_O, ldo);
     hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(1024), 0, stream, c_x, s);
     hipLaunchKernelGGL((k_quant_rows<0, RowScale::Given>), grid, block, dyn, stream, X, s, h, mask, nullptr,
                        nullptr, nullptr, Xq, c_x, X_O, ldo);

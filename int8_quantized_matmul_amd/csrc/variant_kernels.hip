@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void k_quant_rows_zp(const uint16_t* __restric
                                                        const uint32_t* __restrict__ mask, int8_t* __restrict__ Xq,
                                                        float* __restrict__ nd_x, int32_t* __restrict__ zp_x,
                                                        int32_t* __restrict__ rowsum_x, uint16_t* __restrict__ X_O,
-                                                       int64_t ldo) {
+                                                       int64_t ldo, uint32_t* __restrict__ mask_out,
+                                                       int32_t* __restrict__ idx, int32_t* __restrict__ n_out) {
     extern __shared__ uint32_t dyn[];
     __shared__ int wsum[4];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
@@ -77,6 +78,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_zp(const uint16_t* __restric
     for (int w = t; w < nw; w += 256) smask[w] = mask[w];
     __syncthreads();
     const int n = block_mask_prefix(smask, pre, nw, wsum, 256);
+    if (blockIdx.x == 0 && idx != nullptr) emit_outlier_set(smask, pre, nw, n, mask_out, idx, n_out, 256);
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + wid;
     if (i >= s) return;
 
@@ -140,14 +142,18 @@ __global__ __launch_bounds__(256) void k_quant_rows_zp(const uint16_t* __restric
 // read once, the outlier values go to X_O straight from the registers, min
 // and max exclude the outlier columns, and the parts of a row meet in LDS
 // for min, max and the code sum. The codes are those of k_quant_rows_zp
-// (same zeropoint_of / zeropoint_code). Dynamic LDS: nw mask words + nw
-// prefix counts.
+// (same zeropoint_of / zeropoint_code). If idx is non-null, block 0 also
+// writes the index list and |O| (and the mask to mask_out if that is
+// non-null), as the absmax row quantiser does. Dynamic LDS: nw mask words +
+// nw prefix counts.
 template <int CPL, int WPR>
 __global__ __launch_bounds__(256) void k_quant_rows_zp_reg(const uint16_t* __restrict__ X, int64_t s, int64_t h,
                                                            const uint32_t* __restrict__ mask,
                                                            int8_t* __restrict__ Xq, float* __restrict__ nd_x,
                                                            int32_t* __restrict__ zp_x, int32_t* __restrict__ rowsum_x,
-                                                           uint16_t* __restrict__ X_O, int64_t ldo) {
+                                                           uint16_t* __restrict__ X_O, int64_t ldo,
+                                                           uint32_t* __restrict__ mask_out, int32_t* __restrict__ idx,
+                                                           int32_t* __restrict__ n_out) {
     extern __shared__ uint32_t dyn[];
     __shared__ int wsum[4];
     __shared__ float part_lo[4], part_hi[4];
@@ -175,6 +181,7 @@ __global__ __launch_bounds__(256) void k_quant_rows_zp_reg(const uint16_t* __res
     for (int w = t + 256; w < nw; w += 256) smask[w] = mask[w];   // h > 8192
     __syncthreads();
     const int n = block_mask_prefix(smask, pre, nw, wsum, 256);
+    if (blockIdx.x == 0 && idx != nullptr) emit_outlier_set(smask, pre, nw, n, mask_out, idx, n_out, 256);
 
     uint16_t* orow = X_O + i * ldo;
     auto bits_of = [&](int64_t c) { return (smask[c >> 2] >> ((c & 3) * 8)) & 0xffu; };
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(256) void k_quant_cols_zp(const uint16_t* __restric
 
 hipError_t launch_quantize_rows_zp(const uint16_t* X, int64_t s, int64_t h, const uint32_t* mask, int8_t* Xq,
                                    float* nd_x, int32_t* zp_x, int32_t* rowsum_x, uint16_t* X_O, int64_t ldo,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, uint32_t* mask_out, int32_t* idx, int32_t* n_out) {
     const size_t dyn = static_cast<size_t>(2 * (h / 32) * 4);
     // Wavefronts per row as for the absmax row quantiser: ~4096 wavefronts
     // in all while each holds at most 16 chunks of its row.
@@ -354,13 +361,13 @@ hipError_t launch_quantize_rows_zp(const uint16_t* X, int64_t s, int64_t h, cons
     if (per_lane > 16) {
         // long rows: one wavefront per row reading it twice
         hipLaunchKernelGGL(k_quant_rows_zp, dim3(static_cast<unsigned>((s + 3) / 4)), dim3(256), dyn, stream, X, s,
-                           h, mask, Xq, nd_x, zp_x, rowsum_x, X_O, ldo);
+                           h, mask, Xq, nd_x, zp_x, rowsum_x, X_O, ldo, mask_out, idx, n_out);
         return hipGetLastError();
     }
     const dim3 grid(static_cast<unsigned>((s + 4 / wpr - 1) / (4 / wpr))), block(256);
 #define I8MM_ZPROWS(CPL, W)                                                                                      \
     hipLaunchKernelGGL((k_quant_rows_zp_reg<CPL, W>), grid, block, dyn, stream, X, s, h, mask, Xq, nd_x, zp_x,    \
-                       rowsum_x, X_O, ldo)
+                       rowsum_x, X_O, ldo, mask_out, idx, n_out)
 #define I8MM_ZPROWS_W(W)                                 \
     if (per_lane <= 2) I8MM_ZPROWS(2, W);                \
     else if (per_lane <= 4) I8MM_ZPROWS(4, W);           \

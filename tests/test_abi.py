@@ -82,6 +82,25 @@ def test_forward_rejects_unaligned_workspace():
     assert lib.i8mm_forward(P, 4, 64, 64, 6.0, P, P, P, MIS, ctypes.c_void_p(1 << 20), P, None) == -1
 
 
+def test_variant_forwards_reject():
+    lib = _lib()
+    ws = ctypes.c_void_p(1 << 20)
+    # unaligned workspace, misaligned bias, null weights
+    assert lib.i8mm_forward_tensorwise(P, 4, 64, 64, 6.0, P, P, P, None, ctypes.c_void_p((1 << 20) + 16), P,
+                                       None) == -1
+    assert lib.i8mm_forward_tensorwise(P, 4, 64, 64, 6.0, P, P, P, MIS, ws, P, None) == -1
+    assert lib.i8mm_forward_tensorwise(P, 4, 64, 64, 6.0, None, P, P, None, ws, P, None) == -1
+    assert lib.i8mm_forward_tensorwise(P, 4, 64, 64, float("nan"), P, P, P, None, ws, P, None) == -1
+    # zeropoint: W is required; bad shape; NaN alpha
+    assert lib.i8mm_forward_zeropoint(P, 4, 64, 64, 6.0, P, P, P, P, None, None, ws, P, None) == -1
+    assert lib.i8mm_forward_zeropoint(P, 4, 96, 64, 6.0, P, P, P, P, P, None, ws, P, None) == -1
+    assert lib.i8mm_forward_zeropoint(P, 4, 64, 64, -1.0, P, P, P, P, P, None, ws, P, None) == -1
+    for s, h in [(1, 64), (2048, 4096), (3, 133120)]:
+        extra = 2 * ((4 * s + 255) // 256 * 256)
+        assert lib.i8mm_forward_zeropoint_workspace_bytes(s, h) == lib.i8mm_forward_workspace_bytes(s, h) + extra
+    assert lib.i8mm_forward_zeropoint_workspace_bytes(0, 64) == 0
+
+
 def test_forward_workspace_layout():
     lib = _lib()
     for s, h in [(1, 64), (16, 256), (2048, 4096), (4096, 12288), (3, 133120)]:

@@ -177,3 +177,54 @@ def test_tensorwise_rows_every_launch_shape(s, h, label):
     assert np.array_equal(H(Xq), Xq_r), "tensor-wise Xq differs"
     assert np.array_equal(H(c_x).view(np.uint32), cx_r.view(np.uint32)), "tensor-wise c_x differs"
     _check_XO(X_O, XO_r)
+
+
+@pytest.mark.parametrize("seed,s,h,o,nout,alpha", SHAPES, ids=IDS)
+def test_one_call_variant_forwards(seed, s, h, o, nout, alpha):
+    """forward_tensorwise / forward_zeropoint (detection accumulated in the
+    workspace, the quantiser writing the index list) give the separate calls'
+    C bit for bit, and the oracle's within the bar."""
+    inp = random_case(280 + seed, s, h, o, nout, row_frac=0.5)
+    X, W = inp["X"].copy(), inp["W"]
+    X[: s // 2] += np.float16(0.75)                    # shifted rows for the zero points
+    b = (np.random.default_rng(seed).standard_normal(o) * 0.5).astype(np.float16) if seed % 2 else None
+    Xd, Wd = T(X), T(W)
+    bd = T(b) if b is not None else None
+    say(f"  launch: one-call tensor-wise / zeropoint s={s} h={h} o={o} |O|={nout} alpha={alpha}")
+    wt = i8.quantize_weights(Wd, "tensor")
+    wz = i8.quantize_weights(Wd, "zeropoint")
+    Ct = i8.forward_tensorwise(Xd, wt[0], wt[1], Wd, alpha, bias=bd)
+    Cz = i8.forward_zeropoint(Xd, wz, Wd, alpha, bias=bd)
+    Ct_sep = i8.variant_forward(Xd, wt, Wd, "tensor", alpha, bias=bd)
+    Cz_sep = i8.variant_forward(Xd, wz, Wd, "zeropoint", alpha, bias=bd)
+    torch.cuda.synchronize()
+    assert torch.equal(Ct, Ct_sep), "one-call tensor-wise forward differs from the separate calls"
+    assert torch.equal(Cz, Cz_sep), "one-call zeropoint forward differs from the separate calls"
+    check_C(Ct, oracle.variant_forward(X, W, "tensor", alpha, bias=b))
+    check_C(Cz, oracle.variant_forward(X, W, "zeropoint", alpha, bias=b))
+
+
+def test_one_call_forwards_share_a_workspace():
+    """One workspace, sized for the largest zeropoint case, serves every
+    one-call forward in turn, across shapes and both prologue paths (the
+    accumulator must come back to zero after each)."""
+    seq = [("zeropoint", 300, 640, 320), ("vector", 8, 1024, 256), ("tensor", 40, 512, 192),
+           ("zeropoint", 5, 1024, 128), ("vector", 260, 640, 576), ("tensor", 3, 192, 64),
+           ("zeropoint", 17, 192, 320)]
+    ws = i8.forward_workspace(300, 1024, DEV, zeropoint=True)
+    for k, (scheme, s, h, o) in enumerate(seq):
+        inp = random_case(300 + k, s, h, o, 3, row_frac=0.5)
+        Xd, Wd = T(inp["X"]), T(inp["W"])
+        say(f"  launch: shared workspace {scheme} s={s} h={h} o={o}")
+        qw = i8.quantize_weights(Wd, scheme)
+        if scheme == "zeropoint":
+            C = i8.forward_zeropoint(Xd, qw, Wd, workspace=ws)
+        elif scheme == "tensor":
+            C = i8.forward_tensorwise(Xd, qw[0], qw[1], Wd, workspace=ws)
+        else:
+            C = i8.forward(Xd, qw[0], qw[1], Wd, workspace=ws)
+        C_sep = i8.variant_forward(Xd, qw, Wd, scheme)
+        torch.cuda.synchronize()
+        assert torch.equal(C, C_sep), f"{scheme} call {k} differs from the separate calls"
+    acc = H(ws[: i8.ACC_BYTES])
+    assert not acc.any(), "the accumulator is not zero after the calls"
