@@ -11,7 +11,6 @@ import os
 import re
 import subprocess
 
-import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "int8_quantized_matmul_amd", "csrc", "gemm_kernels.hip")

@@ -11,7 +11,6 @@ Page tags: [TM] transformer-math LLM.int8() tutorial (aicassindra.com);
 """
 
 import json
-import math
 import os
 from fractions import Fraction
 
