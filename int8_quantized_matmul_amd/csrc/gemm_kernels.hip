@@ -273,11 +273,15 @@ __device__ __forceinline__ void store_staged_block(const uint16_t* out_st, uint1
     const uint32_t col = static_cast<uint32_t>(ocol0) + (lane & 15) * 8;
     const bool col_ok = col < o32;
     const uint32_t off0 = ((lane >> 4) * o32 + col) * 2;
+    // all eight LDS reads first, so that their latencies overlap
+    v4i v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = *reinterpret_cast<const v4i*>(out_st + (4 * i + (lane >> 4)) * kOutRow + (lane & 15) * 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const v4i v = *reinterpret_cast<const v4i*>(out_st + (4 * i + (lane >> 4)) * kOutRow + (lane & 15) * 8);
         const uint32_t off = col_ok ? off0 + static_cast<uint32_t>(i) * 8 * o32 : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rC, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v[i]), rC, off, 0, 0);
     }
 }
 
@@ -506,7 +510,9 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                         make_uint2(lo, hi);
                 }
             }
-            store_staged_block(out_st, C, s0 + ws * 128 + sb * 32, o0 + wo * 128, s, o, lane);
+            // row and column origin through scalar registers (uniform descriptor)
+            store_staged_block(out_st, C, s0 + __builtin_amdgcn_readfirstlane(ws) * 128 + sb * 32,
+                               o0 + __builtin_amdgcn_readfirstlane(wo) * 128, s, o, lane);
         }
     } else if constexpr (MODE == GemmOut::Int32) {
         int32_t* C = static_cast<int32_t*>(Cout);
@@ -605,9 +611,13 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         // The lane's indices are derived again here from an opaque copy of
         // the thread index: left to the compiler, it computed them before
         // the K loop and carried them (or spilled them) across it.
+        // The wavefront index goes to a scalar register, so that the output
+        // descriptor and the LDS bases built from it are known to be uniform
+        // (a descriptor in vector registers costs a loop around every store).
         int te = static_cast<int>(threadIdx.x);
         asm volatile("" : "+v"(te));
-        const int lane = te & 63, wid = te >> 6, wo = wid & 1, ws = wid >> 1, r32 = lane & 31, khalf = lane >> 5;
+        const int lane = te & 63, wid = __builtin_amdgcn_readfirstlane(te >> 6), wo = wid & 1, ws = wid >> 1,
+                  r32 = lane & 31, khalf = lane >> 5;
         uint16_t* out_st = wid < 3 ? reinterpret_cast<uint16_t*>(A1) + wid * kOutWave : reinterpret_cast<uint16_t*>(B1);
         const float* inv_rows = scl + ws * 128;
         const float* invw = scl + 256 + wo * 128;

@@ -173,7 +173,10 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
     extern __shared__ uint32_t dyn[];
     __shared__ int wsum[4];
     __shared__ uint32_t part_max[4];
-    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    // wavefront index in a scalar register: the row's buffer descriptor is
+    // then known to be uniform (in vector registers it costs a loop around
+    // every load)
+    const int t = threadIdx.x, lane = t & 63, wid = __builtin_amdgcn_readfirstlane(t >> 6);
     const int part = wid % WPR;
     const int nw = static_cast<int>(h / 32);
     uint32_t* smask = dyn;

@@ -158,7 +158,8 @@ __global__ __launch_bounds__(256) void k_quant_rows_zp_reg(const uint16_t* __res
     __shared__ int wsum[4];
     __shared__ float part_lo[4], part_hi[4];
     __shared__ int part_sum[4];
-    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    // wavefront index in a scalar register (uniform row descriptor)
+    const int t = threadIdx.x, lane = t & 63, wid = __builtin_amdgcn_readfirstlane(t >> 6);
     const int part = wid % WPR;
     const int nw = static_cast<int>(h / 32);
     uint32_t* smask = dyn;
