@@ -5,7 +5,17 @@ if the compiler ever demotes them to scratch memory (for instance when an
 epilogue path grows enough to stop the unrolling that keeps their indices
 constant), the kernels still compute the right result but run several times
 slower. The code-object metadata shows it as a large private segment.
+
+Buffer loads and stores take their resource descriptor in scalar registers.
+When the compiler cannot prove a descriptor uniform across the wavefront
+(for instance when it is built from a wavefront index held in a vector
+register), it wraps each such access in a loop over the distinct
+descriptors: read one lane's descriptor, compare it with every lane's
+(a 64-bit scalar/vector compare), run the access for the matching lanes,
+repeat. The result is still right, but every access pays the loop.
 """
+
+import functools
 
 import os
 import re
@@ -13,14 +23,30 @@ import subprocess
 
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "int8_quantized_matmul_amd", "csrc", "gemm_kernels.hip")
+CSRC = os.path.join(ROOT, "int8_quantized_matmul_amd", "csrc")
+SRC = os.path.join(CSRC, "gemm_kernels.hip")
+
+
+@functools.lru_cache(maxsize=None)
+def _assembly(src):
+    from int8_quantized_matmul_amd import build
+    flags = [f for f in build.HIP_FLAGS if f != "-fPIC"]
+    return subprocess.run([build._hipcc(), *flags, "--cuda-device-only", "-S", "-o", "-", src],
+                          capture_output=True, text=True, check=True).stdout
+
+
+def _kernel_bodies(src):
+    out = _assembly(src)
+    starts = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\S+):", out, re.M)]
+    bodies = {}
+    for i, (pos, name) in enumerate(starts):
+        end = starts[i + 1][0] if i + 1 < len(starts) else len(out)
+        bodies[name] = out[pos:end].split(".Lfunc_end")[0]
+    return bodies
 
 
 def _kernel_metadata():
-    from int8_quantized_matmul_amd import build
-    flags = [f for f in build.HIP_FLAGS if f != "-fPIC"]
-    out = subprocess.run([build._hipcc(), *flags, "--cuda-device-only", "-S", "-o", "-", SRC],
-                         capture_output=True, text=True, check=True).stdout
+    out = _assembly(SRC)
     meta = {}
     for block in re.split(r"\n\s+- \.", out):
         name = re.search(r"\.name:\s+(\S+)", block)
@@ -36,3 +62,21 @@ def test_product_kernels_keep_accumulators_in_registers():
     assert len(gemm) >= 5, sorted(meta)
     big = {k: v for k, v in gemm.items() if v > 128}
     assert not big, f"kernels with scratch-resident arrays: {big}"
+
+
+# A 64-bit compare of a scalar register pair with a vector register pair: the
+# test at the head of a loop over distinct buffer descriptors.
+_DESCRIPTOR_LOOP = re.compile(r"v_cmp_eq_u64_e(?:32|64)\s+\S+,\s*s\[\d+:\d+\],\s*v\[\d+:\d+\]")
+
+
+def test_hot_kernels_use_uniform_buffer_descriptors():
+    checked = {}
+    for src, pats in (("gemm_kernels.hip", ("k_gemm_prefill", "k_gemm_decode")),
+                      ("quant_kernels.hip", ("k_quant_rows", "k_detect", "k_small_")),
+                      ("variant_kernels.hip", ("k_quant_rows_zp",))):
+        for name, body in _kernel_bodies(os.path.join(CSRC, src)).items():
+            if any(p in name for p in pats):
+                checked[name] = len(_DESCRIPTOR_LOOP.findall(body))
+    assert len(checked) >= 20, sorted(checked)
+    looped = {k: v for k, v in checked.items() if v}
+    assert not looped, f"kernels with per-access descriptor loops: {looped}"
