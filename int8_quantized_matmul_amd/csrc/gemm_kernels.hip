@@ -82,9 +82,10 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // a per-lane offset past every 
 // Block -> output tile. Blocks are dealt to the 8 XCDs round robin
 // (block b runs on XCD b % 8); each XCD is given one contiguous run of the
 // s-fastest tile order so that the tiles sharing weight columns and rows of
-// Xq meet in the same 4 MiB L2.
-__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t nb) {
-    const int64_t q = nb / 8, r = nb % 8, x = b % 8, i = b / 8;
+// Xq meet in the same 4 MiB L2. Block and tile indices are 32-bit (as the
+// grid is), which keeps the index arithmetic short ahead of the first loads.
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t nb) {
+    const uint32_t q = nb / 8, r = nb % 8, x = b % 8, i = b / 8;
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
 
@@ -314,8 +315,10 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     const int wu = __builtin_amdgcn_readfirstlane(wid);
     const int wo = wid & 1, ws = wid >> 1;
     const int r32 = lane & 31, khalf = lane >> 5;
-    const int64_t n_ts = (s + kTS - 1) / kTS;
-    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    // 32-bit division (a 64-bit one is a long scalar sequence that would
+    // delay the first loads): tile < gridDim.x and n_ts < 2^32
+    const uint32_t n_ts = static_cast<uint32_t>((s + kTS - 1) / kTS);
+    const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t ts_i = tile % n_ts, to_i = tile / n_ts;
     const int64_t o0 = to_i * kTO, s0 = ts_i * kTS;
     const int64_t o_rows = o - o0 < kTO ? o - o0 : kTO;

@@ -74,7 +74,9 @@ __global__ __launch_bounds__(256) void k_detect(const uint16_t* __restrict__ X, 
     __shared__ uint32_t words[16];
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     if (t < 16) words[t] = 0u;
-    const int64_t strip = blockIdx.x % n_strips, rb = blockIdx.x / n_strips;
+    // 32-bit division (the grid is 32-bit): short ahead of the loads
+    const uint32_t ns32 = static_cast<uint32_t>(n_strips);
+    const int64_t strip = blockIdx.x % ns32, rb = blockIdx.x / ns32;
     const int64_t col = strip * 512 + lane * 8;
     const int64_t r0 = rb * kDetRows + wid * 8;
     uint32_t flags = 0;
