@@ -89,15 +89,17 @@ def outlier_columns(X_f16: np.ndarray, alpha: float = 6.0) -> Tuple[np.ndarray, 
     [DIGEST] "Mixed-Precision Decomposition", formal definition of O;
     [PY] "第二件武器：混合精度分解" (threshold alpha = 6.0).
     Readings: ">=" (the digest's wording) rather than "exceeds"; the index range
-    is 0 <= j < h. Returns (mask u32[ceil(h/32)], idx int32 ascending, |O|).
+    is 0 <= j < h. A column is in O when some element of it reaches alpha,
+    tested element by element, so a NaN elsewhere in the column neither adds
+    nor removes it. Returns (mask u32[ceil(h/32)], idx int32 ascending, |O|).
     """
     X32 = np.asarray(X_f16, dtype=np.float16).astype(F32)
     s, h = X32.shape
     if s == 0:
         idx = np.zeros(0, dtype=np.int32)
     else:
-        col_absmax = np.abs(X32).max(axis=0)
-        idx = np.nonzero(col_absmax >= F32(alpha))[0].astype(np.int32)
+        reaches = np.abs(X32) >= F32(alpha)          # False for NaN
+        idx = np.nonzero(reaches.any(axis=0))[0].astype(np.int32)
     return mask_from_indices(idx, h), idx, int(idx.size)
 
 

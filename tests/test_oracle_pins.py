@@ -166,6 +166,24 @@ def test_alpha_tie_is_outlier():
     assert mask.tolist() == [(1 << 5) | (1 << 9), 0]
 
 
+def test_outlier_set_is_elementwise_with_nan():
+    """[DIGEST] 'The Full LLM.int8() Algorithm', Step 1: a column is in O when
+    one of its elements reaches alpha. A NaN in the same column must not hide
+    that element, and a NaN alone does not reach alpha (brute force over the
+    elements in plain Python)."""
+    X = np.zeros((4, 64), np.float16)
+    X[0, 3] = np.nan
+    X[2, 3] = 10.0            # NaN and an outlier: in O
+    X[1, 7] = np.nan          # NaN only: not in O
+    X[3, 20] = -np.nan
+    X[0, 20] = 5.99609375     # NaN and a near miss: not in O
+    X[3, 33] = -6.0           # plain outlier: in O
+    _, idx, n = oracle.outlier_columns(X, 6.0)
+    brute = [j for j in range(64) if any(abs(float(X[i, j])) >= 6.0 for i in range(4))]
+    assert brute == [3, 33]
+    assert idx.tolist() == brute and n == 2
+
+
 def test_outlier_column_excluded_from_row_absmax():
     """[DIGEST] Step 4: the row constant is over X^{not O} only. In row 1 the
     outlier column holds 2.0 (< alpha) but it must not set the row absmax."""
