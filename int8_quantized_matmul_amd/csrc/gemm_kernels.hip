@@ -498,6 +498,11 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         // fp32 accumulators rounded once to fp16, staged per 32-row block and
         // written as full 256-byte rows.
         uint16_t* C = static_cast<uint16_t*>(Cout);
+        // The last stage's loads of the stage after it (all out of range)
+        // still write zeros into a stage buffer, and the barrier's fence
+        // does not wait for direct-to-LDS loads: wait for them before any
+        // wavefront reuses the buffers.
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         __syncthreads();   // every wavefront is done with the stage buffers
         uint16_t* out_st = wid < 3 ? reinterpret_cast<uint16_t*>(A1) + wid * kOutWave : reinterpret_cast<uint16_t*>(B1);
 #pragma unroll
@@ -536,6 +541,9 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             }
     } else {
         uint16_t* C = static_cast<uint16_t*>(Cout);
+        // As above: the last stage's out-of-range loads must have landed
+        // before the stage buffers take slices, staging, bias and scales.
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         __syncthreads();   // every wavefront is done with the stage buffers
         // Epilogue LDS: extra outlier slices q = 1, 2 in A0, 3, 4 in B0 and
         // 5 in B1; output staging of waves 0-2 in A1, followed there by the
