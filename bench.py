@@ -8,17 +8,22 @@ fused dequantise + fp16 outlier epilogue. Weights are converted once at load
 time (timed separately, not part of a step).
 
 Prints ONE JSON line. `value` is the effective throughput 2*s*h*o / t_step
-(TOPS) on the OPT-6.7B-style FFN expansion prefill layer
-(X [2048, 4096], W [4096, 16384], 6 outlier columns in 75% of rows).
-`roofline` is the product kernel against the MI355X dense int8 MFMA peak;
-`decode` reports the weight-streaming GB/s of the 175B-style FFN expansion
-decode layer (X [8, 12288], W [12288, 49152]) against 8 TB/s HBM;
-`cpu_baseline` times the CPU oracle on host cores.
+(TOPS) on the largest layer, the 175B-style fused QKV projection prefill
+(X [4096, 12288], W [12288, 36864], 7 outlier columns in 75% of rows).
+`roofline` is the product kernel on that layer against the MI355X dense int8
+MFMA peak; `decode` reports the weight-streaming GB/s of the 175B-style FFN
+expansion decode layer (X [8, 12288], W [12288, 49152]) against 8 TB/s HBM;
+`all_configs` times every other workload (tiny, the OPT-6.7B-style FFN
+prefill and the nine outlier-density sweep points), each with its own CPU
+oracle baseline; `cpu_baseline` times the CPU oracle on host cores on a
+bounded sample of the headline layer; `clocks` are the GPU clocks sampled
+during the timed steps.
 """
 
 from __future__ import annotations
 
 import argparse
+import contextlib
 import json
 import os
 import sys
@@ -153,7 +158,7 @@ def table5_set(i8, torch, X, W, Wq, c_w, alpha, n, ws=None):
     }
 
 
-def run_prefill(i8, torch, w, steps, warmup, dev):
+def run_prefill(i8, torch, w, steps, warmup, dev, clocks=None, extras=True):
     from workloads import make_inputs
     inp = make_inputs(w)
     X = torch.from_numpy(inp["X"]).to(dev)
@@ -185,19 +190,24 @@ def run_prefill(i8, torch, w, steps, warmup, dev):
         step()
     torch.cuda.synchronize()
     t0, t1 = _events(torch)
-    wall0 = time.perf_counter()
-    t0.record()
-    for _ in range(steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    with clocks if clocks is not None else contextlib.nullcontext():
+        wall0 = time.perf_counter()
+        t0.record()
+        for _ in range(steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
     step_ms = t0.elapsed_time(t1) / steps
-    gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
-        v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
+    with clocks if clocks is not None else contextlib.nullcontext():
+        gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
+            v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
 
     n_out = int(v["n_out"].cpu()[0])
     pct = step_percentiles(torch, steps, step)
+    if not extras:
+        return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out, inputs=inp,
+                    pct=pct)
     table5 = table5_set(i8, torch, X, W, Wq, c_w, w.alpha, steps)
     # MALL-cold steps: rotate over weight copies whose total exceeds the
     # 256 MB Infinity Cache, so every step streams its weights from HBM
@@ -223,12 +233,11 @@ def run_prefill(i8, torch, w, steps, warmup, dev):
                 inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies, w8=w8, quant=quant)
 
 
-def run_decode(i8, torch, w, steps, warmup, dev):
+def run_decode(i8, torch, w, steps, warmup, dev, extras=True):
     from workloads import make_inputs
     inp = make_inputs(w)
     X = torch.from_numpy(inp["X"]).to(dev)
     W = torch.from_numpy(inp["W"]).to(dev)
-    del inp
     s, h, o = w.s, w.h, w.o
     Wq, c_w = i8.quantize_colwise_weights(W)
     ws = i8.forward_workspace(s, h, dev)
@@ -249,10 +258,13 @@ def run_decode(i8, torch, w, steps, warmup, dev):
         v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
     n_out = int(v["n_out"].cpu()[0])
     weight_bytes = h * o + 2 * n_out * o + 4 * o
+    if not extras:
+        return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, inputs=inp)
     w8 = variant_ms(i8, torch, steps, X, Wq, c_w, W, w.alpha, ws, C)
     del Wq, c_w
     quant = quantiser_variants(i8, torch, steps, X, W, w.alpha, w8["base"])
-    return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, w8=w8, quant=quant)
+    return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, w8=w8, quant=quant,
+                inputs=inp)
 
 
 def quantiser_variants(i8, torch, steps, X, W, alpha, fused_ms):
@@ -342,89 +354,239 @@ def run_table5(i8, torch, dev, s, n):
     return rows
 
 
-def run_all_configs(i8, torch, dev, steps):
-    """The one-call forward step and the product kernel alone on every
+def config_row(w, n_out, step_ms, gemm_ms):
+    """One workload's step and product-kernel figures in the metric's units:
+    effective TOPS (2 s h o / step) for prefill shapes, weight bytes per
+    second for the weight-streaming one."""
+    s, h, o = w.s, w.h, w.o
+    row = {"workload": w.name, "s": s, "h": h, "o": o, "n_outliers": n_out, "outlier_row_frac": w.row_frac,
+           "step_ms": round(step_ms, 5), "product_kernel_ms": round(gemm_ms, 5)}
+    if w.decode:
+        wb = h * o + 2 * n_out * o + 4 * o
+        row["weight_GB_per_s"] = round(wb / (step_ms * 1e-3) / 1e9, 1)
+        row["pct_hbm_peak"] = round(100 * wb / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
+        row["product_kernel_weight_GB_per_s"] = round(wb / (gemm_ms * 1e-3) / 1e9, 1)
+    else:
+        tops = 2.0 * s * h * o / (step_ms * 1e-3) / 1e12
+        gemm_tops = 2.0 * s * (h - n_out) * o / (gemm_ms * 1e-3) / 1e12
+        row["effective_TOPS"] = round(tops, 1)
+        row["pct_int8_peak"] = round(100 * tops / INT8_PEAK_TOPS, 2)
+        row["product_kernel_TOPS"] = round(gemm_tops, 1)
+        row["product_kernel_pct_peak"] = round(100 * gemm_tops / INT8_PEAK_TOPS, 2)
+    return row
+
+
+def run_all_configs(i8, torch, dev, steps, names, host=None, cpu_budget=0.0):
+    """The one-call forward step and the product kernel alone on each named
     configuration's seeded inputs (the parity tests' inputs), weights
-    converted beforehand: effective TOPS (2 s h o / step) for the prefill
-    shapes, weight bytes per second for the weight-streaming one."""
-    from workloads import CONFIGS, make_inputs
+    converted beforehand, each with a CPU oracle baseline on a bounded
+    sample when cpu_budget > 0. The next configuration's inputs are drawn in
+    a background thread while the current one is timed."""
+    from concurrent.futures import ThreadPoolExecutor
+    from workloads import get_config, make_inputs
     rows = []
-    for name, w in CONFIGS.items():
-        inp = make_inputs(w)
-        X = torch.from_numpy(inp["X"]).to(dev)
-        W = torch.from_numpy(inp["W"]).to(dev)
-        del inp
-        s, h, o = w.s, w.h, w.o
-        Wq, c_w = i8.quantize_colwise_weights(W)
-        ws = i8.forward_workspace(s, h, dev)
-        v = i8.forward_workspace_views(ws, s, h)
-        C = torch.empty((s, o), dtype=torch.float16, device=dev)
+    with ThreadPoolExecutor(1) as pool:
+        pending = pool.submit(make_inputs, get_config(names[0])) if names else None
+        for k, name in enumerate(names):
+            w = get_config(name)
+            inp = pending.result()
+            pending = pool.submit(make_inputs, get_config(names[k + 1])) if k + 1 < len(names) else None
+            X = torch.from_numpy(inp["X"]).to(dev)
+            W = torch.from_numpy(inp["W"]).to(dev)
+            s, h, o = w.s, w.h, w.o
+            Wq, c_w = i8.quantize_colwise_weights(W)
+            ws = i8.forward_workspace(s, h, dev)
+            v = i8.forward_workspace_views(ws, s, h)
+            C = torch.empty((s, o), dtype=torch.float16, device=dev)
 
-        def step():
-            i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C)
+            def step():
+                i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C)
 
-        settle(torch, step)
-        step_ms = timed_ms(torch, steps, step)
-        gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
-            v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
-        n_out = int(v["n_out"].cpu()[0])
-        row = {"workload": name, "s": s, "h": h, "o": o, "n_outliers": n_out, "outlier_row_frac": w.row_frac,
-               "step_ms": round(step_ms, 5), "product_kernel_ms": round(gemm_ms, 5)}
-        if w.decode:
-            wb = h * o + 2 * n_out * o + 4 * o
-            row["weight_GB_per_s"] = round(wb / (step_ms * 1e-3) / 1e9, 1)
-            row["pct_hbm_peak"] = round(100 * wb / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)
-            row["product_kernel_weight_GB_per_s"] = round(wb / (gemm_ms * 1e-3) / 1e9, 1)
-        else:
-            tops = 2.0 * s * h * o / (step_ms * 1e-3) / 1e12
-            gemm_tops = 2.0 * s * (h - n_out) * o / (gemm_ms * 1e-3) / 1e12
-            row["effective_TOPS"] = round(tops, 1)
-            row["pct_int8_peak"] = round(100 * tops / INT8_PEAK_TOPS, 2)
-            row["product_kernel_TOPS"] = round(gemm_tops, 1)
-            row["product_kernel_pct_peak"] = round(100 * gemm_tops / INT8_PEAK_TOPS, 2)
-        _log(f"[configs] {row}")
-        rows.append(row)
-        del X, W, Wq, c_w, ws, v, C
-        torch.cuda.empty_cache()
+            settle(torch, step)
+            step_ms = timed_ms(torch, steps, step)
+            gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
+                v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
+            row = config_row(w, int(v["n_out"].cpu()[0]), step_ms, gemm_ms)
+            del X, W, Wq, c_w, ws, v, C
+            torch.cuda.empty_cache()
+            if cpu_budget > 0:
+                row["cpu_baseline"] = cpu_baseline(w, inp, cpu_budget, host)
+            _log(f"[configs] {row}")
+            rows.append(row)
+            del inp
     return rows
 
 
-def cpu_baseline(w, inputs, budget_s):
-    """Time the CPU oracle (as it stands) on the same workload's inputs.
-
-    The sample is the first R rows of X against all of W, repeated; R and the
-    repetition count are chosen so that the timed work takes about budget_s.
-    """
-    import oracle
+def host_info():
+    """The host the CPU baseline runs on: the cores this process may use,
+    the CPU model, and numpy's BLAS (vendor, version, threads)."""
+    import numpy as np  # noqa: F401  (loads the BLAS so that threadpoolctl sees it)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", int(os.environ.get("OMP_NUM_THREADS", "1"))
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()
-                            if d.get("user_api") == "blas"] or [1])
+        libs = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        if libs:
+            d = libs[0]
+            blas = f"{d.get('internal_api')} {d.get('version')} ({d.get('threading_layer')}, {d.get('architecture')})"
+            threads = max(int(x.get("num_threads", 1)) for x in libs)
     except Exception:  # threadpoolctl missing or unreadable
-        blas_threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+        pass
+    return {"affinity_cores": affinity, "cpu_model": model, "blas": blas, "blas_threads": threads}
+
+
+def _sample_work(w, rows, cols, n_out):
+    """The metric's amount of work in an oracle sample of rows x cols."""
+    if w.decode:
+        return (w.h * cols + 2 * n_out * cols + 4 * cols) / 1e9, "GB/s"   # weight bytes
+    return 2.0 * rows * w.h * cols / 1e12, "TOPS"
+
+
+def cpu_baseline(w, inputs, budget_s, host, reps=3):
+    """Time the CPU oracle (as it stands) on a bounded sample of one workload.
+
+    The sample is the first R rows of X against the first Q columns of W
+    (columns are independent: each output column needs only its own weight
+    column and constant); their load-time weight conversion is done first
+    and not timed. One untimed warm-up, then timed repetitions of
+    oracle.forward; R (Q is at most 2048) is chosen from a probe so that
+    the timed repetitions take about budget_s (with few rows, all rows and
+    more repetitions). The result is scaled to the
+    metric's unit: effective TOPS 2 R h Q / t (prefill), or weight bytes
+    (h Q + 2 |O| Q + 4 Q) / t in GB/s (decode).
+    """
+    import oracle
     X, W = inputs["X"], inputs["W"]
-    Wq_t, c_w = oracle.quantize_colwise_weights(W)      # load time, not timed
-    rows = min(w.s, 256)
+    n_out = int(oracle.outlier_columns(X, w.alpha)[2])
+    cols = min(w.o, 2048)
+    Wq_t, c_w = oracle.quantize_colwise_weights(W[:, :cols])     # load time, not timed
+    probe_rows = min(w.s, 64)
     t = time.perf_counter()
-    oracle.forward(X[:rows], W, w.alpha, Wq_t=Wq_t, c_w=c_w)
-    probe = time.perf_counter() - t
-    per_row = probe / rows
-    rows = int(min(w.s, max(16, budget_s / per_row)))
-    reps = max(1, int(budget_s / (per_row * rows)))
+    oracle.forward(X[:probe_rows], W[:, :cols], w.alpha, Wq_t=Wq_t, c_w=c_w)
+    probe = max(time.perf_counter() - t, 1e-6)
+    if w.s <= probe_rows:
+        rows = w.s                                   # every row; more repetitions instead
+        reps = max(reps, int(budget_s / probe))
+    else:
+        rows = int(min(w.s, max(16, probe_rows * budget_s / reps / probe)))
+    Xs, Ws = X[:rows], W[:, :cols]
+    oracle.forward(Xs, Ws, w.alpha, Wq_t=Wq_t, c_w=c_w)              # warm-up
     t = time.perf_counter()
     for _ in range(reps):
-        oracle.forward(X[:rows], W, w.alpha, Wq_t=Wq_t, c_w=c_w)
+        oracle.forward(Xs, Ws, w.alpha, Wq_t=Wq_t, c_w=c_w)
     el = time.perf_counter() - t
-    tops = 2.0 * rows * w.h * w.o * reps / el / 1e12
+    work, unit = _sample_work(w, rows, cols, n_out)
     return {
-        "value": round(tops, 6),
-        "unit": "TOPS",
-        "cores": blas_threads,
+        "value": round(work * reps / el, 6),
+        "unit": unit,
+        "cores": host["blas_threads"],
         "kind": "oracle",
-        "sample": (f"oracle.forward on the first {rows} of {w.s} rows of X against the full W "
-                   f"[{w.h}x{w.o}], {reps} rep(s), {el:.1f} s; numpy float64 BLAS with "
-                   f"{blas_threads} thread(s), elementwise steps single-threaded"),
+        "sample": (f"oracle.forward on the first {rows} of {w.s} rows of X and the first {cols} of {w.o} "
+                   f"columns of W [{w.h}x{w.o}] (weights converted beforehand), 1 warm-up + {reps} timed "
+                   f"rep(s) in {el:.2f} s; numpy BLAS ({host['blas']}) with {host['blas_threads']} "
+                   f"thread(s) for the products, elementwise steps on one thread"),
+        "affinity_cores": host["affinity_cores"],
+        "cpu_model": host["cpu_model"],
     }
+
+
+class ClockSampler:
+    """Samples the GPU's graphics (sclk) and memory (mclk) clocks from the
+    driver's metrics table (amdsmi) in a background thread while a timed
+    region runs. Reading the table touches no GPU queue."""
+
+    def __init__(self, torch, period_s=0.002):
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self.handle = None
+        self._amdsmi = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self.handle = handles[0] if handles else None
+            try:   # the handle of the GPU torch uses, by PCI bus
+                prop = torch.cuda.get_device_properties(0)
+                want = int(getattr(prop, "pci_bus_id"))
+                for hd in handles:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(hd)
+                    if int(bdf.split(":")[1], 16) == want:
+                        self.handle = hd
+                        break
+            except Exception:
+                pass
+            self._amdsmi = amdsmi
+            if self.handle is None:
+                self.error = "no GPU handle"
+        except Exception as e:  # amdsmi missing or the driver's table unreadable
+            self.error = repr(e)
+
+    def read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+
+        def nums(v):
+            vals = v if isinstance(v, (list, tuple)) else [v]
+            return [float(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 0xFFFF]
+
+        gfx = nums(m.get("current_gfxclks", [])) or nums(m.get("current_gfxclk"))
+        mem = nums(m.get("current_uclk"))
+        return (sum(gfx) / len(gfx) if gfx else None, mem[0] if mem else None)
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+        if self.error is None:
+            try:
+                self.read()
+            except Exception as e:
+                self.error = repr(e)
+        if self.error is None:
+            def loop():
+                while not self._stop.is_set():
+                    try:
+                        self.samples.append(self.read())
+                    except Exception as e:
+                        self.error = repr(e)
+                        return
+                    self._stop.wait(self.period)
+            self._thread = threading.Thread(target=loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if getattr(self, "_thread", None) is not None:
+            self._thread.join()
+        return False
+
+    def summary(self):
+        def stats(vals):
+            vals = sorted(v for v in vals if v is not None)
+            if not vals:
+                return None
+            return {"min": vals[0], "median": vals[len(vals) // 2], "max": vals[-1], "samples": len(vals)}
+        if self.error is not None and not self.samples:
+            return {"error": self.error}
+        return {"sclk_MHz": stats(s for s, _ in self.samples), "mclk_MHz": stats(m for _, m in self.samples),
+                "source": "amdsmi gpu_metrics current_gfxclk(s) / current_uclk, polled every "
+                          f"{self.period * 1e3:.0f} ms during the timed steps"}
+
+
+CONFIG_NAMES = ["tiny", "opt67b_ffn1_prefill", "sweep_o0"] + \
+    [f"sweep_o{n}_r{r}" for n in (7, 64) for r in (6, 28, 75, 100)]
 
 
 def main(argv=None):
@@ -432,11 +594,19 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="opt67b_ffn1_prefill")
+    ap.add_argument("--workload", default="b175_qkv_prefill")
     ap.add_argument("--decode-workload", default="b175_ffn1_decode")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline step and product kernel only: no Table 5 set, weight-copy rotation, "
+                         "storage, bias or quantiser variants")
+    ap.add_argument("--no-all-configs", action="store_true", help="skip the per-configuration rows")
+    ap.add_argument("--config-steps", type=int, default=30, help="timed steps per configuration row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of timed oracle work for the headline cpu_baseline")
+    ap.add_argument("--config-cpu-budget", type=float, default=1.5,
+                    help="seconds of timed oracle work for each configuration's cpu_baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic of the product kernel measured with rocprofv3 counters")
     ap.add_argument("--table5", action="store_true",
@@ -445,7 +615,7 @@ def main(argv=None):
     ap.add_argument("--table5-rows", type=int, default=2048, help="rows of X (tokens) for --table5")
     ap.add_argument("--all-configs", action="store_true",
                     help="only time the one-call forward and the product kernel on every configuration "
-                         "(tiny, prefill, decode, QKV prefill, outlier-density sweep) and print one JSON line")
+                         "(no CPU baselines) and print one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (5 times) and exit; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -458,7 +628,7 @@ def main(argv=None):
 
     import torch
     import int8_quantized_matmul_amd as i8
-    from workloads import get_config
+    from workloads import CONFIGS, get_config
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -477,13 +647,15 @@ def main(argv=None):
                                   "speed-up = FP16 library GEMM time / variant time"}), flush=True)
         return 0
     if args.all_configs:
-        print(json.dumps({"all_configs": run_all_configs(i8, torch, dev, args.steps),
+        print(json.dumps({"all_configs": run_all_configs(i8, torch, dev, args.steps, list(CONFIGS)),
                           "note": "one-call forward step (detect + quantise + product) and the product "
                                   "kernel alone, weights converted beforehand, inputs resident"}), flush=True)
         return 0
+    host = host_info()
     w = get_config(args.workload)
     _log(f"[bench] prefill workload {w.name}: s={w.s} h={w.h} o={w.o}")
-    pre = run_prefill(i8, torch, w, args.steps, args.warmup, dev)
+    clocks = ClockSampler(torch)
+    pre = run_prefill(i8, torch, w, args.steps, args.warmup, dev, clocks=clocks, extras=not args.no_extras)
     s, h, o, n_out = w.s, w.h, w.o, pre["n_out"]
     tops = 2.0 * s * h * o / (pre["step_ms"] * 1e-3) / 1e12
     alg_ops = 2.0 * s * (h - n_out) * o                  # int8 ops one product launch performs
@@ -519,7 +691,7 @@ def main(argv=None):
             "kernel": "k_gemm_prefill (int8 MFMA + fused dequant/outlier epilogue)",
             "achieved": round(gemm_tops, 3),
             "peak": INT8_PEAK_TOPS,
-            "unit": "TFLOP/s",
+            "unit": "TOP/s",
             "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
             "traffic": traffic,
             "algorithmic_ops_per_launch": alg_ops,
@@ -527,20 +699,30 @@ def main(argv=None):
         },
         "pct_int8_peak_effective": round(100 * tops / INT8_PEAK_TOPS, 2),
         "step_ms_percentiles": pre["pct"],
-        "step_ms_weights_from_hbm": {"ms": round(pre["cold_ms"], 5), "weight_copies_rotated": pre["copies"]},
-        "table5_comparison": pre["table5"],
-        "without_fp16_weights": _w8_entry(pre["w8"], h, o),
-        "with_bias": _bias_entry(pre["w8"]),
-        "quantiser_variants": pre["quant"],
+        "clocks": clocks.summary(),
         "weight_conversion": {"ms": round(pre["conv_ms"], 4),
-                              "GB_per_s": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1)},
+                              "GB_per_s_3ho": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1)},
     }
+    if not args.no_extras:
+        out.update({
+            "step_ms_weights_from_hbm": {"ms": round(pre["cold_ms"], 5), "weight_copies_rotated": pre["copies"]},
+            "table5_comparison": pre["table5"],
+            "without_fp16_weights": _w8_entry(pre["w8"], h, o),
+            "with_bias": _bias_entry(pre["w8"]),
+            "quantiser_variants": pre["quant"],
+        })
     inputs = pre.pop("inputs")
+    rows = [config_row(w, n_out, pre["step_ms"], pre["gemm_ms"])]
+    if not args.no_cpu_baseline:
+        _log("[bench] timing the CPU oracle (headline)")
+        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget, host)
+        rows[0]["cpu_baseline"] = out["cpu_baseline"]
+    del inputs
 
     if not args.no_decode:
         wd = get_config(args.decode_workload)
         _log(f"[bench] decode workload {wd.name}: s={wd.s} h={wd.h} o={wd.o}")
-        dec = run_decode(i8, torch, wd, args.steps, args.warmup, dev)
+        dec = run_decode(i8, torch, wd, args.steps, args.warmup, dev, extras=not args.no_extras)
         gbs = dec["weight_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
         gbs_gemm = dec["weight_bytes"] / (dec["gemm_ms"] * 1e-3) / 1e9
         out["decode"] = {
@@ -550,14 +732,29 @@ def main(argv=None):
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "product_kernel_ms": round(dec["gemm_ms"], 5),
             "product_kernel_weight_GB_per_s": round(gbs_gemm, 1),
-            "without_fp16_weights": _w8_entry(dec["w8"], wd.h, wd.o),
-            "with_bias": _bias_entry(dec["w8"]),
-            "quantiser_variants": dec["quant"],
         }
+        if not args.no_extras:
+            out["decode"].update({
+                "without_fp16_weights": _w8_entry(dec["w8"], wd.h, wd.o),
+                "with_bias": _bias_entry(dec["w8"]),
+                "quantiser_variants": dec["quant"],
+            })
+        drow = config_row(wd, dec["n_out"], dec["step_ms"], dec["gemm_ms"])
+        if not args.no_cpu_baseline:
+            _log("[bench] timing the CPU oracle (decode)")
+            out["decode"]["cpu_baseline"] = cpu_baseline(wd, dec.pop("inputs"), args.config_cpu_budget * 2, host)
+            drow["cpu_baseline"] = out["decode"]["cpu_baseline"]
+        dec.pop("inputs", None)
+        rows.append(drow)
+        del dec
+        torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
-        _log("[bench] timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
+    if not args.no_all_configs:
+        _log("[bench] every other configuration")
+        rows += run_all_configs(i8, torch, dev, args.config_steps, CONFIG_NAMES, host,
+                                0.0 if args.no_cpu_baseline else args.config_cpu_budget)
+        out["all_configs"] = rows
+    out["host"] = host
     print(json.dumps(out), flush=True)
     return 0
 

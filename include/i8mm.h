@@ -45,8 +45,32 @@
  *     even), c = 1 when m == 0. Quantisation is v = fl32(x * c) rounded half
  *     away from zero, in [-127, 127].
  *   - X may hold +-inf (always an outlier: |x| >= alpha for every accepted
- *     alpha); a NaN is never an outlier, and a NaN among a row's
- *     non-outlier values leaves that row's scale and codes unspecified.
+ *     alpha). A NaN element never makes its column an outlier, and it does
+ *     not hide an element of the same column that reaches alpha (the test is
+ *     element by element); a NaN among a row's non-outlier values leaves
+ *     that row's scale and codes unspecified.
+ *
+ * Where this interface departs from the plain signatures one would write
+ * from the pages' five steps (W_i8 as a [o, h] matrix, one workspace-size
+ * query, no bias), and why:
+ *   - Wq is in the panel layout below, not a plain [o, h] matrix: the decode
+ *     product streams 16-column panel tiles as contiguous KiB runs (a probe
+ *     of the same loop went from 4.6 to 7.0 TB/s of weights). It is written
+ *     once by the load-time conversion, so it costs nothing per forward.
+ *   - The workspace queries are i8mm_forward_workspace_bytes (plus the
+ *     _layout query that returns the offsets of the intermediates, and a
+ *     zeropoint variant), named for the call they serve.
+ *   - i8mm_int8_mixed_matmul and the one-call forwards take an optional
+ *     fp16 layer bias (NULL for none) added before the single rounding, and
+ *     accept W = NULL (no resident fp16 weights, outlier rows rebuilt).
+ *   - The products require h * o < 2^31: Wq (h o bytes) and W (2 h o bytes)
+ *     are read through 32-bit buffer offsets; larger layers are rejected
+ *     with I8MM_EINVAL.
+ *   - i8mm_quantize_rowwise derives O from the mask alone; idx and n_out are
+ *     validated but not read.
+ *   - Extra entry points beyond the four steps: the one-call forwards, the
+ *     int32 and outlier-only products (inspection), the dense fp16 baseline
+ *     and the quantiser variants of Table 1.
  */
 #ifndef I8MM_H
 #define I8MM_H
@@ -63,7 +87,10 @@ typedef enum {
     I8MM_OK = 0,
     I8MM_EINVAL = -1,   /* bad pointer, shape, alignment or argument value */
     I8MM_EDEVICE = -2,  /* no HIP device, or the current device is not gfx950 */
-    I8MM_ELAUNCH = -3   /* a kernel launch was rejected by the runtime */
+    I8MM_ELAUNCH = -3,  /* a kernel launch was rejected by the runtime */
+    I8MM_EWORKSPACE = -4 /* a one-call forward's launch failed after its detection had
+                            written the workspace accumulator, and the launch that
+                            clears it failed too: zero the accumulator before reuse */
 } i8mm_status;
 
 /* Largest h accepted (int32 accumulator bound, rounded down to 64). */
@@ -324,6 +351,12 @@ size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h);
  * workspace may be reused for any shape whose size fits. Calls that share a
  * workspace must not overlap. After completion the workspace holds the
  * intermediates at the offsets given by i8mm_forward_workspace_layout.
+ * Errors: I8MM_EINVAL / I8MM_EDEVICE before anything is enqueued. If a
+ * launch fails after the detection was enqueued, one more launch on the
+ * same stream clears the accumulator and the call returns I8MM_ELAUNCH (C
+ * is not written; the workspace stays valid); if that launch fails as well,
+ * the call returns I8MM_EWORKSPACE and the caller must zero the
+ * accumulator before the workspace is used again.
  * X: [s, h] fp16; Wq: panel layout (above); c_w: [o] fp32; W: [h, o] fp16
  * or NULL, and bias: [o] fp16 or NULL (both as for i8mm_int8_mixed_matmul);
  * C: [s, o] fp16 (written).
@@ -380,6 +413,14 @@ i8mm_status i8mm_forward_zeropoint(const uint16_t* X, int64_t s, int64_t h, int6
  * pointers. Host-only; touches no device.
  */
 i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[7], int64_t* ldo);
+
+/*
+ * Test hook: the next `count` one-call forwards (i8mm_forward and its
+ * tensor-wise and zeropoint variants) report their product launch as
+ * failed without launching it, so that tests can drive the error path
+ * above from the host; count <= 0 turns it off. Not for production use.
+ */
+void i8mm_test_fail_product_launches(int count);
 
 /* Library version string (static storage). */
 const char* i8mm_version(void);

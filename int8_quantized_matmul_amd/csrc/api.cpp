@@ -60,6 +60,37 @@ i8mm_status check_device() {
 
 i8mm_status launched(hipError_t e) { return e == hipSuccess ? I8MM_OK : I8MM_ELAUNCH; }
 
+// Test hook: the number of one-call forwards whose product launch is to
+// report a failure without launching (i8mm_test_fail_product_launches).
+std::atomic<int> g_fail_products{0};
+
+bool product_launch_suppressed() {
+    int n = g_fail_products.load(std::memory_order_relaxed);
+    while (n > 0)
+        if (g_fail_products.compare_exchange_weak(n, n - 1, std::memory_order_relaxed)) return true;
+    return false;
+}
+
+// Status of a one-call forward whose launches after the first (the
+// detection, which writes the workspace accumulator) may have failed: on a
+// failure the accumulator is cleared again by one more launch on the same
+// stream, so that the workspace stays valid for the next call.
+i8mm_status forward_status(hipError_t e, uint32_t* acc, hipStream_t stream) {
+    if (e == hipSuccess) return I8MM_OK;
+    (void)hipGetLastError();
+    if (i8mm::launch_fill_u32(acc, I8MM_FORWARD_ACC_BYTES / 4, 0u, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return I8MM_EWORKSPACE;
+    }
+    return I8MM_ELAUNCH;
+}
+
+// The product launch of a one-call forward (or the simulated failure).
+template <typename F>
+hipError_t product_launch(F&& launch) {
+    return product_launch_suppressed() ? hipErrorLaunchFailure : launch();
+}
+
 // Workspace of i8mm_forward: the detection accumulator (fixed size, so that its
 // place does not depend on the shape), then mask, idx, n_out, Xq, c_x, X_O;
 // each 256-byte aligned.
@@ -96,6 +127,7 @@ const char* i8mm_status_string(i8mm_status st) {
         case I8MM_EINVAL: return "invalid argument";
         case I8MM_EDEVICE: return "no gfx950 device";
         case I8MM_ELAUNCH: return "kernel launch failed";
+        case I8MM_EWORKSPACE: return "kernel launch failed and the workspace accumulator could not be cleared";
     }
     return "unknown status";
 }
@@ -299,10 +331,12 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
     int clear_words = 0;
     hipError_t e = i8mm::launch_forward_prologue(X, s, h, alpha, acc, mask, idx, n_out, Xq, c_x, X_O, ldo, stream,
                                                  &clear_words);
-    if (e != hipSuccess) return I8MM_ELAUNCH;
-    e = i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s, h, o,
-                               C, stream, clear_words > 0 ? acc : nullptr, clear_words);
-    return launched(e);
+    if (e == hipSuccess)
+        e = product_launch([&] {
+            return i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s,
+                                          h, o, C, stream, clear_words > 0 ? acc : nullptr, clear_words);
+        });
+    return forward_status(e, acc, stream);
 }
 
 i8mm_status i8mm_forward_tensorwise(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
@@ -330,10 +364,12 @@ i8mm_status i8mm_forward_tensorwise(const uint16_t* X, int64_t s, int64_t h, int
     hipError_t e = i8mm::launch_forward_prologue_variant(false, X, s, h, alpha, acc,
                                                          reinterpret_cast<uint32_t*>(ws + off[1]), idx, n_out, Xq,
                                                          c_x, nullptr, nullptr, X_O, ldo, stream, &clear_words);
-    if (e != hipSuccess) return I8MM_ELAUNCH;
-    e = i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s, h, o,
-                               C, stream, acc, clear_words);
-    return launched(e);
+    if (e == hipSuccess)
+        e = product_launch([&] {
+            return i8mm::launch_int8_gemm(i8mm::GemmOut::Mixed, Xq, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s,
+                                          h, o, C, stream, acc, clear_words);
+        });
+    return forward_status(e, acc, stream);
 }
 
 size_t i8mm_forward_zeropoint_workspace_bytes(int64_t s, int64_t h) {
@@ -372,10 +408,17 @@ i8mm_status i8mm_forward_zeropoint(const uint16_t* X, int64_t s, int64_t h, int6
     hipError_t e = i8mm::launch_forward_prologue_variant(true, X, s, h, alpha, acc,
                                                          reinterpret_cast<uint32_t*>(ws + off[1]), idx, n_out, Xq,
                                                          nd_x, zp_x, rowsum_x, X_O, ldo, stream, &clear_words);
-    if (e != hipSuccess) return I8MM_ELAUNCH;
-    e = i8mm::launch_int8_gemm(i8mm::GemmOut::ZeroPoint, Xq, nd_x, X_O, ldo, idx, n_out, Wq, nd_w, W, bias, s, h,
-                               o, C, stream, acc, clear_words, i8mm::ZpArgs{zp_x, rowsum_x, zp_w, colsum_w});
-    return launched(e);
+    if (e == hipSuccess)
+        e = product_launch([&] {
+            return i8mm::launch_int8_gemm(i8mm::GemmOut::ZeroPoint, Xq, nd_x, X_O, ldo, idx, n_out, Wq, nd_w, W, bias,
+                                          s, h, o, C, stream, acc, clear_words,
+                                          i8mm::ZpArgs{zp_x, rowsum_x, zp_w, colsum_w});
+        });
+    return forward_status(e, acc, stream);
+}
+
+void i8mm_test_fail_product_launches(int count) {
+    g_fail_products.store(count > 0 ? count : 0, std::memory_order_relaxed);
 }
 
 }  // extern "C"

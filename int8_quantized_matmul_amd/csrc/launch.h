@@ -11,6 +11,10 @@ namespace i8mm {
 hipError_t launch_detect(const uint16_t* X, int64_t s, int64_t h, float alpha,
                          uint32_t* mask, int32_t* idx, int32_t* n_out, hipStream_t stream);
 
+// p[0 .. n) = v (one small kernel; also clears state inside captured graphs,
+// where a memset node is avoided).
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
+
 hipError_t launch_quantize_rows(const uint16_t* X, int64_t s, int64_t h,
                                 const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
                                 int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,

@@ -625,6 +625,11 @@ hipError_t launch_detect(const uint16_t* X, int64_t s, int64_t h, float alpha,
     return hipGetLastError();
 }
 
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream) {
+    hipLaunchKernelGGL(k_fill_u32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, p, n, v);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_rows(const uint16_t* X, int64_t s, int64_t h,
                                 const uint32_t* mask, const int32_t* idx, const int32_t* n_out,
                                 int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,

@@ -2,7 +2,9 @@
 
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -59,3 +61,32 @@ def check_C(C_d, C_ref: np.ndarray, tol: float = 2e-3):
     err = np.abs(C - R).max() if R.size else 0.0
     assert err <= tol * norm + 1e-30, f"max |C - C_ref| = {err:.3e} > {tol} * {norm:.3e}"
     return err / norm if norm else 0.0
+
+
+def host_threads() -> int:
+    """Threads for host-side oracle work: the cores this process may run on,
+    at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_weights_by_columns(W: np.ndarray, chunk: int = 2048):
+    """The oracle's load-time conversion of every column of W, evaluated on
+    column chunks in parallel threads. Columns are converted independently
+    (each has its own constant), so this is oracle.quantize_colwise_weights
+    of the whole W; only the evaluation is spread over threads."""
+    h, o = W.shape
+    Wq_t = np.empty((o, h), np.int8)
+    c_w = np.empty(o, np.float32)
+
+    def job(j0):
+        q, c = oracle.quantize_colwise_weights(W[:, j0:j0 + chunk])
+        Wq_t[j0:j0 + chunk] = q
+        c_w[j0:j0 + chunk] = c
+
+    with ThreadPoolExecutor(host_threads()) as ex:
+        list(ex.map(job, range(0, o, chunk)))
+    return Wq_t, c_w

@@ -31,6 +31,29 @@ def test_version_and_status_strings():
     assert lib.i8mm_status_string(0) == b"ok"
     assert lib.i8mm_status_string(-1) == b"invalid argument"
     assert lib.i8mm_status_string(-2) == b"no gfx950 device"
+    assert lib.i8mm_status_string(-3) == b"kernel launch failed"
+    assert b"workspace accumulator" in lib.i8mm_status_string(-4)
+    assert lib.i8mm_status_string(-99) == b"unknown status"
+
+
+def test_forward_error_contract_is_declared():
+    """The one-call forwards' error path as the header states it: a failed
+    launch after the detection returns I8MM_ELAUNCH with the accumulator
+    cleared by one more launch, or I8MM_EWORKSPACE if that launch fails too;
+    the test hook that forces the failure from the host is exported."""
+    with open(_native.HEADER) as f:
+        text = f.read()
+    assert "I8MM_EWORKSPACE = -4" in text
+    assert "clears the accumulator and the call returns I8MM_ELAUNCH" in text
+    lib = _lib()
+    lib.i8mm_test_fail_product_launches(0)   # host-only: sets nothing on a device
+    # with no device the check comes first and leaves the hook untouched
+    import torch
+    if torch.cuda.device_count() == 0:
+        lib.i8mm_test_fail_product_launches(1)
+        ws = ctypes.c_void_p(1 << 20)
+        assert lib.i8mm_forward(P, 4, 64, 64, 6.0, P, P, P, None, ws, P, None) == -2
+        lib.i8mm_test_fail_product_launches(0)
 
 
 P = ctypes.c_void_p(1 << 20)          # a 16-byte aligned non-null stand-in (never dereferenced)
