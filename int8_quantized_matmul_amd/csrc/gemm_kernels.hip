@@ -79,14 +79,27 @@ __device__ __forceinline__ uint32_t bytes_left(int64_t total, int64_t from) {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // a per-lane offset past every buffer
 
-// Block -> output tile. Blocks are dealt to the 8 XCDs round robin
-// (block b runs on XCD b % 8); each XCD is given one contiguous run of the
-// s-fastest tile order so that the tiles sharing weight columns and rows of
-// Xq meet in the same 4 MiB L2. Block and tile indices are 32-bit (as the
-// grid is), which keeps the index arithmetic short ahead of the first loads.
-__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t nb) {
+// Block -> output tile. Blocks are dealt to the 8 XCDs round robin (block b
+// runs on XCD b % 8), and each XCD is given one contiguous run of a grouped
+// tile order: column groups of kGroup weight tiles that span every row tile,
+// row by row inside a group. The ~32 tiles an XCD runs at once then cover
+// about 4 row tiles x 8 weight tiles, i.e. ~12 operand panels streamed
+// through its 4 MiB L2 per round instead of every row panel of Xq (an order
+// with rows fastest made each round re-fetch all of Xq). Block and tile
+// indices are 32-bit (as the grid is), which keeps the index arithmetic
+// short ahead of the first loads.
+constexpr uint32_t kGroup = 8;
+
+__device__ __forceinline__ void grouped_tile(uint32_t b, uint32_t nb, uint32_t n_ts, uint32_t n_to,
+                                             uint32_t& ts, uint32_t& to) {
     const uint32_t q = nb / 8, r = nb % 8, x = b % 8, i = b / 8;
-    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+    const uint32_t t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;   // place in the grouped order
+    const uint32_t per = kGroup * n_ts;
+    const uint32_t g = t / per, j = t % per;
+    const uint32_t c0 = g * kGroup;
+    const uint32_t w = n_to - c0 < kGroup ? n_to - c0 : kGroup;
+    ts = j / w;
+    to = c0 + j % w;
 }
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -318,8 +331,10 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     // 32-bit division (a 64-bit one is a long scalar sequence that would
     // delay the first loads): tile < gridDim.x and n_ts < 2^32
     const uint32_t n_ts = static_cast<uint32_t>((s + kTS - 1) / kTS);
-    const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t ts_i = tile % n_ts, to_i = tile / n_ts;
+    const uint32_t n_to = static_cast<uint32_t>((o + kTO - 1) / kTO);
+    uint32_t ts_u, to_u;
+    grouped_tile(blockIdx.x, gridDim.x, n_ts, n_to, ts_u, to_u);
+    const int64_t ts_i = ts_u, to_i = to_u;
     const int64_t o0 = to_i * kTO, s0 = ts_i * kTS;
     const int64_t o_rows = o - o0 < kTO ? o - o0 : kTO;
     const int64_t s_rows = s - s0 < kTS ? s - s0 : kTS;
