@@ -88,9 +88,11 @@ typedef enum {
     I8MM_EINVAL = -1,   /* bad pointer, shape, alignment or argument value */
     I8MM_EDEVICE = -2,  /* no HIP device, or the current device is not gfx950 */
     I8MM_ELAUNCH = -3,  /* a kernel launch was rejected by the runtime */
-    I8MM_EWORKSPACE = -4 /* a one-call forward's launch failed after its detection had
-                            written the workspace accumulator, and the launch that
-                            clears it failed too: zero the accumulator before reuse */
+    I8MM_EWORKSPACE = -4, /* a one-call forward's launch failed after its detection had
+                             written the workspace accumulator, and the launch that
+                             clears it failed too: zero the accumulator before reuse */
+    I8MM_ESCRATCH = -5    /* i8mm_forward_noalloc: the shape needs more workspace than
+                             I8MM_NOALLOC_SCRATCH_BYTES */
 } i8mm_status;
 
 /* Largest h accepted (int32 accumulator bound, rounded down to 64). */
@@ -413,6 +415,31 @@ i8mm_status i8mm_forward_zeropoint(const uint16_t* X, int64_t s, int64_t h, int6
  * pointers. Host-only; touches no device.
  */
 i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[7], int64_t* ldo);
+
+/* Bytes of the static device scratch that i8mm_forward_noalloc uses as its
+ * workspace (64 MiB per GPU the library runs on). */
+#define I8MM_NOALLOC_SCRATCH_BYTES 67108864
+
+/*
+ * i8mm_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. The call allocates nothing (no
+ * hipMalloc, no allocating library routine); its workspace is a static
+ * device array of I8MM_NOALLOC_SCRATCH_BYTES bytes that every GPU the
+ * library runs on holds from module load until the process ends. Shapes
+ * whose i8mm_forward_workspace_bytes(s, h) exceeds that return
+ * I8MM_ESCRATCH before anything is enqueued (e.g. s * h up to about 21 M
+ * elements fits: 2048 x 8192, or any few-row decode step). The array's
+ * device address is looked up once per device on the first call, which
+ * also enqueues one small launch that zeroes its accumulator.
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * intermediates; calls that overlap on one GPU (concurrent streams or
+ * threads) race on it and must not be issued. Other arguments, the
+ * computation, the launches and the errors are those of i8mm_forward.
+ */
+i8mm_status i8mm_forward_noalloc(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                 const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                 uint16_t* C, hipStream_t stream);
 
 /*
  * Test hook: the next `count` one-call forwards (i8mm_forward and its

@@ -30,6 +30,8 @@ __all__ = [
     "forward",
     "forward_tensorwise",
     "forward_zeropoint",
+    "forward_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "pack_fp16_weights",
     "fp16_gemm",
     "quantize_tensorwise",
@@ -63,6 +65,8 @@ _lib = _LazyLib()
 
 # Bytes of the forward workspace's leading accumulator (I8MM_FORWARD_ACC_BYTES).
 ACC_BYTES = _native.header_define("I8MM_FORWARD_ACC_BYTES")
+# Bytes of the static device scratch behind forward_noalloc (I8MM_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = _native.header_define("I8MM_NOALLOC_SCRATCH_BYTES")
 
 
 class I8MMError(RuntimeError):
@@ -499,4 +503,23 @@ def forward_zeropoint(X: torch.Tensor, qw: Tuple[torch.Tensor, ...], W: torch.Te
         _dev(cs_w, "colsum_w", torch.int32, (o,)), _dev(W, "W", torch.float16, (h, o)), _bias_ptr(bias, o),
         _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
     _check(st, "forward_zeropoint")
+    return C
+
+
+def forward_noalloc(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Optional[torch.Tensor],
+                    alpha: float = 6.0, C: torch.Tensor = None, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """forward() over the library's static device scratch instead of a
+    workspace: the call allocates nothing on the device when C is given
+    (for graph capture and loops that must not allocate). Raises I8MMError
+    (status -5) when the shape needs more than NOALLOC_SCRATCH_BYTES of
+    workspace. Calls on one GPU share the scratch and must not overlap."""
+    s, h = X.shape
+    o = Wq.shape[1]
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.float16, device=X.device)
+    st = _lib.i8mm_forward_noalloc(
+        _dev(X, "X", torch.float16), s, h, o, float(alpha), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)),
+        _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o), _bias_ptr(bias, o),
+        _dev(C, "C", torch.float16, (s, o)), _stream(X))
+    _check(st, "forward_noalloc")
     return C

@@ -12,6 +12,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -115,6 +116,45 @@ void forward_layout(int64_t s, int64_t h, size_t off[7], int64_t* ldo, size_t* t
     *total = cur;
 }
 
+// Scratch of i8mm_forward_noalloc: the forward workspace (accumulator,
+// mask, idx, n_out, Xq, c_x, X_O) in a static device array, so that the
+// call allocates nothing. Each GPU the library runs on holds its own copy
+// from module load until the process ends; zero-initialised at load, and
+// the forward leaves its accumulator zero again after every call.
+__device__ __align__(256) unsigned char scratch[I8MM_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on each GPU, looked up once per device with
+// that device current (the array's name is only a host-side stand-in).
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+void* scratch_on_current_device(hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    ScratchSlot& slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot, stream] {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        // The array is zero from load; clearing the accumulator once more on
+        // the first call's stream costs one small launch per device.
+        if (i8mm::launch_fill_u32(static_cast<uint32_t*>(p), I8MM_FORWARD_ACC_BYTES / 4, 0u, stream) != hipSuccess) {
+            (void)hipGetLastError();
+            return;
+        }
+        slot.ptr = p;
+    });
+    return slot.ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,6 +168,7 @@ const char* i8mm_status_string(i8mm_status st) {
         case I8MM_EDEVICE: return "no gfx950 device";
         case I8MM_ELAUNCH: return "kernel launch failed";
         case I8MM_EWORKSPACE: return "kernel launch failed and the workspace accumulator could not be cleared";
+        case I8MM_ESCRATCH: return "shape needs more workspace than the static scratch holds";
     }
     return "unknown status";
 }
@@ -306,17 +347,26 @@ i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[7
     return I8MM_OK;
 }
 
-i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
-                         const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
-                         void* workspace, uint16_t* C, hipStream_t stream) {
-    if (!X || !Wq || !c_w || !workspace || !C) return I8MM_EINVAL;   // W and bias may be null
+}  // extern "C"
+
+namespace {
+
+// Arguments of the absmax one-call forward other than its workspace.
+i8mm_status check_forward_args(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha, const int8_t* Wq,
+                               const float* c_w, const uint16_t* W, const uint16_t* bias, const uint16_t* C) {
+    if (!X || !Wq || !c_w || !C) return I8MM_EINVAL;   // W and bias may be null
     if (!valid_shape_sh(s, h) || !valid_o(o) || !valid_w_extent(h, o)) return I8MM_EINVAL;
     if (std::isnan(alpha) || alpha < 0.0f) return I8MM_EINVAL;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(c_w) || !aligned16(W) || !aligned16(bias) ||
         !aligned16(C))
         return I8MM_EINVAL;
-    if (i8mm_status d = check_device()) return d;
+    return I8MM_OK;
+}
+
+// The launches of the absmax one-call forward over a checked workspace.
+i8mm_status run_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha, const int8_t* Wq,
+                        const float* c_w, const uint16_t* W, const uint16_t* bias, void* workspace, uint16_t* C,
+                        hipStream_t stream) {
     size_t off[7], total;
     int64_t ldo;
     forward_layout(s, h, off, &ldo, &total);
@@ -337,6 +387,31 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
                                           h, o, C, stream, clear_words > 0 ? acc : nullptr, clear_words);
         });
     return forward_status(e, acc, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                         const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                         void* workspace, uint16_t* C, hipStream_t stream) {
+    if (!workspace) return I8MM_EINVAL;
+    if (i8mm_status a = check_forward_args(X, s, h, o, alpha, Wq, c_w, W, bias, C)) return a;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return run_forward(X, s, h, o, alpha, Wq, c_w, W, bias, workspace, C, stream);
+}
+
+i8mm_status i8mm_forward_noalloc(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                 const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                 uint16_t* C, hipStream_t stream) {
+    if (i8mm_status a = check_forward_args(X, s, h, o, alpha, Wq, c_w, W, bias, C)) return a;
+    if (i8mm_forward_workspace_bytes(s, h) > I8MM_NOALLOC_SCRATCH_BYTES) return I8MM_ESCRATCH;
+    if (i8mm_status d = check_device()) return d;
+    void* ws = scratch_on_current_device(stream);
+    if (ws == nullptr) return I8MM_EDEVICE;
+    return run_forward(X, s, h, o, alpha, Wq, c_w, W, bias, ws, C, stream);
 }
 
 i8mm_status i8mm_forward_tensorwise(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
