@@ -701,7 +701,10 @@ def main(argv=None):
         "step_ms_percentiles": pre["pct"],
         "clocks": clocks.summary(),
         "weight_conversion": {"ms": round(pre["conv_ms"], 4),
-                              "GB_per_s_3ho": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1)},
+                              "GB_per_s_3ho": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1),
+                              "GB_per_s_5ho_moved": round(5.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1),
+                              "pct_hbm_peak_5ho": round(100 * 5.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9
+                                                        / HBM_PEAK_GBS, 2)},
     }
     if not args.no_extras:
         out.update({

@@ -450,74 +450,129 @@ __global__ __launch_bounds__(1024) void k_tensor_scale(float* __restrict__ m, in
 // Load-time column-wise quantisation of W [h, o] into the panel layout
 // Wq [h / 64][o][64] (W_i8[k, j] at (k / 64) o 64 + 64 j + k % 64)
 // ([DIGEST] "The Full LLM.int8() Algorithm", Step 4; "Why vector-wise
-// rather than row-wise": constants computed once at load time).
-//
-// One 256-thread block per 64-column strip. Pass 1: per-column absmax over
-// all h rows (thread = 8 columns x every 32nd row; one wavefront reads 8
-// rows x 128 bytes). Pass 2: 64x64 tiles are quantised, transposed through
-// LDS and written as the strip's contiguous 4 KiB of each panel.
-// SC as for k_quant_rows: MaxOnly writes the column absmax to c_w and stops
-// after pass 1; Given skips pass 1 and quantises with the scales in c_w.
-template <RowScale SC = RowScale::Absmax>
-__global__ __launch_bounds__(256) void k_quant_cols(const uint16_t* __restrict__ W, int64_t h, int64_t o,
-                                                    int8_t* __restrict__ Wq, float* __restrict__ c_w) {
-    __shared__ float red[32][65];
-    __shared__ float scale[64];
-    __shared__ __attribute__((aligned(16))) int8_t tile[64][80];
-    const int t = threadIdx.x;
-    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 64;
-    const int cc = t & 7, rg = t >> 3;
+// rather than row-wise": constants computed once at load time), in three
+// launches that each cover the whole matrix with many blocks:
+//   1. k_col_absmax_part: the largest |W_ij| of each column over each chunk
+//      of kColRows rows, as fp16 bit patterns (the patterns of |x| order
+//      like the values), into a small array of partial maxima;
+//   2. k_col_absmax_reduce: one thread per column takes the largest of its
+//      partial maxima and writes c_w_j = fl32(127 / m_j) (MaxOnly: m_j);
+//   3. k_quant_panels: one block per 64-row panel and 512 columns quantises
+//      the panel with the column constants and writes the columns' 64-code
+//      runs, which lie contiguous in the panel.
+// The partial maxima live in the Wq buffer itself (h / kColRows rows of o
+// patterns, far smaller than h o bytes): the last launch overwrites them
+// after the reduction has read them (same stream).
+constexpr int kColRows = 256;
 
-    if constexpr (SC == RowScale::Given) {
-        if (t < 64) scale[t] = c_w[j0 + t];
-        __syncthreads();
-    } else {
-    float m[8];
+__global__ __launch_bounds__(256) void k_col_absmax_part(const uint16_t* __restrict__ W, int64_t h, int64_t o,
+                                                         uint16_t* __restrict__ part) {
+    __shared__ uint4 red[4][64];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 512 + lane * 8;   // the lane's 8 columns
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kColRows;
+    const int64_t nrows = h - r0 < kColRows ? h - r0 : kColRows;           // a multiple of 64
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    if (j0 < o) {
+        const uint16_t* src = W + r0 * o + j0;
+        // wavefront wid reads rows wid, wid + 4, ...: one KiB of one row per
+        // load, 16 loads in flight per lane (nrows is a multiple of 64)
+        for (int64_t i0 = wid; i0 < nrows; i0 += 64) {
+            uint4 v[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m[e] = 0.0f;
-    for (int64_t r = rg; r < h; r += 32) {
-        uint4 v = *reinterpret_cast<const uint4*>(W + r * o + j0 + cc * 8);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int u = 0; u < 16; ++u) v[u] = load_chunk(src + (i0 + 4 * u) * o);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            m[e] = fmaxf(m[e], fabsf(half_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu)));
-    }
+            for (int u = 0; u < 16; ++u)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[rg][cc * 8 + e] = m[e];
-    __syncthreads();
-    if (t < 64) {
-        float mm = 0.0f;
-        for (int g = 0; g < 32; ++g) mm = fmaxf(mm, red[g][t]);
-        if constexpr (SC == RowScale::MaxOnly) {
-            c_w[j0 + t] = mm;
-        } else {
-            const float sc = absmax_scale(mm);
-            scale[t] = sc;
-            c_w[j0 + t] = sc;
+                for (int k = 0; k < 4; ++k) m[k] = pk_max_u16(m[k], word_of(v[u], k) & kAbs2);
         }
     }
-    if constexpr (SC == RowScale::MaxOnly) return;
+    red[wid][lane] = make_uint4(m[0], m[1], m[2], m[3]);
     __syncthreads();
+    if (wid == 0 && j0 < o) {
+        uint4 r = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            const uint4 q = red[w][lane];
+            r = make_uint4(pk_max_u16(r.x, q.x), pk_max_u16(r.y, q.y), pk_max_u16(r.z, q.z), pk_max_u16(r.w, q.w));
+        }
+        *reinterpret_cast<uint4*>(part + static_cast<int64_t>(blockIdx.y) * o + j0) = r;
     }
+}
 
-    for (int64_t r0 = 0; r0 < h; r0 += 64) {
+template <RowScale SC>
+__global__ __launch_bounds__(256) void k_col_absmax_reduce(const uint16_t* __restrict__ part, int nparts, int64_t o,
+                                                           float* __restrict__ c_w) {
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (j >= o) return;
+    uint32_t m = 0;
+#pragma unroll 8
+    for (int r = 0; r < nparts; ++r) {
+        const uint32_t v = part[r * o + j];
+        m = v > m ? v : m;
+    }
+    const float mx = half_bits_to_float(m);
+    c_w[j] = SC == RowScale::MaxOnly ? mx : absmax_scale(mx);
+}
+
+// Panel quantisation: block = one 64-row panel x 512 columns; wavefront w
+// quantises rows 16 w .. 16 w + 15, lane l the 8 columns 8 l .. 8 l + 7
+// (one 16-byte load per row: a wavefront reads one KiB of a row at once).
+// Each column's 16 codes go to LDS as one 16-byte write at the column's
+// 64-byte run; the block then writes its 512 runs (32 KiB, contiguous in
+// the panel) with 16-byte stores, one KiB per wavefront store. LDS keeps
+// 16 bytes of padding after every 8 columns, so both the 16-byte writes
+// (lanes 8 columns apart) and the read-back (4 lanes per column) fill the
+// banks without conflicts beyond the passes a 16-byte access needs.
+constexpr int kPanelCols = 512;
+
+__device__ __forceinline__ int panel_lds_offset(int col, int seg) { return col * 64 + (col >> 3) * 16 + seg * 16; }
+
+__global__ __launch_bounds__(256) void k_quant_panels(const uint16_t* __restrict__ W, int64_t o,
+                                                      const float* __restrict__ c_w, int8_t* __restrict__ Wq) {
+    __shared__ __attribute__((aligned(16))) int8_t tile[kPanelCols * 64 + kPanelCols / 8 * 16];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int64_t p = blockIdx.y;                                        // rows 64 p .. 64 p + 63
+    const int64_t jb = static_cast<int64_t>(blockIdx.x) * kPanelCols;    // the block's first column
+    const int64_t ncols = o - jb < kPanelCols ? o - jb : kPanelCols;     // a multiple of 64
+    const int64_t j0 = jb + 8 * lane;
+    if (8 * lane < ncols) {
+        const uint4 s0 = *reinterpret_cast<const uint4*>(c_w + j0);
+        const uint4 s1 = *reinterpret_cast<const uint4*>(c_w + j0 + 4);
+        const float sc[8] = {__builtin_bit_cast(float, s0.x), __builtin_bit_cast(float, s0.y),
+                             __builtin_bit_cast(float, s0.z), __builtin_bit_cast(float, s0.w),
+                             __builtin_bit_cast(float, s1.x), __builtin_bit_cast(float, s1.y),
+                             __builtin_bit_cast(float, s1.z), __builtin_bit_cast(float, s1.w)};
+        const uint16_t* src = W + (p * 64 + 16 * wid) * o + j0;
+        uint4 v[16];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int q = t + 256 * p;
-            const int row = q >> 3, ch = q & 7;
-            uint4 v = *reinterpret_cast<const uint4*>(W + (r0 + row) * o + j0 + ch * 8);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int i = 0; i < 16; ++i) v[i] = load_chunk(src + i * o);
+        // codes of column 8 lane + e for the wavefront's 16 rows, 4 rows per word
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = half_bits_to_float((w[e >> 1] >> ((e & 1) * 16)) & 0xffffu);
-                tile[ch * 8 + e][row] = static_cast<int8_t>(quantize_one(x, scale[ch * 8 + e]));
+        for (int e = 0; e < 8; ++e) {
+            uint32_t q[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                int c[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t wd = word_of(v[4 * k + r], e >> 1);
+                    c[r] = round_code((e & 1) ? mul_half<true>(wd, sc[e]) : mul_half<false>(wd, sc[e]));
+                }
+                q[k] = pack_bytes(c[0], c[1], c[2], c[3]);
             }
+            *reinterpret_cast<uint4*>(tile + panel_lds_offset(8 * lane + e, wid)) = make_uint4(q[0], q[1], q[2], q[3]);
         }
-        __syncthreads();
-        const int col = t >> 2, seg = t & 3;
-        *reinterpret_cast<uint4*>(Wq + (r0 / 64) * o * 64 + (j0 + col) * 64 + seg * 16) =
-            *reinterpret_cast<const uint4*>(&tile[col][seg * 16]);
-        __syncthreads();
+    }
+    __syncthreads();
+    // the block's runs: bytes 16 i .. 16 i + 15 of the 64 ncols contiguous bytes
+    int8_t* dst = Wq + p * o * 64 + jb * 64;
+    const int nchunks = static_cast<int>(ncols * 4);
+#pragma unroll
+    for (int k = 0; k < kPanelCols * 4 / 256; ++k) {
+        const int i = t + 256 * k;
+        if (i < nchunks)
+            *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(tile + panel_lds_offset(i >> 2, i & 3));
     }
 }
 
@@ -688,11 +743,32 @@ hipError_t launch_pack_fp16_panels(const uint16_t* W, int64_t h, int64_t o, uint
     return hipGetLastError();
 }
 
+// The column constants of W (SC: Absmax scales, or MaxOnly maxima) via the
+// partial maxima kept in the Wq buffer.
+template <RowScale SC>
+hipError_t launch_col_constants(const uint16_t* W, int64_t h, int64_t o, int8_t* Wq, float* c_w, hipStream_t stream) {
+    const int nparts = static_cast<int>((h + kColRows - 1) / kColRows);
+    uint16_t* part = reinterpret_cast<uint16_t*>(Wq);
+    hipLaunchKernelGGL(k_col_absmax_part, dim3(static_cast<unsigned>((o + 511) / 512), static_cast<unsigned>(nparts)),
+                       dim3(256), 0, stream, W, h, o, part);
+    hipLaunchKernelGGL(k_col_absmax_reduce<SC>, dim3(static_cast<unsigned>((o + 255) / 256)), dim3(256), 0, stream,
+                       part, nparts, o, c_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_panels(const uint16_t* W, int64_t h, int64_t o, const float* c_w, int8_t* Wq,
+                               hipStream_t stream) {
+    hipLaunchKernelGGL(k_quant_panels, dim3(static_cast<unsigned>((o + kPanelCols - 1) / kPanelCols),
+                                            static_cast<unsigned>(h / 64)),
+                       dim3(256), 0, stream, W, o, c_w, Wq);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_cols(const uint16_t* W, int64_t h, int64_t o,
                                 int8_t* Wq, float* c_w, hipStream_t stream) {
-    hipLaunchKernelGGL(k_quant_cols<RowScale::Absmax>, dim3(static_cast<unsigned>(o / 64)), dim3(256), 0, stream,
-                       W, h, o, Wq, c_w);
-    return hipGetLastError();
+    hipError_t e = launch_col_constants<RowScale::Absmax>(W, h, o, Wq, c_w, stream);
+    if (e != hipSuccess) return e;
+    return launch_quant_panels(W, h, o, c_w, Wq, stream);
 }
 
 hipError_t launch_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h, const uint32_t* mask, int8_t* Xq,
@@ -728,11 +804,13 @@ hipError_t launch_quantize_tensorwise(const uint16_t* X, int64_t s, int64_t h, c
 
 hipError_t launch_quantize_weights_tensorwise(const uint16_t* W, int64_t h, int64_t o, int8_t* Wq, float* c_w,
                                               hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(o / 64)), block(256);
-    hipLaunchKernelGGL(k_quant_cols<RowScale::MaxOnly>, grid, block, 0, stream, W, h, o, Wq, c_w);
+    // column maxima, one constant over them in every entry, then the codes
+    hipError_t e = launch_col_constants<RowScale::MaxOnly>(W, h, o, Wq, c_w, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_tensor_scale, dim3(1), dim3(1024), 0, stream, c_w, o);
-    hipLaunchKernelGGL(k_quant_cols<RowScale::Given>, grid, block, 0, stream, W, h, o, Wq, c_w);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_quant_panels(W, h, o, c_w, Wq, stream);
 }
 
 }  // namespace i8mm
