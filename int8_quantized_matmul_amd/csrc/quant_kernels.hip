@@ -636,11 +636,17 @@ hipError_t launch_rows(const uint16_t* X, int64_t s, int64_t h, const uint32_t* 
                        int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
                        hipStream_t stream) {
     // Wavefronts per row: enough for ~4096 wavefronts in all (4 per SIMD),
-    // as long as each still holds its part of the row in registers.
+    // and more while a lane would hold over 8 chunks of its row (long rows:
+    // at 4096 x 12288 four wavefronts per row took the prologue from 54 to
+    // 42 us), as long as each still holds its part of the row in registers;
+    // rows too long even for four (over 32768 columns) take one wavefront
+    // per row that re-reads the row.
     const int64_t nch = h / 8;
+    auto per_lane_of = [&](int w) { return (nch + 64 * w - 1) / (64 * w); };
     int wpr = s >= 4096 ? 1 : s >= 2048 ? 2 : 4;
-    while (wpr > 1 && (nch + 64 * wpr - 1) / (64 * wpr) > 16) wpr = wpr == 4 ? 1 : 4;
-    const int64_t per_lane = (nch + 64 * wpr - 1) / (64 * wpr);
+    while (wpr < 4 && per_lane_of(wpr) > 8) wpr *= 2;
+    if (per_lane_of(wpr) > 16) wpr = 1;
+    const int64_t per_lane = per_lane_of(wpr);
     const dim3 grid(static_cast<unsigned>((s + 4 / wpr - 1) / (4 / wpr))), block(256);
     const size_t dyn = static_cast<size_t>(2 * (h / 32) * 4);
 #define I8MM_QROWS(CPL, W)                                                                                     \
@@ -649,16 +655,14 @@ hipError_t launch_rows(const uint16_t* X, int64_t s, int64_t h, const uint32_t* 
 #define I8MM_QROWS_W(W)                                  \
     if (per_lane <= 2) I8MM_QROWS(2, W);                 \
     else if (per_lane <= 4) I8MM_QROWS(4, W);            \
-    else if (per_lane <= 8) I8MM_QROWS(8, W);            \
-    else I8MM_QROWS(16, W);
+    else I8MM_QROWS(8, W);
     if (wpr == 4) {
-        I8MM_QROWS_W(4)
+        if (per_lane <= 8) { I8MM_QROWS_W(4) }
+        else I8MM_QROWS(16, 4);
     } else if (wpr == 2) {
         I8MM_QROWS_W(2)
-    } else if (per_lane <= 16) {
+    } else if (per_lane <= 8) {
         I8MM_QROWS_W(1)
-    } else if (per_lane <= 32) {
-        I8MM_QROWS(32, 1);
     } else {
         I8MM_QROWS(0, 1);
     }

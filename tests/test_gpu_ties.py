@@ -84,9 +84,9 @@ def _detect(X):
 # row re-read instead of held in registers) that the launch picks.
 ROW_SHAPES = [(64, 256, "W4 CPL2"), (64, 8192, "W4 CPL4"), (16, 16384, "W4 CPL8"), (4, 32768, "W4 CPL16"),
               (8, 65536, "W1 CPL0"),
-              (2048, 1024, "W2 CPL2"), (2048, 4096, "W2 CPL4"), (2048, 8192, "W2 CPL8"), (2048, 16384, "W2 CPL16"),
-              (4096, 512, "W1 CPL2"), (4096, 2048, "W1 CPL4"), (4096, 4096, "W1 CPL8"), (4096, 8192, "W1 CPL16"),
-              (4096, 8256, "W1 CPL32")]
+              (2048, 1024, "W2 CPL2"), (2048, 4096, "W2 CPL4"), (2048, 8192, "W2 CPL8"), (4096, 8192, "W2 CPL8 many"),
+              (4096, 512, "W1 CPL2"), (4096, 2048, "W1 CPL4"), (4096, 4096, "W1 CPL8"),
+              (4096, 12288, "W4 CPL8 many"), (4096, 8256, "W4 CPL8 ragged")]
 
 
 @pytest.mark.parametrize("s,h,label", ROW_SHAPES, ids=[c[2] for c in ROW_SHAPES])
