@@ -258,13 +258,21 @@ def run_decode(i8, torch, w, steps, warmup, dev, extras=True):
         v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
     n_out = int(v["n_out"].cpu()[0])
     weight_bytes = h * o + 2 * n_out * o + 4 * o
+    # the same forward as one launch (i8mm_forward_decode), interleaved with
+    # the three-launch step, best of three windows each
+    single = three = float("inf")
+    for _ in range(3):
+        three = min(three, timed_ms(torch, steps, lambda: i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C)))
+        single = min(single, timed_ms(torch, steps, lambda: i8.forward_decode(X, Wq, c_w, W, w.alpha,
+                                                                              workspace=ws, C=C)))
     if not extras:
-        return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, inputs=inp)
+        return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, inputs=inp,
+                    single=single, three=three)
     w8 = variant_ms(i8, torch, steps, X, Wq, c_w, W, w.alpha, ws, C)
     del Wq, c_w
     quant = quantiser_variants(i8, torch, steps, X, W, w.alpha, w8["base"])
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, w8=w8, quant=quant,
-                inputs=inp)
+                inputs=inp, single=single, three=three)
 
 
 def quantiser_variants(i8, torch, steps, X, W, alpha, fused_ms):
@@ -698,6 +706,7 @@ def main(argv=None):
             "avg_launch_ms": round(pre["gemm_ms"], 5),
         },
         "pct_int8_peak_effective": round(100 * tops / INT8_PEAK_TOPS, 2),
+        "prologue_ms": round(pre["step_ms"] - pre["gemm_ms"], 5),
         "step_ms_percentiles": pre["pct"],
         "clocks": clocks.summary(),
         "weight_conversion": {"ms": round(pre["conv_ms"], 4),
@@ -735,6 +744,9 @@ def main(argv=None):
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "product_kernel_ms": round(dec["gemm_ms"], 5),
             "product_kernel_weight_GB_per_s": round(gbs_gemm, 1),
+            "prologue_ms": round(dec["step_ms"] - dec["gemm_ms"], 5),
+            "single_launch": {"ms_per_step": round(dec["single"], 5), "three_launch_ms_per_step": round(dec["three"], 5),
+                              "vs_three_launch": round(dec["single"] / dec["three"], 3)},
         }
         if not args.no_extras:
             out["decode"].update({

@@ -416,6 +416,31 @@ i8mm_status i8mm_forward_zeropoint(const uint16_t* X, int64_t s, int64_t h, int6
  */
 i8mm_status i8mm_forward_workspace_layout(int64_t s, int64_t h, size_t offsets[7], int64_t* ldo);
 
+/* Largest row count of i8mm_forward_decode. */
+#define I8MM_DECODE_MAX_ROWS 16
+
+/*
+ * The whole per-forward path of i8mm_forward in ONE kernel launch, for few
+ * rows (1 <= s <= I8MM_DECODE_MAX_ROWS: token-by-token decoding). [DIGEST]
+ * "The Full LLM.int8() Algorithm", Steps 1-5; the single launch removes
+ * the per-layer detection and quantisation launches that [DIGEST]
+ * "Runtime Overhead Makes LLM.int8() Slower Than 16-Bit for Models Below
+ * ~13B Parameters" and [PY] "实验：无损扩展到 175B" name as the overhead
+ * of the method. Every block derives the outlier set and the row constants
+ * from all of X itself while its first weights are in flight, then streams
+ * its weight columns with the int8 operand of X quantised on the fly; no
+ * block waits for another. Results equal i8mm_forward's: the same codes,
+ * constants and int32 products, and C from the same epilogue arithmetic.
+ * Arguments as for i8mm_forward (W and bias may be NULL). The workspace
+ * (i8mm_forward_workspace_bytes(s, h) bytes, 256-byte aligned) receives the
+ * intermediates at the offsets of i8mm_forward_workspace_layout; its
+ * accumulator is neither read nor written. s > I8MM_DECODE_MAX_ROWS gives
+ * I8MM_EINVAL.
+ */
+i8mm_status i8mm_forward_decode(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                void* workspace, uint16_t* C, hipStream_t stream);
+
 /* Bytes of the static device scratch that i8mm_forward_noalloc uses as its
  * workspace (64 MiB per GPU the library runs on). */
 #define I8MM_NOALLOC_SCRATCH_BYTES 67108864

@@ -31,6 +31,7 @@ __all__ = [
     "forward_tensorwise",
     "forward_zeropoint",
     "forward_noalloc",
+    "forward_decode",
     "NOALLOC_SCRATCH_BYTES",
     "pack_fp16_weights",
     "fp16_gemm",
@@ -503,6 +504,28 @@ def forward_zeropoint(X: torch.Tensor, qw: Tuple[torch.Tensor, ...], W: torch.Te
         _dev(cs_w, "colsum_w", torch.int32, (o,)), _dev(W, "W", torch.float16, (h, o)), _bias_ptr(bias, o),
         _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
     _check(st, "forward_zeropoint")
+    return C
+
+
+def forward_decode(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Optional[torch.Tensor],
+                   alpha: float = 6.0, workspace: Optional[torch.Tensor] = None,
+                   C: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """forward() in one kernel launch for s <= 16 rows (i8mm_forward_decode);
+    the workspace receives the same intermediates as forward()'s."""
+    s, h = X.shape
+    o = Wq.shape[1]
+    if workspace is None:
+        workspace = forward_workspace(s, h, X.device)
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.float16, device=X.device)
+    need = _lib.i8mm_forward_workspace_bytes(s, h)
+    if workspace.numel() < need or workspace.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
+    st = _lib.i8mm_forward_decode(
+        _dev(X, "X", torch.float16), s, h, o, float(alpha), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)),
+        _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o), _bias_ptr(bias, o),
+        _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
+    _check(st, "forward_decode")
     return C
 
 

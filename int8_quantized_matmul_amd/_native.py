@@ -41,6 +41,7 @@ _SIGNATURES = {
     "i8mm_forward_zeropoint_workspace_bytes": (c_size, [c_i64, c_i64]),
     "i8mm_forward_zeropoint": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p,
                                        c_p]),
+    "i8mm_forward_decode": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     "i8mm_forward_noalloc": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p]),
     "i8mm_test_fail_product_launches": (None, [c_int]),
     "i8mm_version": (ctypes.c_char_p, []),

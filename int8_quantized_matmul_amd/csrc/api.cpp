@@ -403,6 +403,25 @@ i8mm_status i8mm_forward(const uint16_t* X, int64_t s, int64_t h, int64_t o, flo
     return run_forward(X, s, h, o, alpha, Wq, c_w, W, bias, workspace, C, stream);
 }
 
+i8mm_status i8mm_forward_decode(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                void* workspace, uint16_t* C, hipStream_t stream) {
+    if (!workspace) return I8MM_EINVAL;
+    if (i8mm_status a = check_forward_args(X, s, h, o, alpha, Wq, c_w, W, bias, C)) return a;
+    if (s > I8MM_DECODE_MAX_ROWS) return I8MM_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    size_t off[7], total;
+    int64_t ldo;
+    forward_layout(s, h, off, &ldo, &total);
+    char* ws = static_cast<char*>(workspace);
+    return launched(i8mm::launch_decode_fused(
+        X, s, h, o, alpha, Wq, c_w, W, bias, C, reinterpret_cast<uint32_t*>(ws + off[1]),
+        reinterpret_cast<int32_t*>(ws + off[2]), reinterpret_cast<int32_t*>(ws + off[3]),
+        reinterpret_cast<int8_t*>(ws + off[4]), reinterpret_cast<float*>(ws + off[5]),
+        reinterpret_cast<uint16_t*>(ws + off[6]), ldo, stream));
+}
+
 i8mm_status i8mm_forward_noalloc(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
                                  const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
                                  uint16_t* C, hipStream_t stream) {

@@ -36,6 +36,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "quant_common.h"
 
 namespace i8mm {
 namespace {
@@ -953,6 +954,242 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     }
 }
 
+// ------------------------------------------------------------------ single-launch decode forward
+// The whole forward of [DIGEST] "The Full LLM.int8() Algorithm" (Steps 1-5)
+// in one launch for few rows (s <= 16), where the two prologue launches of
+// the three-launch forward cost a tenth of a weight-streaming step
+// ([DIGEST] "Runtime Overhead Makes LLM.int8() Slower Than 16-Bit for
+// Models Below ~13B Parameters" names these per-layer steps as the overhead).
+// Every block works from X alone and waits for no other block:
+//  1. it issues its first weight batch, then scans all of X (s x h fp16, a
+//     few hundred KiB at most: L2 hits for all but the first blocks) for
+//     the outlier mask and the per-row maxima over the non-outlier columns
+//     (each thread sees every row of its 8-column chunks, so a chunk's
+//     flags are final before its values enter the row maxima);
+//  2. it streams its weight columns as k_gemm_decode does, with the int8
+//     operand of X quantised on the fly from X, the mask and the row
+//     constants in LDS;
+//  3. its epilogue takes the outlier columns by rank from the mask (binary
+//     search over the prefix counts) and reads their values from X and W.
+// Block 0 also writes the intermediates (mask, index list, |O|, c_x, Xq,
+// X_O with its zero padding) for inspection.
+
+// Column of rank k in O (its k-th member in ascending order), k < |O|, from
+// the LDS mask words and their exclusive prefix counts.
+__device__ __forceinline__ int kth_outlier(const uint32_t* smask, const int* pre, int nw, int k) {
+    int lo = 0, hi = nw - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= k)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    uint32_t bits = smask[lo];
+    for (int r = k - pre[lo]; r > 0; --r) bits &= bits - 1u;
+    return lo * 32 + __ffs(bits) - 1;
+}
+
+template <int NT, int kDecodeU = 2, int kDecodeSplit = 4>
+__global__ __launch_bounds__(256) void k_decode_fused(const uint16_t* __restrict__ X, int s, int64_t h, int64_t o,
+                                                      Threshold th, const int8_t* __restrict__ Wq,
+                                                      const float* __restrict__ c_w, const uint16_t* __restrict__ W,
+                                                      const uint16_t* __restrict__ bias, uint16_t* __restrict__ C,
+                                                      uint32_t* __restrict__ mask_out, int32_t* __restrict__ idx_out,
+                                                      int32_t* __restrict__ n_out_out, int8_t* __restrict__ Xq_out,
+                                                      float* __restrict__ c_x_out, uint16_t* __restrict__ X_O_out,
+                                                      int64_t ldo) {
+    extern __shared__ uint32_t dyn[];   // mask words [nw], then their exclusive prefix counts [nw]
+    __shared__ v4i red[kDecodeSplit][NT][64];
+    __shared__ uint32_t rmax[4][16];
+    __shared__ float cx[16];
+    __shared__ int wsum[4];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int nw = static_cast<int>(h / 32);
+    uint32_t* smask = dyn;
+    int* pre = reinterpret_cast<int*>(dyn + nw);
+    const int64_t obase = static_cast<int64_t>(blockIdx.x) * 16 * NT;
+    const int r16 = lane & 15, g = lane >> 4;
+    const bool first = blockIdx.x == 0;
+
+    // The block's weight columns, as in k_gemm_decode.
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq + obase * 64, static_cast<uint32_t>(h * o - obase * 64));
+    uint32_t vA[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) vA[nt] = static_cast<uint32_t>((nt * 16 + r16) * 64 + g * 16);
+    const int64_t nsteps = h / 64;
+    const int64_t per = ((nsteps + kDecodeSplit - 1) / kDecodeSplit + kDecodeU - 1) / kDecodeU * kDecodeU;
+    const int64_t st0 = wid * per < nsteps ? wid * per : nsteps;
+    const int64_t st1 = st0 + per < nsteps ? st0 + per : nsteps;
+    v4i a0[kDecodeU][NT], a1[kDecodeU][NT];
+    auto load_w = [&](v4i (&a)[kDecodeU][NT], int64_t stb) {
+#pragma unroll
+        for (int u = 0; u < kDecodeU; ++u) {
+            const bool ok = stb + u < st1;
+            const uint32_t kA = ok ? static_cast<uint32_t>((stb + u) * o * 64) : 0u;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) a[u][nt] = buf_load16_nt(rA, ok ? vA[nt] : kOutOfRange, kA);
+        }
+    };
+    load_w(a0, st0);
+
+    // 1. Scan of X: mask, and the packed |x| maxima of each row over this
+    // thread's non-outlier columns (rows past s read zero from the resource,
+    // which neither flags a column nor raises a maximum).
+    for (int w = t; w < nw; w += 256) smask[w] = 0u;
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rX = range_rsrc(X, static_cast<uint32_t>(2 * static_cast<int64_t>(s) * h));
+    uint32_t rm[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rm[i] = 0u;
+    for (int64_t c = t; c < h / 8; c += 256) {
+        uint4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            v[i] = i < s ? load_chunk_rsrc(rX, static_cast<uint32_t>(2 * (i * h + c * 8))) : make_uint4(0, 0, 0, 0);
+        uint4 d = detect_init();
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (i < s) detect_fold(d, v[i], th.thr2);
+        const uint32_t f = detect_flags(d, th.span);
+        if (f) atomicOr(&smask[c >> 2], f << ((c & 3) * 8));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rm[i] = chunk_absmax_fold(chunk_clear(v[i], f), rm[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        uint32_t m2 = rm[i];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1)
+            m2 = pk_max_u16(m2, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2), off, kWave)));
+        if (lane == 0) rmax[wid][i] = m2;
+    }
+    __syncthreads();
+    if (t < 16)
+        cx[t] = absmax_scale(absmax_value(pk_max_u16(pk_max_u16(rmax[0][t], rmax[1][t]),
+                                                     pk_max_u16(rmax[2][t], rmax[3][t]))));
+    const int n = block_mask_prefix(smask, pre, nw, wsum, 256);   // its barriers also publish cx
+
+    if (first) {
+        emit_outlier_set(smask, pre, nw, n, mask_out, idx_out, n_out_out, 256);
+        if (t < s) c_x_out[t] = cx[t];
+        // X_O: the outlier columns of every row by rank, zero up to a multiple of 32
+        for (int w = t; w < nw; w += 256) {
+            int r = pre[w];
+            for (uint32_t b = smask[w]; b; b &= b - 1u, ++r) {
+                const int64_t col = static_cast<int64_t>(w) * 32 + __ffs(b) - 1;
+                for (int i = 0; i < s; ++i) X_O_out[i * ldo + r] = X[i * h + col];
+            }
+        }
+        const int npad = (n + 31) & ~31;
+        for (int k = n + t; k < npad; k += 256)
+            for (int i = 0; i < s; ++i) X_O_out[i * ldo + k] = 0;
+    }
+
+    // 2. Weight stream with the int8 operand of X made on the fly: lane
+    // (r16, g) of step st holds the codes of X[r16, 64 st + 16 g .. + 15].
+    uint4 x0[kDecodeU][2], x1[kDecodeU][2];
+    auto load_x = [&](uint4 (&x)[kDecodeU][2], int64_t stb) {
+#pragma unroll
+        for (int u = 0; u < kDecodeU; ++u) {
+            const bool ok = stb + u < st1;
+            const uint32_t off = ok ? static_cast<uint32_t>(2 * (r16 * h + (stb + u) * 64 + 16 * g)) : kOutOfRange;
+            x[u][0] = load_chunk_rsrc(rX, off);
+            x[u][1] = load_chunk_rsrc(rX, off + 16);
+        }
+    };
+    const float scr = cx[r16];
+    auto codes = [&](const uint4 (&x)[kDecodeU][2], int64_t stb, v4i (&b)[kDecodeU]) {
+#pragma unroll
+        for (int u = 0; u < kDecodeU; ++u) {
+            b[u] = v4i{0, 0, 0, 0};
+            if (stb + u < st1) {
+                const int64_t col = (stb + u) * 64 + 16 * g;
+                const uint32_t bits = (smask[col >> 5] >> (col & 31)) & 0xffffu;
+                const uint2 q0 = chunk_quantize(chunk_clear(x[u][0], bits & 0xffu), scr);
+                const uint2 q1 = chunk_quantize(chunk_clear(x[u][1], bits >> 8), scr);
+                b[u] = v4i{static_cast<int>(q0.x), static_cast<int>(q0.y), static_cast<int>(q1.x),
+                           static_cast<int>(q1.y)};
+                if (first && r16 < s) *reinterpret_cast<v4i*>(Xq_out + r16 * h + col) = b[u];
+            }
+        }
+    };
+    v4i acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
+    auto mma = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU]) {
+#pragma unroll
+        for (int u = 0; u < kDecodeU; ++u)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][nt], b[u], acc[nt], 0, 0, 0);
+    };
+    v4i b[kDecodeU];
+    load_x(x0, st0);
+    for (int64_t stb = st0; stb < st1; stb += 2 * kDecodeU) {
+        load_w(a1, stb + kDecodeU);
+        load_x(x1, stb + kDecodeU);
+        codes(x0, stb, b);
+        mma(a0, b);
+        load_w(a0, stb + 2 * kDecodeU);
+        load_x(x0, stb + 2 * kDecodeU);
+        codes(x1, stb + kDecodeU, b);
+        mma(a1, b);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) red[wid][nt][lane] = acc[nt];
+    __syncthreads();
+    if (wid >= NT) return;
+    const int nt = wid;
+    v4i sum = red[0][nt][lane];
+#pragma unroll
+    for (int w = 1; w < kDecodeSplit; ++w) sum += red[w][nt][lane];
+
+    // 3. Epilogue (lane layout of a 16x16 accumulator: register r holds
+    // D[o = 4 g + r][s = r16]).
+    const int64_t ocol0 = obase + nt * 16;
+    const int64_t ocol = ocol0 + 4 * g;
+    const float inv_x = __builtin_amdgcn_rcpf(scr);
+    const v4f cw = *reinterpret_cast<const v4f*>(c_w + ocol);
+    v4f f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+    // Outlier product X_O W[idx, :], 32 outlier columns per fp16 MFMA.
+    {
+        const int64_t wcol = ocol0 + r16;   // this lane's column of W in the operand layout
+        const float inv_cw = inverse_scale(W == nullptr ? c_w[wcol] : 1.0f);
+        for (int kb = 0; kb * 32 < n; ++kb) {
+            v8h wa, xb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = kb * 32 + 8 * g + e;
+                uint16_t wbits = 0, xbits = 0;
+                if (k < n) {
+                    const int id = kth_outlier(smask, pre, nw, k);
+                    wbits = W != nullptr ? W[static_cast<int64_t>(id) * o + wcol]
+                                         : dequantized_weight(Wq, inv_cw, id, wcol, o);
+                    xbits = r16 < s ? X[r16 * h + id] : static_cast<uint16_t>(0);
+                }
+                wa[e] = __builtin_bit_cast(_Float16, wbits);
+                xb[e] = __builtin_bit_cast(_Float16, xbits);
+            }
+            f = __builtin_amdgcn_mfma_f32_16x16x32_f16(wa, xb, f, 0, 0, 0);
+        }
+    }
+    if (bias != nullptr) {
+        const uint2 b4 = *reinterpret_cast<const uint2*>(bias + ocol);
+        f[0] += half_bits_to_float(b4.x & 0xffffu);
+        f[1] += half_bits_to_float(b4.x >> 16);
+        f[2] += half_bits_to_float(b4.y & 0xffffu);
+        f[3] += half_bits_to_float(b4.y >> 16);
+    }
+    if (r16 < s) {
+        const uint32_t lo = pack_half2(f[0], f[1]);
+        const uint32_t hi = pack_half2(f[2], f[3]);
+        *reinterpret_cast<uint2*>(C + r16 * o + ocol) = make_uint2(lo, hi);
+    }
+}
+
 // ------------------------------------------------------------------ outlier product alone
 // One wavefront per 16x16 tile of C_O (fp32).
 __global__ __launch_bounds__(256) void k_outlier_only(const uint16_t* __restrict__ X_O, int64_t ldo,
@@ -1021,6 +1258,18 @@ hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, in
     hipLaunchKernelGGL((k_gemm_prefill<GemmOut::Fp16Dense>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
                        reinterpret_cast<const int8_t*>(X), reinterpret_cast<const int8_t*>(Wp), s, 2 * h, o,
                        nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, C, nullptr, 0, ZpArgs{});
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_fused(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha, const int8_t* Wq,
+                               const float* c_w, const uint16_t* W, const uint16_t* bias, uint16_t* C, uint32_t* mask,
+                               int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
+                               hipStream_t stream) {
+    constexpr int NT = 4;
+    const size_t dyn = static_cast<size_t>(8 * (h / 32));
+    hipLaunchKernelGGL((k_decode_fused<NT>), dim3(static_cast<unsigned>(o / (16 * NT))), dim3(256), dyn, stream, X,
+                       static_cast<int>(s), h, o, make_threshold(alpha), Wq, c_w, W, bias, C, mask, idx, n_out, Xq,
+                       c_x, X_O, ldo);
     return hipGetLastError();
 }
 

@@ -97,6 +97,13 @@ hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, in
 
 hipError_t launch_pack_fp16_panels(const uint16_t* W, int64_t h, int64_t o, uint16_t* Wp, hipStream_t stream);
 
+// The whole forward in one launch for s <= 16 (k_decode_fused); the
+// intermediates go to mask .. X_O (block 0 writes them).
+hipError_t launch_decode_fused(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha, const int8_t* Wq,
+                               const float* c_w, const uint16_t* W, const uint16_t* bias, uint16_t* C, uint32_t* mask,
+                               int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
+                               hipStream_t stream);
+
 hipError_t launch_outlier_matmul(const uint16_t* X_O, int64_t ldo,
                                  const int32_t* idx, const int32_t* n_out,
                                  const uint16_t* W, int64_t s, int64_t o,

@@ -22,35 +22,6 @@ namespace i8mm {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Outlier test ([DIGEST] "The Full LLM.int8() Algorithm", Step 1: column j
-// is an outlier iff some |X_ij| >= alpha). With thr = the smallest fp16 bit
-// pattern in [0, inf] whose value is >= alpha, |x| >= alpha holds iff
-// thr <= bits(|x|) <= inf (NaN fails both tests), i.e. iff
-// (bits(|x|) - thr) mod 2^16 <= inf - thr. A column's flag is therefore the
-// running minimum of that difference over the rows, tested once at the end.
-struct Threshold {
-    uint32_t thr2;    // thr in both halves
-    uint32_t span;    // inf - thr
-};
-
-__device__ __forceinline__ void detect_fold(uint4& d, const uint4& v, uint32_t thr2) {
-    d.x = pk_min_u16(d.x, pk_sub_u16(v.x & kAbs2, thr2));
-    d.y = pk_min_u16(d.y, pk_sub_u16(v.y & kAbs2, thr2));
-    d.z = pk_min_u16(d.z, pk_sub_u16(v.z & kAbs2, thr2));
-    d.w = pk_min_u16(d.w, pk_sub_u16(v.w & kAbs2, thr2));
-}
-
-__device__ __forceinline__ uint4 detect_init() { return make_uint4(~0u, ~0u, ~0u, ~0u); }
-
-// Bit e set iff column e of the chunk is flagged.
-__device__ __forceinline__ uint32_t detect_flags(const uint4& d, uint32_t span) {
-    uint32_t f = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f |= (((word_of(d, e >> 1) >> ((e & 1) * 16)) & 0xffffu) <= span ? 1u : 0u) << e;
-    return f;
-}
-
-// ---------------------------------------------------------------------------
 // Fill a uint32 array (used to clear the outlier mask before detection; a
 // kernel rather than a memset so that the sequence is graph-capture safe).
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
@@ -603,25 +574,6 @@ __global__ __launch_bounds__(256) void k_pack_fp16_panels(const uint16_t* __rest
 }  // namespace
 
 namespace {
-
-// Exact fp16 value of a bit pattern in [0, 0x7c00].
-float half_value(uint32_t b) {
-    const int e = static_cast<int>(b >> 10), m = static_cast<int>(b & 0x3ffu);
-    if (e == 31) return INFINITY;
-    return e == 0 ? std::ldexp(static_cast<float>(m), -24) : std::ldexp(static_cast<float>(m + 1024), e - 25);
-}
-
-// The smallest fp16 bit pattern in [0, inf] whose value is >= alpha (alpha
-// >= 0, not NaN); the values of [0, inf] increase with their patterns.
-Threshold make_threshold(float alpha) {
-    uint32_t lo = 0, hi = kInfBits;
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi) / 2;
-        if (half_value(mid) >= alpha) hi = mid;
-        else lo = mid + 1;
-    }
-    return Threshold{lo | (lo << 16), kInfBits - lo};
-}
 
 hipError_t launch_detect_into(const uint16_t* X, int64_t s, int64_t h, float alpha, uint32_t* mask,
                               hipStream_t stream) {

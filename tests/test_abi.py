@@ -97,6 +97,15 @@ def test_mixed_matmul_and_gemm_reject():
     assert lib.i8mm_outlier_matmul(P, 64, P, P, P, 4, 64, 64, MIS, None) == -1
 
 
+def test_single_launch_decode_rejects():
+    lib = _lib()
+    ws = ctypes.c_void_p(1 << 20)
+    # more rows than the single launch takes; null workspace; misaligned bias
+    assert lib.i8mm_forward_decode(P, 17, 64, 64, 6.0, P, P, P, None, ws, P, None) == -1
+    assert lib.i8mm_forward_decode(P, 8, 64, 64, 6.0, P, P, P, None, None, P, None) == -1
+    assert lib.i8mm_forward_decode(P, 8, 64, 64, 6.0, P, P, P, MIS, ws, P, None) == -1
+
+
 def test_forward_rejects_unaligned_workspace():
     lib = _lib()
     ws = ctypes.c_void_p((1 << 20) + 16)
