@@ -16,14 +16,14 @@ expansion decode layer (X [8, 12288], W [12288, 49152]) against 8 TB/s HBM;
 `all_configs` times every other workload (tiny, the OPT-6.7B-style FFN
 prefill and the nine outlier-density sweep points), each with its own CPU
 oracle baseline; `cpu_baseline` times the CPU oracle on host cores on a
-bounded sample of the headline layer; `clocks` are the GPU clocks sampled
-during the timed steps.
+bounded sample of the headline layer; `clocks` are the GPU clocks and socket
+power read from the driver's metrics table over a clock window of the same
+step (the table is refreshed every few hundred ms).
 """
 
 from __future__ import annotations
 
 import argparse
-import contextlib
 import json
 import os
 import sys
@@ -190,24 +190,23 @@ def run_prefill(i8, torch, w, steps, warmup, dev, clocks=None, extras=True):
         step()
     torch.cuda.synchronize()
     t0, t1 = _events(torch)
-    with clocks if clocks is not None else contextlib.nullcontext():
-        wall0 = time.perf_counter()
-        t0.record()
-        for _ in range(steps):
-            step()
-        t1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
     step_ms = t0.elapsed_time(t1) / steps
-    with clocks if clocks is not None else contextlib.nullcontext():
-        gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
-            v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
+    gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
+        v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
+    clk = clock_window(torch, step, step_ms, clocks) if clocks is not None else None
 
     n_out = int(v["n_out"].cpu()[0])
     pct = step_percentiles(torch, steps, step)
     if not extras:
         return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out, inputs=inp,
-                    pct=pct)
+                    pct=pct, clk=clk)
     table5 = table5_set(i8, torch, X, W, Wq, c_w, w.alpha, steps)
     # MALL-cold steps: rotate over weight copies whose total exceeds the
     # 256 MB Infinity Cache, so every step streams its weights from HBM
@@ -230,10 +229,10 @@ def run_prefill(i8, torch, w, steps, warmup, dev, clocks=None, extras=True):
     step()
     torch.cuda.synchronize()
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out,
-                inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies, w8=w8, quant=quant)
+                inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies, w8=w8, quant=quant, clk=clk)
 
 
-def run_decode(i8, torch, w, steps, warmup, dev, extras=True):
+def run_decode(i8, torch, w, steps, warmup, dev, extras=True, clocks=None):
     from workloads import make_inputs
     inp = make_inputs(w)
     X = torch.from_numpy(inp["X"]).to(dev)
@@ -256,6 +255,10 @@ def run_decode(i8, torch, w, steps, warmup, dev, extras=True):
     step_ms = t0.elapsed_time(t1) / steps
     gemm_ms = product_kernel_ms(i8, torch, steps, lambda: i8.int8_mixed_matmul(
         v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
+    clk = None
+    if clocks is not None:
+        clocks.samples.clear()
+        clk = clock_window(torch, lambda: i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C), step_ms, clocks)
     n_out = int(v["n_out"].cpu()[0])
     weight_bytes = h * o + 2 * n_out * o + 4 * o
     # the same forward as one launch (i8mm_forward_decode), interleaved with
@@ -267,12 +270,12 @@ def run_decode(i8, torch, w, steps, warmup, dev, extras=True):
                                                                               workspace=ws, C=C)))
     if not extras:
         return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, inputs=inp,
-                    single=single, three=three)
+                    single=single, three=three, clk=clk)
     w8 = variant_ms(i8, torch, steps, X, Wq, c_w, W, w.alpha, ws, C)
     del Wq, c_w
     quant = quantiser_variants(i8, torch, steps, X, W, w.alpha, w8["base"])
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, w8=w8, quant=quant,
-                inputs=inp, single=single, three=three)
+                inputs=inp, single=single, three=three, clk=clk)
 
 
 def quantiser_variants(i8, torch, steps, X, W, alpha, fused_ms):
@@ -418,7 +421,7 @@ def run_all_configs(i8, torch, dev, steps, names, host=None, cpu_budget=0.0):
             del X, W, Wq, c_w, ws, v, C
             torch.cuda.empty_cache()
             if cpu_budget > 0:
-                row["cpu_baseline"] = cpu_baseline(w, inp, cpu_budget, host)
+                row["cpu_baseline"] = cpu_baseline(w, inp, cpu_budget, host, rows=512)
             _log(f"[configs] {row}")
             rows.append(row)
             del inp
@@ -462,35 +465,31 @@ def _sample_work(w, rows, cols, n_out):
     return 2.0 * rows * w.h * cols / 1e12, "TOPS"
 
 
-def cpu_baseline(w, inputs, budget_s, host, reps=3):
+def cpu_baseline(w, inputs, budget_s, host, rows=None, reps=3):
     """Time the CPU oracle (as it stands) on a bounded sample of one workload.
 
-    The sample is the first R rows of X against the first Q columns of W
-    (columns are independent: each output column needs only its own weight
-    column and constant); their load-time weight conversion is done first
-    and not timed. One untimed warm-up, then timed repetitions of
-    oracle.forward; R (Q is at most 2048) is chosen from a probe so that
-    the timed repetitions take about budget_s (with few rows, all rows and
-    more repetitions). The result is scaled to the
-    metric's unit: effective TOPS 2 R h Q / t (prefill), or weight bytes
-    (h Q + 2 |O| Q + 4 Q) / t in GB/s (decode).
+    The sample is the first R rows of X (all rows, or `rows`) against the
+    first Q = min(o, 2048) columns of W (columns are independent: each
+    output column needs only its own weight column and constant); their
+    load-time weight conversion is done first and not timed. One untimed
+    warm-up forward, then at least `reps` timed repetitions of
+    oracle.forward, more while they fit in budget_s. A fixed sample per
+    workload keeps the oracle's per-call costs (weight-side conversions
+    that do not depend on R) the same share of every figure. The result is
+    scaled to the metric's unit: effective TOPS 2 R h Q / t (prefill), or
+    weight bytes (h Q + 2 |O| Q + 4 Q) / t in GB/s (decode).
     """
     import oracle
     X, W = inputs["X"], inputs["W"]
     n_out = int(oracle.outlier_columns(X, w.alpha)[2])
     cols = min(w.o, 2048)
+    rows = min(w.s, rows or w.s)
     Wq_t, c_w = oracle.quantize_colwise_weights(W[:, :cols])     # load time, not timed
-    probe_rows = min(w.s, 64)
-    t = time.perf_counter()
-    oracle.forward(X[:probe_rows], W[:, :cols], w.alpha, Wq_t=Wq_t, c_w=c_w)
-    probe = max(time.perf_counter() - t, 1e-6)
-    if w.s <= probe_rows:
-        rows = w.s                                   # every row; more repetitions instead
-        reps = max(reps, int(budget_s / probe))
-    else:
-        rows = int(min(w.s, max(16, probe_rows * budget_s / reps / probe)))
     Xs, Ws = X[:rows], W[:, :cols]
+    t = time.perf_counter()
     oracle.forward(Xs, Ws, w.alpha, Wq_t=Wq_t, c_w=c_w)              # warm-up
+    warm = max(time.perf_counter() - t, 1e-6)
+    reps = max(reps, int(budget_s / warm))
     t = time.perf_counter()
     for _ in range(reps):
         oracle.forward(Xs, Ws, w.alpha, Wq_t=Wq_t, c_w=c_w)
@@ -511,11 +510,14 @@ def cpu_baseline(w, inputs, budget_s, host, reps=3):
 
 
 class ClockSampler:
-    """Samples the GPU's graphics (sclk) and memory (mclk) clocks from the
-    driver's metrics table (amdsmi) in a background thread while a timed
-    region runs. Reading the table touches no GPU queue."""
+    """Samples the GPU's graphics clock (per XCD), memory clock and socket
+    power from the driver's metrics table (amdsmi) in a background thread.
+    The table is refreshed by the power-management firmware only every few
+    hundred ms, so the sampler is run over a clock window of >= 1 s of the
+    same step back to back, and the distinct snapshots are reported.
+    Reading the table touches no GPU queue."""
 
-    def __init__(self, torch, period_s=0.002):
+    def __init__(self, torch, period_s=0.01):
         self.period = period_s
         self.samples = []
         self.error = None
@@ -527,11 +529,9 @@ class ClockSampler:
             handles = amdsmi.amdsmi_get_processor_handles()
             self.handle = handles[0] if handles else None
             try:   # the handle of the GPU torch uses, by PCI bus
-                prop = torch.cuda.get_device_properties(0)
-                want = int(getattr(prop, "pci_bus_id"))
+                want = int(getattr(torch.cuda.get_device_properties(0), "pci_bus_id"))
                 for hd in handles:
-                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(hd)
-                    if int(bdf.split(":")[1], 16) == want:
+                    if int(amdsmi.amdsmi_get_gpu_device_bdf(hd).split(":")[1], 16) == want:
                         self.handle = hd
                         break
             except Exception:
@@ -550,17 +550,13 @@ class ClockSampler:
             return [float(x) for x in vals if isinstance(x, (int, float)) and 0 < x < 0xFFFF]
 
         gfx = nums(m.get("current_gfxclks", [])) or nums(m.get("current_gfxclk"))
-        mem = nums(m.get("current_uclk"))
-        return (sum(gfx) / len(gfx) if gfx else None, mem[0] if mem else None)
+        return (tuple(gfx), (nums(m.get("current_uclk")) or [None])[0],
+                (nums(m.get("current_socket_power")) or [None])[0])
 
     def __enter__(self):
         import threading
         self._stop = threading.Event()
-        if self.error is None:
-            try:
-                self.read()
-            except Exception as e:
-                self.error = repr(e)
+        self._thread = None
         if self.error is None:
             def loop():
                 while not self._stop.is_set():
@@ -576,21 +572,51 @@ class ClockSampler:
 
     def __exit__(self, *exc):
         self._stop.set()
-        if getattr(self, "_thread", None) is not None:
+        if self._thread is not None:
             self._thread.join()
         return False
 
-    def summary(self):
-        def stats(vals):
-            vals = sorted(v for v in vals if v is not None)
-            if not vals:
-                return None
-            return {"min": vals[0], "median": vals[len(vals) // 2], "max": vals[-1], "samples": len(vals)}
+    def summary(self, window_s=None, steps=None):
         if self.error is not None and not self.samples:
             return {"error": self.error}
-        return {"sclk_MHz": stats(s for s, _ in self.samples), "mclk_MHz": stats(m for _, m in self.samples),
-                "source": "amdsmi gpu_metrics current_gfxclk(s) / current_uclk, polled every "
-                          f"{self.period * 1e3:.0f} ms during the timed steps"}
+        # the table holds each snapshot for a while: keep the distinct ones,
+        # and drop the idle snapshot the window may start with
+        snaps = []
+        for smp in self.samples:
+            if not snaps or smp != snaps[-1]:
+                snaps.append(smp)
+        busy = [x for x in snaps if x[0] and sum(x[0]) / len(x[0]) > 500.0] or snaps
+
+        def med(vals):
+            vals = sorted(v for v in vals if v is not None)
+            return vals[len(vals) // 2] if vals else None
+
+        return {"sclk_MHz_median": med(sum(x[0]) / len(x[0]) for x in busy if x[0]),
+                "sclk_MHz_per_xcd_last": list(busy[-1][0]) if busy and busy[-1][0] else None,
+                "mclk_MHz_median": med(x[1] for x in busy),
+                "socket_power_W_median": med(x[2] for x in busy),
+                "snapshots": len(busy), "polls": len(self.samples),
+                "window_s": window_s, "window_steps": steps,
+                "source": "amdsmi gpu_metrics current_gfxclks / current_uclk / current_socket_power, polled every "
+                          f"{self.period * 1e3:.0f} ms over a window of the same step run back to back right after "
+                          "the timed steps (the firmware refreshes the table every few hundred ms, longer than the "
+                          "timed steps)"}
+
+
+def clock_window(torch, fn, step_ms, clocks, seconds=1.5):
+    """Runs fn back to back for about `seconds` under the clock sampler."""
+    n = max(50, int(seconds * 1e3 / max(step_ms, 1e-3)))
+    with clocks:
+        t0 = time.perf_counter()
+        done = 0
+        while done < n:
+            k = min(200, n - done)
+            for _ in range(k):
+                fn()
+            torch.cuda.synchronize()
+            done += k
+        el = time.perf_counter() - t0
+    return clocks.summary(round(el, 3), n)
 
 
 CONFIG_NAMES = ["tiny", "opt67b_ffn1_prefill", "sweep_o0"] + \
@@ -708,7 +734,7 @@ def main(argv=None):
         "pct_int8_peak_effective": round(100 * tops / INT8_PEAK_TOPS, 2),
         "prologue_ms": round(pre["step_ms"] - pre["gemm_ms"], 5),
         "step_ms_percentiles": pre["pct"],
-        "clocks": clocks.summary(),
+        "clocks": pre["clk"],
         "weight_conversion": {"ms": round(pre["conv_ms"], 4),
                               "GB_per_s_3ho": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1),
                               "GB_per_s_5ho_moved": round(5.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1),
@@ -734,7 +760,7 @@ def main(argv=None):
     if not args.no_decode:
         wd = get_config(args.decode_workload)
         _log(f"[bench] decode workload {wd.name}: s={wd.s} h={wd.h} o={wd.o}")
-        dec = run_decode(i8, torch, wd, args.steps, args.warmup, dev, extras=not args.no_extras)
+        dec = run_decode(i8, torch, wd, args.steps, args.warmup, dev, extras=not args.no_extras, clocks=clocks)
         gbs = dec["weight_bytes"] / (dec["step_ms"] * 1e-3) / 1e9
         gbs_gemm = dec["weight_bytes"] / (dec["gemm_ms"] * 1e-3) / 1e9
         out["decode"] = {
@@ -745,6 +771,7 @@ def main(argv=None):
             "product_kernel_ms": round(dec["gemm_ms"], 5),
             "product_kernel_weight_GB_per_s": round(gbs_gemm, 1),
             "prologue_ms": round(dec["step_ms"] - dec["gemm_ms"], 5),
+            "clocks": dec["clk"],
             "single_launch": {"ms_per_step": round(dec["single"], 5), "three_launch_ms_per_step": round(dec["three"], 5),
                               "vs_three_launch": round(dec["single"] / dec["three"], 3)},
         }
