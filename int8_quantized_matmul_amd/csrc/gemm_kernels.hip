@@ -82,23 +82,24 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // a per-lane offset past every 
 
 // Block -> output tile. Blocks are dealt to the 8 XCDs round robin (block b
 // runs on XCD b % 8), and each XCD is given one contiguous run of a grouped
-// tile order: column groups of kGroup weight tiles that span every row tile,
-// row by row inside a group. The ~32 tiles an XCD runs at once then cover
-// about 4 row tiles x 8 weight tiles, i.e. ~12 operand panels streamed
-// through its 4 MiB L2 per round instead of every row panel of Xq (an order
-// with rows fastest made each round re-fetch all of Xq). Block and tile
-// indices are 32-bit (as the grid is), which keeps the index arithmetic
-// short ahead of the first loads.
-constexpr uint32_t kGroup = 8;
-
-__device__ __forceinline__ void grouped_tile(uint32_t b, uint32_t nb, uint32_t n_ts, uint32_t n_to,
+// tile order: column groups of `group` weight tiles that span every row
+// tile, row by row inside a group. The ~32 tiles an XCD runs at once then
+// cover about 32 / group row tiles x group weight tiles, i.e. ~12 operand
+// panels streamed through its 4 MiB L2 per round (an order with rows
+// fastest made each round re-fetch every row panel of Xq). Over the whole
+// product the weights are fetched (row tiles / (32 / group)) times and Xq
+// (weight tiles / group) times, so the launch takes group 4 when the int8
+// weights exceed the 256 MiB Infinity Cache (fewer passes over them) and 8
+// otherwise. Block and tile indices are 32-bit (as the grid is), which
+// keeps the index arithmetic short ahead of the first loads.
+__device__ __forceinline__ void grouped_tile(uint32_t b, uint32_t nb, uint32_t n_ts, uint32_t n_to, uint32_t group,
                                              uint32_t& ts, uint32_t& to) {
     const uint32_t q = nb / 8, r = nb % 8, x = b % 8, i = b / 8;
     const uint32_t t = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;   // place in the grouped order
-    const uint32_t per = kGroup * n_ts;
+    const uint32_t per = group * n_ts;
     const uint32_t g = t / per, j = t % per;
-    const uint32_t c0 = g * kGroup;
-    const uint32_t w = n_to - c0 < kGroup ? n_to - c0 : kGroup;
+    const uint32_t c0 = g * group;
+    const uint32_t w = n_to - c0 < group ? n_to - c0 : group;
     ts = j / w;
     to = c0 + j % w;
 }
@@ -318,7 +319,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     const uint16_t* __restrict__ X_O, int64_t ldo,
                     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out,
                     const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ Cout,
-                    uint32_t* __restrict__ clear, int clear_words, ZpArgs zp) {
+                    uint32_t* __restrict__ clear, int clear_words, ZpArgs zp, uint32_t group) {
     __shared__ v4i A0[kBuf], A1[kBuf], B0[kBuf], B1[kBuf];
     __shared__ __attribute__((aligned(16))) uint16_t olds[2 * kSlice];
     __shared__ __attribute__((aligned(16))) float scl[512];   // c_x of the tile's rows, then c_w of its columns
@@ -334,7 +335,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     const uint32_t n_ts = static_cast<uint32_t>((s + kTS - 1) / kTS);
     const uint32_t n_to = static_cast<uint32_t>((o + kTO - 1) / kTO);
     uint32_t ts_u, to_u;
-    grouped_tile(blockIdx.x, gridDim.x, n_ts, n_to, ts_u, to_u);
+    grouped_tile(blockIdx.x, gridDim.x, n_ts, n_to, group, ts_u, to_u);
     const int64_t ts_i = ts_u, to_i = to_u;
     const int64_t o0 = to_i * kTO, s0 = ts_i * kTS;
     const int64_t o_rows = o - o0 < kTO ? o - o0 : kTO;
@@ -1211,6 +1212,14 @@ __global__ __launch_bounds__(256) void k_outlier_only(const uint16_t* __restrict
     if (srow < s) *reinterpret_cast<v4f*>(C_O + srow * o + ocol) = f;
 }
 
+// Weight tiles per group of the grouped tile order (grouped_tile): 4 when
+// the weight operand (hb reduction bytes per column) exceeds the Infinity
+// Cache, else 8. On 4096 x 12288 x 36864 (453 MB of weights) 4 took the
+// product from 1554 to 1494 us; on 4096 x 8192 x 28672 (235 MB) 8 is 2 %
+// faster than 4.
+constexpr int64_t kMallBytes = int64_t(256) << 20;
+uint32_t tile_group(int64_t hb, int64_t o) { return hb * o > kMallBytes ? 4u : 8u; }
+
 template <GemmOut MODE>
 hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, int64_t ldo,
                        const int32_t* idx, const int32_t* n_out, const int8_t* Wq, const float* c_w,
@@ -1228,7 +1237,8 @@ hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, 
     } else {
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
         hipLaunchKernelGGL((k_gemm_prefill<MODE>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
-                           Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp);
+                           Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp,
+                           tile_group(h, o));
     }
     return hipGetLastError();
 }
@@ -1257,7 +1267,8 @@ hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, in
     const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
     hipLaunchKernelGGL((k_gemm_prefill<GemmOut::Fp16Dense>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
                        reinterpret_cast<const int8_t*>(X), reinterpret_cast<const int8_t*>(Wp), s, 2 * h, o,
-                       nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, C, nullptr, 0, ZpArgs{});
+                       nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, C, nullptr, 0, ZpArgs{},
+                       tile_group(2 * h, o));
     return hipGetLastError();
 }
 
