@@ -78,7 +78,12 @@ __device__ __forceinline__ uint32_t bytes_left(int64_t total, int64_t from) {
     return static_cast<uint32_t>(from < total ? total - from : 0);
 }
 
-constexpr uint32_t kOutOfRange = 0x80000000u;   // a per-lane offset past every buffer
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a per-lane offset past every buffer under 2 GiB
+
+// The fp16 W rows span 2 h o bytes, which can pass 2^31 (h o < 2^31 only).
+// With h and o multiples of 64, 2 h o <= 2^32 - 8192, so this offset (with
+// no scalar or instruction offset added) is past the end of every W.
+constexpr uint32_t kOutOfRangeW = 0xfffff000u;
 
 // Block -> output tile. Blocks are dealt to the 8 XCDs round robin (block b
 // runs on XCD b % 8), and each XCD is given one contiguous run of a grouped
@@ -130,7 +135,7 @@ __device__ __forceinline__ void stage_outlier_slice(int kb, int n, int wid, int 
             const int64_t col = o0 + (lane & 31) * 8;
             const bool okW = k < n && col < o;
             const uint32_t vW = okW ? static_cast<uint32_t>(((lane >> 5) ? id1 : id0) * o * 2 + (lane & 31) * 16)
-                                    : kOutOfRange;
+                                    : kOutOfRangeW;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, LDS_PTR(dst + j * 512), 16, vW, 0, 0, 0);
         }
         const int r = 32 * j + (lane >> 1);
