@@ -24,7 +24,8 @@ SOURCES = ["quant_kernels.hip", "variant_kernels.hip", "gemm_kernels.hip", "api.
 
 # -ffp-contract=off and correctly rounded fp32 division keep the scales and
 # int8 codes bit-defined; packed fp32 instructions are disabled for device
-# code (the host pass warns that it does not know the feature: harmless).
+# code (the host pass notes that it does not know the feature: harmless, and
+# not a compiler warning). Warnings are errors.
 HIP_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -34,6 +35,8 @@ HIP_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    "-Wextra",
+    "-Werror",
     "-I", INCLUDE,
 ]
 

@@ -30,7 +30,7 @@ SRC = os.path.join(CSRC, "gemm_kernels.hip")
 @functools.lru_cache(maxsize=None)
 def _assembly(src):
     from int8_quantized_matmul_amd import build
-    flags = [f for f in build.HIP_FLAGS if f != "-fPIC"]
+    flags = [f for f in build.HIP_FLAGS if f not in ("-fPIC", "-Werror")]   # hipcc adds an unused --hip-link to -S
     return subprocess.run([build._hipcc(), *flags, "--cuda-device-only", "-S", "-o", "-", src],
                           capture_output=True, text=True, check=True).stdout
 
