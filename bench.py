@@ -204,9 +204,19 @@ def run_prefill(i8, torch, w, steps, warmup, dev, clocks=None, extras=True):
 
     n_out = int(v["n_out"].cpu()[0])
     pct = step_percentiles(torch, steps, step)
+    # the same forward with the int8 codes of X made inside the product
+    # (i8mm_forward_inline_quant, no Xq round trip), interleaved with the
+    # two-pass step, best of three windows each
+    inline = two = float("inf")
+    for _ in range(3):
+        two = min(two, timed_ms(torch, steps, step))
+        inline = min(inline, timed_ms(torch, steps, lambda: i8.forward_inline_quant(X, Wq, c_w, W, w.alpha,
+                                                                                    workspace=ws, C=C)))
+    iq = dict(inline=inline, two=two)
+    step()
     if not extras:
         return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out, inputs=inp,
-                    pct=pct, clk=clk)
+                    pct=pct, clk=clk, iq=iq)
     table5 = table5_set(i8, torch, X, W, Wq, c_w, w.alpha, steps)
     # MALL-cold steps: rotate over weight copies whose total exceeds the
     # 256 MB Infinity Cache, so every step streams its weights from HBM
@@ -229,7 +239,8 @@ def run_prefill(i8, torch, w, steps, warmup, dev, clocks=None, extras=True):
     step()
     torch.cuda.synchronize()
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, conv_ms=conv_ms, wall_s=wall, n_out=n_out,
-                inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies, w8=w8, quant=quant, clk=clk)
+                inputs=inp, pct=pct, table5=table5, cold_ms=cold_ms, copies=copies, w8=w8, quant=quant, clk=clk,
+                iq=iq)
 
 
 def run_decode(i8, torch, w, steps, warmup, dev, extras=True, clocks=None):
@@ -735,6 +746,9 @@ def main(argv=None):
         "prologue_ms": round(pre["step_ms"] - pre["gemm_ms"], 5),
         "step_ms_percentiles": pre["pct"],
         "clocks": pre["clk"],
+        "inline_quant": {"ms_per_step": round(pre["iq"]["inline"], 5),
+                         "two_pass_ms_per_step": round(pre["iq"]["two"], 5),
+                         "vs_two_pass": round(pre["iq"]["inline"] / pre["iq"]["two"], 3)},
         "weight_conversion": {"ms": round(pre["conv_ms"], 4),
                               "GB_per_s_3ho": round(3.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1),
                               "GB_per_s_5ho_moved": round(5.0 * h * o / (pre["conv_ms"] * 1e-3) / 1e9, 1),

@@ -441,6 +441,29 @@ i8mm_status i8mm_forward_decode(const uint16_t* X, int64_t s, int64_t h, int64_t
                                 const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
                                 void* workspace, uint16_t* C, hipStream_t stream);
 
+/* Smallest row count of i8mm_forward_inline_quant. */
+#define I8MM_INLINE_QUANT_MIN_ROWS 65
+
+/*
+ * i8mm_forward with the row quantisation folded into the product: the
+ * int8 codes of X are made inside the product kernel, from X, the outlier
+ * mask and c_x, while it stages its operand tiles, and are never stored
+ * (the fusion of [DIGEST] "The Full LLM.int8() Algorithm" Step 2 into
+ * Step 4 that drops the Xq round trip; [DIGEST] "Runtime Overhead Makes
+ * LLM.int8() Slower Than 16-Bit for Models Below ~13B Parameters" names
+ * input quantisation as overhead). Two launches: detection, then the row
+ * pass that writes c_x, X_O and the outlier set only; then the product.
+ * Every row block of X is quantised once per column tile of the product
+ * (o / 256 times) instead of once. Results equal i8mm_forward's bit for
+ * bit (the same codes, made by the same rounding). Arguments, workspace
+ * and errors as for i8mm_forward; the workspace's Xq region is not
+ * written. s < I8MM_INLINE_QUANT_MIN_ROWS gives I8MM_EINVAL (fewer rows
+ * take the weight-streaming product, which has no such operand staging).
+ */
+i8mm_status i8mm_forward_inline_quant(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                      const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                      void* workspace, uint16_t* C, hipStream_t stream);
+
 /* Bytes of the static device scratch that i8mm_forward_noalloc uses as its
  * workspace (64 MiB per GPU the library runs on). */
 #define I8MM_NOALLOC_SCRATCH_BYTES 67108864

@@ -32,6 +32,8 @@ __all__ = [
     "forward_zeropoint",
     "forward_noalloc",
     "forward_decode",
+    "forward_inline_quant",
+    "INLINE_QUANT_MIN_ROWS",
     "NOALLOC_SCRATCH_BYTES",
     "pack_fp16_weights",
     "fp16_gemm",
@@ -68,6 +70,8 @@ _lib = _LazyLib()
 ACC_BYTES = _native.header_define("I8MM_FORWARD_ACC_BYTES")
 # Bytes of the static device scratch behind forward_noalloc (I8MM_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = _native.header_define("I8MM_NOALLOC_SCRATCH_BYTES")
+# Fewest rows forward_inline_quant takes (I8MM_INLINE_QUANT_MIN_ROWS).
+INLINE_QUANT_MIN_ROWS = _native.header_define("I8MM_INLINE_QUANT_MIN_ROWS")
 
 
 class I8MMError(RuntimeError):
@@ -526,6 +530,30 @@ def forward_decode(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Opti
         _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o), _bias_ptr(bias, o),
         _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
     _check(st, "forward_decode")
+    return C
+
+
+def forward_inline_quant(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Optional[torch.Tensor],
+                         alpha: float = 6.0, workspace: Optional[torch.Tensor] = None,
+                         C: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """forward() with the int8 codes of X made inside the product kernel
+    and never stored (i8mm_forward_inline_quant; s >= INLINE_QUANT_MIN_ROWS).
+    The workspace receives the outlier set, c_x and X_O; its Xq region is
+    not written."""
+    s, h = X.shape
+    o = Wq.shape[1]
+    if workspace is None:
+        workspace = forward_workspace(s, h, X.device)
+    if C is None:
+        C = torch.empty((s, o), dtype=torch.float16, device=X.device)
+    need = _lib.i8mm_forward_workspace_bytes(s, h)
+    if workspace.numel() < need or workspace.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a uint8 tensor of at least {need} bytes")
+    st = _lib.i8mm_forward_inline_quant(
+        _dev(X, "X", torch.float16), s, h, o, float(alpha), _dev(Wq, "Wq", torch.int8, weight_panels_shape(h, o)),
+        _dev(c_w, "c_w", torch.float32, (o,)), _weights_ptr(W, h, o), _bias_ptr(bias, o),
+        _dev(workspace, "workspace", torch.uint8), _dev(C, "C", torch.float16, (s, o)), _stream(X))
+    _check(st, "forward_inline_quant")
     return C
 
 

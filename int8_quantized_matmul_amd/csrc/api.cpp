@@ -433,6 +433,35 @@ i8mm_status i8mm_forward_noalloc(const uint16_t* X, int64_t s, int64_t h, int64_
     return run_forward(X, s, h, o, alpha, Wq, c_w, W, bias, ws, C, stream);
 }
 
+i8mm_status i8mm_forward_inline_quant(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
+                                      const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                      void* workspace, uint16_t* C, hipStream_t stream) {
+    if (!workspace) return I8MM_EINVAL;
+    if (i8mm_status a = check_forward_args(X, s, h, o, alpha, Wq, c_w, W, bias, C)) return a;
+    if (s < I8MM_INLINE_QUANT_MIN_ROWS) return I8MM_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    size_t off[7], total;
+    int64_t ldo;
+    forward_layout(s, h, off, &ldo, &total);
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* acc = reinterpret_cast<uint32_t*>(ws + off[0]);
+    uint32_t* mask = reinterpret_cast<uint32_t*>(ws + off[1]);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + off[2]);
+    int32_t* n_out = reinterpret_cast<int32_t*>(ws + off[3]);
+    float* c_x = reinterpret_cast<float*>(ws + off[5]);
+    uint16_t* X_O = reinterpret_cast<uint16_t*>(ws + off[6]);
+    int clear_words = 0;
+    hipError_t e = i8mm::launch_forward_prologue(X, s, h, alpha, acc, mask, idx, n_out, nullptr, c_x, X_O, ldo,
+                                                 stream, &clear_words);
+    if (e == hipSuccess)
+        e = product_launch([&] {
+            return i8mm::launch_int8_gemm_inline_quant(X, mask, c_x, X_O, ldo, idx, n_out, Wq, c_w, W, bias, s, h, o,
+                                                       C, stream, acc, clear_words);
+        });
+    return forward_status(e, acc, stream);
+}
+
 i8mm_status i8mm_forward_tensorwise(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
                                     const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
                                     void* workspace, uint16_t* C, hipStream_t stream) {

@@ -316,7 +316,15 @@ __device__ __forceinline__ void store_staged_block(const uint16_t* out_st, uint1
 // sub-steps, interleaved with the MFMAs, so that the loads never queue up
 // in front of the matrix-core instructions; the fourth sub-step before the
 // barrier covers their latency.
-template <GemmOut MODE>
+//
+// QX (MODE Mixed only): the int8 operand of X is made inside this kernel
+// from the fp16 rows Xh instead of being read from Xq, which is then never
+// written ([DIGEST] Step 2 folded into the product's operand staging). A
+// stage's B slots are filled through registers: the fp16 values of the
+// slot's 16 columns, those in O (xmask) cleared, scaled by the row's c_x
+// and rounded exactly as the row quantiser does, so the codes, and C, are
+// bit-identical to the two-pass forward's.
+template <GemmOut MODE, bool QX = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
                     int64_t s, int64_t h /* reduction bytes per row */, int64_t o,
@@ -324,7 +332,9 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                     const uint16_t* __restrict__ X_O, int64_t ldo,
                     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out,
                     const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, void* __restrict__ Cout,
-                    uint32_t* __restrict__ clear, int clear_words, ZpArgs zp, uint32_t group) {
+                    uint32_t* __restrict__ clear, int clear_words, ZpArgs zp, uint32_t group,
+                    const uint16_t* __restrict__ Xh, const uint32_t* __restrict__ xmask) {
+    static_assert(!QX || MODE == GemmOut::Mixed, "X is quantised in the product only for the LLM.int8() output");
     __shared__ v4i A0[kBuf], A1[kBuf], B0[kBuf], B1[kBuf];
     __shared__ __attribute__((aligned(16))) uint16_t olds[2 * kSlice];
     __shared__ __attribute__((aligned(16))) float scl[512];   // c_x of the tile's rows, then c_w of its columns
@@ -383,8 +393,76 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         for (int q = q0; q < q1; ++q) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, LDS_PTR(A + (wu * 8 + q) * 64), 16,
                                                      (vA[q & 1] | oob[q & 1]) + q * 512, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(B + (wu * 8 + q) * 64), 16, vB[q] | oob[q & 1], k, 0,
-                                                     0);
+            if constexpr (!QX)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(B + (wu * 8 + q) * 64), 16, vB[q] | oob[q & 1],
+                                                         k, 0, 0);
+        }
+    };
+
+    // QX operand path. Lane (w, q) makes the slot that load q of wavefront
+    // w fills above: row 64 w + 8 q + dr, chunk c = c0 (even q) or c0 ^ 4
+    // (odd q), i.e. reduction columns k + 16 c .. + 15, read as two 16-byte
+    // fp16 chunks. Rows past s and columns past h read zero (code 0); mask
+    // words past h read zero.
+    const __amdgpu_buffer_rsrc_t rXh = make_rsrc(QX ? Xh + s0 * h : nullptr,
+                                                 QX ? static_cast<uint32_t>(s_rows * h * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rMask = make_rsrc(QX ? xmask : nullptr, QX ? static_cast<uint32_t>(h / 8) : 0u);
+    // per-lane byte offset of row 64 w + dr, chunk c0 (vXh[0]) or c0 ^ 4
+    // (vXh[1]); row 64 w + 8 q + dr adds the uniform 16 h q bytes, passed as
+    // the scalar offset
+    uint32_t vXh[2];
+    float xsc[8];
+    if constexpr (QX) {
+        const __amdgpu_buffer_rsrc_t rcs = make_rsrc(c_x + s0, static_cast<uint32_t>(s_rows * 4));
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            vXh[q] = static_cast<uint32_t>(((64 * wu + dr) * h + (c0 ^ (4 * q)) * 16) * 2);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            xsc[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rcs, static_cast<uint32_t>(4 * (64 * wu + 8 * q + dr)), 0, 0));
+    }
+    uint4 xv[8][2];
+    v4u xmw;
+    // Loads / stores q in [Q0, Q1) (std::integral_constant bounds, so that
+    // the loops unroll and the arrays stay in registers).
+    auto x_load = [&](int64_t kt, auto Q0, auto Q1) __attribute__((always_inline)) {
+        constexpr int q0 = decltype(Q0)::value, q1 = decltype(Q1)::value;
+        const uint32_t k = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kt * kTK));
+        const uint32_t oob[2] = {(k + c0 * 16 < static_cast<uint32_t>(h)) ? 0u : kOutOfRange,
+                                 (k + (c0 ^ 4) * 16 < static_cast<uint32_t>(h)) ? 0u : kOutOfRange};
+        if constexpr (q0 == 0) {
+            // word by word: with h % 128 == 64 the last stage's words 2 and
+            // 3 lie past the mask and read zero on their own
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xmw[j] = __builtin_amdgcn_raw_buffer_load_b32(rMask, 4 * j, k / 8, 0);
+        }
+#pragma unroll
+        for (int q = q0; q < q1; ++q) {
+            const uint32_t off = vXh[q & 1] | oob[q & 1];
+            const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(2 * k + 16 * h * q));
+            xv[q][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rXh, off, so, 0));
+            xv[q][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rXh, off + 16, so, 0));
+        }
+    };
+    auto x_store = [&](v4i* B, auto Q0, auto Q1) __attribute__((always_inline)) {
+        constexpr int q0 = decltype(Q0)::value, q1 = decltype(Q1)::value;
+        // O's columns among the stage's 128: bit j of word j / 32 (rarely any)
+        const bool any = __builtin_amdgcn_readfirstlane(static_cast<int>(xmw[0] | xmw[1] | xmw[2] | xmw[3])) != 0;
+        auto bits_of = [&](int c) {
+            const uint32_t w = (c >> 1) == 0 ? xmw[0] : (c >> 1) == 1 ? xmw[1] : (c >> 1) == 2 ? xmw[2] : xmw[3];
+            return (w >> (16 * (c & 1))) & 0xffffu;
+        };
+#pragma unroll
+        for (int q = q0; q < q1; ++q) {
+            uint4 v0 = xv[q][0], v1 = xv[q][1];
+            if (any) {
+                const uint32_t b = bits_of(c0 ^ (4 * (q & 1)));
+                v0 = chunk_clear(v0, b & 0xffu);
+                v1 = chunk_clear(v1, b >> 8);
+            }
+            const uint2 lo = chunk_quantize(v0, xsc[q]), hi = chunk_quantize(v1, xsc[q]);
+            B[(wu * 8 + q) * 64 + lane] = __builtin_bit_cast(v4i, make_uint4(lo.x, lo.y, hi.x, hi.y));
         }
     };
 
@@ -487,9 +565,48 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         mma(fa[1], fb[1]);
         sched_sub();
     };
+    // QX: the same stage, with the fp16 rows of stage kt + 1 loaded in
+    // sub-steps 0 and 1 and quantised into Bn in sub-steps 2 and 3 (Bn was
+    // last read before the previous barrier).
+    auto sched_qx = [&]() {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+            if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);              // VALU
+            if (i & 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);     // DS write
+        }
+    };
+    auto stage_qx = [&](int64_t kt, v4i* Ac, v4i* Bc, v4i* An, v4i* Bn) __attribute__((always_inline)) {
+        frags(Ac, Bc, 1, fa[1], fb[1]);
+        load_part(kt + 1, An, Bn, 3, 6);
+        x_load(kt + 1, std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+        mma(fa[0], fb[0]);
+        sched_sub();
+        frags(Ac, Bc, 2, fa[0], fb[0]);
+        load_part(kt + 1, An, Bn, 6, 8);
+        x_load(kt + 1, std::integral_constant<int, 4>{}, std::integral_constant<int, 8>{});
+        mma(fa[1], fb[1]);
+        sched_sub();
+        frags(Ac, Bc, 3, fa[1], fb[1]);
+        x_store(Bn, std::integral_constant<int, 0>{}, std::integral_constant<int, 4>{});
+        mma(fa[0], fb[0]);
+        sched_qx();
+        x_store(Bn, std::integral_constant<int, 4>{}, std::integral_constant<int, 8>{});
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        __syncthreads();
+        frags(An, Bn, 0, fa[0], fb[0]);
+        load_part(kt + 2, Ac, Bc, 0, 3);
+        mma(fa[1], fb[1]);
+        sched_sub();
+    };
 
     load_part(0, A0, B0, 0, 8);
     load_part(1, A1, B1, 0, 3);
+    if constexpr (QX) {
+        x_load(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 8>{});
+        x_store(B0, std::integral_constant<int, 0>{}, std::integral_constant<int, 8>{});
+    }
     // Behind the first operand loads: the first slice of the outlier
     // operands to its own LDS region, and the row and column scales of the
     // tile to LDS (direct-to-LDS, one dword per lane; entries past s or o
@@ -508,11 +625,19 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     __syncthreads();
     frags(A0, B0, 0, fa[0], fb[0]);
     int64_t kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-        stage(kt, A0, B0, A1, B1);
-        stage(kt + 1, A1, B1, A0, B0);
+    if constexpr (QX) {
+        for (; kt + 2 <= KT; kt += 2) {
+            stage_qx(kt, A0, B0, A1, B1);
+            stage_qx(kt + 1, A1, B1, A0, B0);
+        }
+        if (kt < KT) stage_qx(kt, A0, B0, A1, B1);
+    } else {
+        for (; kt + 2 <= KT; kt += 2) {
+            stage(kt, A0, B0, A1, B1);
+            stage(kt + 1, A1, B1, A0, B0);
+        }
+        if (kt < KT) stage(kt, A0, B0, A1, B1);   // an odd number of stages
     }
-    if (kt < KT) stage(kt, A0, B0, A1, B1);   // an odd number of stages
 
     // Lane layout of a 32x32 accumulator: register r holds
     // D[o = 8 (r / 4) + 4 (lane / 32) + r % 4][s = lane % 32].
@@ -1243,7 +1368,7 @@ hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, 
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
         hipLaunchKernelGGL((k_gemm_prefill<MODE>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
                            Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp,
-                           tile_group(h, o));
+                           tile_group(h, o), nullptr, nullptr);
     }
     return hipGetLastError();
 }
@@ -1273,7 +1398,19 @@ hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, in
     hipLaunchKernelGGL((k_gemm_prefill<GemmOut::Fp16Dense>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
                        reinterpret_cast<const int8_t*>(X), reinterpret_cast<const int8_t*>(Wp), s, 2 * h, o,
                        nullptr, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, C, nullptr, 0, ZpArgs{},
-                       tile_group(2 * h, o));
+                       tile_group(2 * h, o), nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_int8_gemm_inline_quant(const uint16_t* X, const uint32_t* mask, const float* c_x,
+                                         const uint16_t* X_O, int64_t ldo, const int32_t* idx, const int32_t* n_out,
+                                         const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                         int64_t s, int64_t h, int64_t o, uint16_t* C, hipStream_t stream,
+                                         uint32_t* clear, int clear_words) {
+    const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
+    hipLaunchKernelGGL((k_gemm_prefill<GemmOut::Mixed, true>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+                       stream, nullptr, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words,
+                       ZpArgs{}, tile_group(h, o), X, mask);
     return hipGetLastError();
 }
 

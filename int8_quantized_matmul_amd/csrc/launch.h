@@ -24,7 +24,8 @@ hipError_t launch_quantize_rows(const uint16_t* X, int64_t s, int64_t h,
 // Cross-block state (the mask accumulator, or the row maxima for inputs of
 // at most 64 rows) goes to `acc`, which must be zero on entry;
 // *clear_words is how many of its words the product launch must clear
-// again (see launch_int8_gemm).
+// again (see launch_int8_gemm). For s > 64, Xq may be null: the codes are
+// then not written (launch_int8_gemm_inline_quant makes them).
 hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, float alpha, uint32_t* acc,
                                    uint32_t* mask, int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x,
                                    uint16_t* X_O, int64_t ldo, hipStream_t stream, int* clear_words);
@@ -94,6 +95,16 @@ hipError_t launch_int8_gemm(GemmOut mode, const int8_t* Xq, const float* c_x,
 // fp16 panel layout [h / 32][o][32] (see launch_pack_fp16_panels).
 hipError_t launch_fp16_gemm(const uint16_t* X, const uint16_t* Wp, int64_t s, int64_t h, int64_t o, uint16_t* C,
                             hipStream_t stream);
+
+// The LLM.int8() product with the int8 operand of X made inside the
+// product kernel from the fp16 rows X, the final outlier mask and c_x
+// (k_gemm_prefill<Mixed, QX>): no Xq. Any s (the tiled product); the other
+// arguments as launch_int8_gemm's.
+hipError_t launch_int8_gemm_inline_quant(const uint16_t* X, const uint32_t* mask, const float* c_x,
+                                         const uint16_t* X_O, int64_t ldo, const int32_t* idx, const int32_t* n_out,
+                                         const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,
+                                         int64_t s, int64_t h, int64_t o, uint16_t* C, hipStream_t stream,
+                                         uint32_t* clear, int clear_words);
 
 hipError_t launch_pack_fp16_panels(const uint16_t* W, int64_t h, int64_t o, uint16_t* Wp, hipStream_t stream);
 

@@ -233,14 +233,16 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
         if (lane == 0 && part == 0) c_x[i] = sc;
     }
 
-    int8_t* qr = Xq + i * h;
+    // Xq null: the codes are made later, inside the product (c_x, X_O and
+    // the outlier set are still written here).
+    int8_t* qr = Xq != nullptr ? Xq + i * h : nullptr;
     if constexpr (CPL > 0) {
 #pragma unroll
         for (int p = 0; p < CPL; ++p) {
             const int64_t c = chunk_of(p);
-            if (c < nch) *reinterpret_cast<uint2*>(qr + c * 8) = chunk_quantize(cache[p], sc);
+            if (qr != nullptr && c < nch) *reinterpret_cast<uint2*>(qr + c * 8) = chunk_quantize(cache[p], sc);
         }
-    } else {
+    } else if (qr != nullptr) {
         for (int64_t c = lane; c < nch; c += 64)
             *reinterpret_cast<uint2*>(qr + c * 8) =
                 chunk_quantize(chunk_clear(load_chunk(xr + c * 8), bits_of(c)), sc);

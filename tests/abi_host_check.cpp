@@ -211,11 +211,21 @@ void check_forwards(bool no_device) {
         EXPECT_STATUS(i8mm_forward_tensorwise(X, s, h, o, a, Wq, cw, W, nullptr, ws, C, nullptr), I8MM_EINVAL);
         EXPECT_STATUS(i8mm_forward_zeropoint(X, s, h, o, a, Wq, cw, zp, zp, W, nullptr, ws, C, nullptr),
                       I8MM_EINVAL);
+        EXPECT_STATUS(i8mm_forward_inline_quant(X, 128, h, o, a, Wq, cw, W, nullptr, ws, C, nullptr), I8MM_EINVAL);
     }
     // workspace missing or not 256-byte aligned
     EXPECT_STATUS(i8mm_forward(X, s, h, o, 6.0f, Wq, cw, W, nullptr, nullptr, C, nullptr), I8MM_EINVAL);
     EXPECT_STATUS(i8mm_forward(X, s, h, o, 6.0f, Wq, cw, W, nullptr, misaligned<void>(45), C, nullptr), I8MM_EINVAL);
     void* ws16 = reinterpret_cast<void*>(reinterpret_cast<uintptr_t>(ws) + 16);
+    // inline-quantisation forward: at least I8MM_INLINE_QUANT_MIN_ROWS rows, a workspace
+    for (int64_t few : {int64_t(1), int64_t(16), int64_t(I8MM_INLINE_QUANT_MIN_ROWS - 1)})
+        EXPECT_STATUS(i8mm_forward_inline_quant(X, few, h, o, 6.0f, Wq, cw, W, nullptr, ws, C, nullptr), I8MM_EINVAL);
+    EXPECT_STATUS(i8mm_forward_inline_quant(X, 128, h, o, 6.0f, Wq, cw, W, nullptr, nullptr, C, nullptr),
+                  I8MM_EINVAL);
+    EXPECT_STATUS(i8mm_forward_inline_quant(X, 128, h, o, 6.0f, Wq, cw, W, nullptr, ws16, C, nullptr), I8MM_EINVAL);
+    EXPECT_STATUS(i8mm_forward_inline_quant(X, 128, h, o, 6.0f, Wq, cw, misaligned<uint16_t>(43), nullptr, ws, C,
+                                            nullptr),
+                  I8MM_EINVAL);
     EXPECT_STATUS(i8mm_forward(X, s, h, o, 6.0f, Wq, cw, W, nullptr, ws16, C, nullptr), I8MM_EINVAL);
     EXPECT_STATUS(i8mm_forward_decode(X, s, h, o, 6.0f, Wq, cw, W, nullptr, ws16, C, nullptr), I8MM_EINVAL);
     EXPECT_STATUS(i8mm_forward_tensorwise(X, s, h, o, 6.0f, Wq, cw, W, nullptr, nullptr, C, nullptr), I8MM_EINVAL);
@@ -239,6 +249,8 @@ void check_forwards(bool no_device) {
                       I8MM_EINVAL);
         EXPECT_STATUS(i8mm_forward_zeropoint(X, d.s, d.h, d.o, 6.0f, Wq, cw, zp, zp, W, nullptr, ws, C, nullptr),
                       I8MM_EINVAL);
+        EXPECT_STATUS(i8mm_forward_inline_quant(X, d.s, d.h, d.o, 6.0f, Wq, cw, W, nullptr, ws, C, nullptr),
+                      I8MM_EINVAL);
     }
     if (!no_device) return;
     // valid arguments and no device: rejected before anything is enqueued
@@ -247,6 +259,9 @@ void check_forwards(bool no_device) {
     EXPECT_STATUS(i8mm_forward(X, s, h, o, INFINITY, Wq, cw, nullptr, nullptr, ws, C, nullptr), I8MM_EDEVICE);
     EXPECT_STATUS(i8mm_forward_decode(X, s, h, o, 0.0f, Wq, cw, W, nullptr, ws, C, nullptr), I8MM_EDEVICE);
     EXPECT_STATUS(i8mm_forward_noalloc(X, s, h, o, 6.0f, Wq, cw, W, nullptr, C, nullptr), I8MM_EDEVICE);
+    EXPECT_STATUS(i8mm_forward_inline_quant(X, I8MM_INLINE_QUANT_MIN_ROWS, h, o, 6.0f, Wq, cw, W, nullptr, ws, C,
+                                            nullptr),
+                  I8MM_EDEVICE);
     EXPECT_STATUS(i8mm_forward_tensorwise(X, s, h, o, 6.0f, Wq, cw, W, nullptr, ws, C, nullptr), I8MM_EDEVICE);
     EXPECT_STATUS(i8mm_forward_zeropoint(X, s, h, o, 6.0f, Wq, cw, zp, zp, W, nullptr, ws, C, nullptr),
                   I8MM_EDEVICE);
