@@ -1,7 +1,8 @@
-"""Parity at the largest weight extent the products accept (h * o just below
-2^31: Wq and the fp16 weight rows are read through 32-bit buffer offsets),
-on the weight-streaming (s <= 16) and the tiled (s > 16) product, through the
-one-call forward the benchmark times.
+"""Parity at the size limits: the largest weight extent the products accept
+(h * o just below 2^31: Wq and the fp16 weight rows are read through 32-bit
+buffer offsets), on the weight-streaming (s <= 16) and the tiled (s > 16)
+product, through the one-call forward the benchmark times; and tall inputs
+(up to 2^18 rows).
 
 Every code of the converted weights, every c_w and every element of C_i32 is
 compared bit for bit with the oracle, and every element of C within
@@ -108,3 +109,35 @@ def test_largest_weight_extent(max_extent_weights, s):
         torch.cuda.synchronize()
     same = (C2.view(torch.int16) == C.view(torch.int16))
     assert bool(same.all()), f"{int((~same).sum())} outputs changed by a W row outside O"
+
+
+# Tall inputs: thousands of 256-row tiles against one or two weight tiles
+# (the grouped tile order with fewer weight tiles than its group width),
+# thousands of detection row blocks and a row-quantiser grid of 2^16 blocks.
+TALL = [(2 ** 18, 64, 64, 1), (2 ** 18, 128, 320, 3), (100_001, 192, 256, 2)]
+
+
+@pytest.mark.parametrize("s,h,o,nout", TALL, ids=[f"s{c[0]}h{c[1]}o{c[2]}" for c in TALL])
+def test_tall_inputs(s, h, o, nout):
+    inp = random_case(1200 + h, s, h, o, nout, row_frac=0.01)
+    X, W = inp["X"], inp["W"]
+    Xd, Wd = T(X), T(W)
+    say(f"  launch: forward, forward_inline_quant, int8_gemm_i32 s={s} h={h} o={o}")
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    ws = i8.forward_workspace(s, h, DEV)
+    C = i8.forward(Xd, Wq, c_w, Wd, 6.0, workspace=ws)
+    v = i8.forward_workspace_views(ws, s, h)
+    Ci = i8.int8_gemm_i32(v["Xq"], Wq)
+    C2 = i8.forward_inline_quant(Xd, Wq, c_w, Wd, 6.0)
+    torch.cuda.synchronize()
+    idx_r = check_detect(X, 6.0, v["mask"], v["idx"], v["n_out"])
+    assert idx_r.tolist() == sorted(inp["planted"].tolist())
+    Xq_r, cx_r, XO_r = check_rows(X, idx_r, v["Xq"], v["c_x"], v["X_O"])
+    Wq_t_r, cw_r = oracle_weights_by_columns(W)
+    Ci_r = oracle.int8_matmul_i32(Xq_r, Wq_t_r)
+    bad = np.argwhere(H(Ci) != Ci_r)
+    assert bad.size == 0, f"C_i32 differs at {bad[:5].tolist()}"
+    R = oracle.dequantize_and_add(Ci_r, cx_r, cw_r, oracle.outlier_matmul(XO_r, W, idx_r)).astype(np.float64)
+    G = H(C).astype(np.float64)
+    assert np.abs(G - R).max() <= 2e-3 * np.abs(R).max()
+    assert torch.equal(C2, C), "forward_inline_quant differs from forward"
