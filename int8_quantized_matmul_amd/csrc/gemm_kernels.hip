@@ -408,8 +408,10 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
                                                  QX ? static_cast<uint32_t>(s_rows * h * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rMask = make_rsrc(QX ? xmask : nullptr, QX ? static_cast<uint32_t>(h / 8) : 0u);
     // per-lane byte offset of row 64 w + dr, chunk c0 (vXh[0]) or c0 ^ 4
-    // (vXh[1]); row 64 w + 8 q + dr adds the uniform 16 h q bytes, passed as
-    // the scalar offset
+    // (vXh[1]); row 64 w + 8 q + dr adds 16 h q bytes. Everything that can
+    // leave the buffer (the row, the chunk) stays in the per-lane offset,
+    // which the range check covers; only the stage's column offset, always
+    // inside a row whose chunk is in range, goes in the scalar offset.
     uint32_t vXh[2];
     float xsc[8];
     if constexpr (QX) {
@@ -435,14 +437,13 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             // word by word: with h % 128 == 64 the last stage's words 2 and
             // 3 lie past the mask and read zero on their own
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xmw[j] = __builtin_amdgcn_raw_buffer_load_b32(rMask, 4 * j, k / 8, 0);
+            for (int j = 0; j < 4; ++j) xmw[j] = __builtin_amdgcn_raw_buffer_load_b32(rMask, k / 8 + 4 * j, 0, 0);
         }
 #pragma unroll
         for (int q = q0; q < q1; ++q) {
-            const uint32_t off = vXh[q & 1] | oob[q & 1];
-            const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(2 * k + 16 * h * q));
-            xv[q][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rXh, off, so, 0));
-            xv[q][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rXh, off + 16, so, 0));
+            const uint32_t off = (vXh[q & 1] + static_cast<uint32_t>(16 * h * q)) | oob[q & 1];
+            xv[q][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rXh, off, 2 * k, 0));
+            xv[q][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rXh, off + 16, 2 * k, 0));
         }
     };
     auto x_store = [&](v4i* B, auto Q0, auto Q1) __attribute__((always_inline)) {
