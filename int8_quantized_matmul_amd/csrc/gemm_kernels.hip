@@ -407,18 +407,18 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
     const __amdgpu_buffer_rsrc_t rXh = make_rsrc(QX ? Xh + s0 * h : nullptr,
                                                  QX ? static_cast<uint32_t>(s_rows * h * 2) : 0u);
     const __amdgpu_buffer_rsrc_t rMask = make_rsrc(QX ? xmask : nullptr, QX ? static_cast<uint32_t>(h / 8) : 0u);
-    // per-lane byte offset of row 64 w + dr, chunk c0 (vXh[0]) or c0 ^ 4
-    // (vXh[1]); row 64 w + 8 q + dr adds 16 h q bytes. Everything that can
-    // leave the buffer (the row, the chunk) stays in the per-lane offset,
-    // which the range check covers; only the stage's column offset, always
-    // inside a row whose chunk is in range, goes in the scalar offset.
-    uint32_t vXh[2];
+    // per-lane byte offset of load q's slot: row 64 w + 8 q + dr, chunk c0
+    // (even q) or c0 ^ 4 (odd q). Everything that can leave the buffer (the
+    // row, the chunk) stays in the per-lane offset, which the range check
+    // covers; only the stage's column offset, always inside a row whose
+    // chunk is in range, goes in the scalar offset.
+    uint32_t vXh[8];
     float xsc[8];
     if constexpr (QX) {
         const __amdgpu_buffer_rsrc_t rcs = make_rsrc(c_x + s0, static_cast<uint32_t>(s_rows * 4));
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            vXh[q] = static_cast<uint32_t>(((64 * wu + dr) * h + (c0 ^ (4 * q)) * 16) * 2);
+        for (int q = 0; q < 8; ++q)
+            vXh[q] = static_cast<uint32_t>(((64 * wu + 8 * q + dr) * h + (c0 ^ (4 * (q & 1))) * 16) * 2);
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             xsc[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -441,7 +441,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         }
 #pragma unroll
         for (int q = q0; q < q1; ++q) {
-            const uint32_t off = (vXh[q & 1] + static_cast<uint32_t>(16 * h * q)) | oob[q & 1];
+            const uint32_t off = vXh[q] | oob[q & 1];
             xv[q][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rXh, off, 2 * k, 0));
             xv[q][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rXh, off + 16, 2 * k, 0));
         }
