@@ -64,3 +64,52 @@ def test_noalloc_rejects_shapes_beyond_the_scratch():
     assert bool((C == 7.0).all()), "a rejected call wrote C"
     with pytest.raises(i8.I8MMError, match=r"status -5"):
         i8.forward_noalloc(Xd, Wq, c_w, Wd, 6.0, C=C)
+
+
+def test_noalloc_graph_replays():
+    """The use the entry point exists for: two allocation-free forwards (a
+    prefill and a decode shape) captured in one HIP graph (torch's CUDA-graph
+    API over the library's stream-ordered launches) and replayed four times.
+    Between replays, eager work runs: a fill of the outputs, and an eager
+    allocation-free forward on other inputs that rewrites the shared scratch.
+    Every replay must reproduce the workspace forward's C bit for bit."""
+    cases = [(300, 1024, 512, 5), (8, 2048, 256, 3)]
+    data = []
+    for k, (s, h, o, nout) in enumerate(cases):
+        inp = random_case(760 + k, s, h, o, nout, row_frac=0.5)
+        Xd, Wd = T(inp["X"]), T(inp["W"])
+        Wq, c_w = i8.quantize_colwise_weights(Wd)
+        ref = i8.forward(Xd, Wq, c_w, Wd, 6.0)
+        data.append((Xd, Wd, Wq, c_w, ref, torch.empty_like(ref)))
+    other = random_case(790, 512, 1024, 512, 9, row_frac=0.5)
+    Xo, Wo = T(other["X"]), T(other["W"])
+    Wqo, cwo = i8.quantize_colwise_weights(Wo)
+    ref_o = i8.forward(Xo, Wqo, cwo, Wo, 6.0)
+    Co = torch.empty_like(ref_o)
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # first calls outside the capture
+        for Xd, Wd, Wq, c_w, _, C in data:
+            i8.forward_noalloc(Xd, Wq, c_w, Wd, 6.0, C=C)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    say("  capture: two forward_noalloc calls")
+    with torch.cuda.graph(g):
+        for Xd, Wd, Wq, c_w, _, C in data:
+            i8.forward_noalloc(Xd, Wq, c_w, Wd, 6.0, C=C)
+    torch.cuda.synchronize()
+    for r in range(4):
+        for *_, C in data:
+            C.fill_(float("nan"))
+        i8.forward_noalloc(Xo, Wqo, cwo, Wo, 6.0, C=Co)
+        torch.cuda.synchronize()
+        assert torch.equal(Co, ref_o), f"eager call before replay {r + 1}"
+        say(f"  replay {r + 1}")
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (*_, ref, C) in enumerate(data):
+            assert torch.equal(C, ref), f"replay {r + 1}: forward {k} differs from the workspace forward"
