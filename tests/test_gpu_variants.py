@@ -206,24 +206,31 @@ def test_one_call_variant_forwards(seed, s, h, o, nout, alpha):
 
 def test_one_call_forwards_share_a_workspace():
     """One workspace, sized for the largest zeropoint case, serves every
-    one-call forward in turn, across shapes and both prologue paths (the
-    accumulator must come back to zero after each)."""
+    one-call forward in turn (absmax, tensor-wise, zeropoint, the
+    inline-quantisation and the single-launch decode forwards), across
+    shapes and both prologue paths (the accumulator must come back to zero
+    after each)."""
     seq = [("zeropoint", 300, 640, 320), ("vector", 8, 1024, 256), ("tensor", 40, 512, 192),
-           ("zeropoint", 5, 1024, 128), ("vector", 260, 640, 576), ("tensor", 3, 192, 64),
+           ("inline", 100, 1024, 256), ("zeropoint", 5, 1024, 128), ("decode", 12, 640, 192),
+           ("vector", 260, 640, 576), ("tensor", 3, 192, 64), ("inline", 300, 192, 320),
            ("zeropoint", 17, 192, 320)]
     ws = i8.forward_workspace(300, 1024, DEV, zeropoint=True)
     for k, (scheme, s, h, o) in enumerate(seq):
         inp = random_case(300 + k, s, h, o, 3, row_frac=0.5)
         Xd, Wd = T(inp["X"]), T(inp["W"])
         say(f"  launch: shared workspace {scheme} s={s} h={h} o={o}")
-        qw = i8.quantize_weights(Wd, scheme)
+        qw = i8.quantize_weights(Wd, scheme if scheme in ("zeropoint", "tensor") else "vector")
         if scheme == "zeropoint":
             C = i8.forward_zeropoint(Xd, qw, Wd, workspace=ws)
         elif scheme == "tensor":
             C = i8.forward_tensorwise(Xd, qw[0], qw[1], Wd, workspace=ws)
+        elif scheme == "inline":
+            C = i8.forward_inline_quant(Xd, qw[0], qw[1], Wd, workspace=ws)
+        elif scheme == "decode":
+            C = i8.forward_decode(Xd, qw[0], qw[1], Wd, workspace=ws)
         else:
             C = i8.forward(Xd, qw[0], qw[1], Wd, workspace=ws)
-        C_sep = i8.variant_forward(Xd, qw, Wd, scheme)
+        C_sep = i8.variant_forward(Xd, qw, Wd, scheme if scheme in ("zeropoint", "tensor") else "vector")
         torch.cuda.synchronize()
         assert torch.equal(C, C_sep), f"{scheme} call {k} differs from the separate calls"
     acc = H(ws[: i8.ACC_BYTES])
