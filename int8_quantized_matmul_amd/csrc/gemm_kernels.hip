@@ -22,11 +22,11 @@
 //    (two panels), both operands double buffered in LDS through
 //    direct-to-LDS buffer loads, v_mfma_i32_32x32x32_i8, 2x2 waves of
 //    128x128.
-//  * k_gemm_decode (s <= 16): weight streaming. Four wavefronts per 16*NT
+//  * k_gemm_decode (s <= 48): weight streaming. Four wavefronts per 16*NT
 //    output columns (64) split K and read their panels of Wq straight from
 //    HBM into the MFMA operand registers with non-temporal loads
-//    (v_mfma_i32_16x16x64_i8, rows of X beyond s read as zero), two
-//    register batches in flight.
+//    (v_mfma_i32_16x16x64_i8, one to three row groups of 16 rows of X,
+//    rows beyond s read as zero), two register batches in flight.
 // The fused epilogue converts the int32 accumulator to fp32, multiplies by
 // 1/c_x_i * 1/c_w_j (S is never materialised), then accumulates the fp16
 // outlier product on top with fp16 MFMA (fp32 accumulate), adds the
@@ -947,8 +947,10 @@ __device__ __forceinline__ v4f outlier_tile_16x16(v4f f, int lane, int64_t ocol0
 // columns, each streaming its share of K from HBM with two register batches
 // of kDecodeU K steps in flight (range-checked loads: steps past a wave's
 // range read as zero), then an exact int32 reduction of the partial tiles
-// through LDS.
-template <GemmOut MODE, int NT, int kDecodeU = 4, int kDecodeSplit = 4>
+// through LDS. RG row groups of 16 (up to 16 RG rows of X) share every
+// weight load: each step multiplies the NT weight operands by RG operands
+// of X, and the reduction and the epilogue run once per row group.
+template <GemmOut MODE, int NT, int kDecodeU = 4, int kDecodeSplit = 4, int RG = 1>
 __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
                                                      int64_t s, int64_t h, int64_t o,
                                                      const float* __restrict__ c_x, const float* __restrict__ c_w,
@@ -971,10 +973,11 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq + obase * 64, static_cast<uint32_t>(h * o - obase * 64));
     // Xq rows 0 .. s - 1; lanes of rows >= s fall past the range and read zero.
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(Xq, static_cast<uint32_t>(s * h));
-    uint32_t vA[NT];
+    uint32_t vA[NT], vB[RG];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) vA[nt] = static_cast<uint32_t>((nt * 16 + r16) * 64 + g * 16);
-    const uint32_t vB = static_cast<uint32_t>(r16 * h + g * 16);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) vB[rg] = static_cast<uint32_t>((rg * 16 + r16) * h + g * 16);
 
     // Wavefronts that finish an output tile fetch the first slice of its
     // outlier operands now, so the loads complete under the K loop.
@@ -994,14 +997,17 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     const int64_t st0 = wid * per < nsteps ? wid * per : nsteps;
     const int64_t st1 = st0 + per < nsteps ? st0 + per : nsteps;
 
-    v4i acc[NT];
+    v4i acc[RG][NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
-    v4i a0[kDecodeU][NT], b0[kDecodeU], a1[kDecodeU][NT], b1[kDecodeU];
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[rg][nt] = v4i{0, 0, 0, 0};
+    v4i a0[kDecodeU][NT], b0[kDecodeU][RG], a1[kDecodeU][NT], b1[kDecodeU][RG];
 
     // Steps past the wave's range get an out-of-range lane offset and a zero
-    // scalar offset, so no sum of the two can wrap back into the range.
-    auto load = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU], int64_t stb) {
+    // scalar offset, so no sum of the two can wrap back into the range; rows
+    // of X past s lie past the end of rB through their lane offset.
+    auto load = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU][RG], int64_t stb) {
 #pragma unroll
         for (int u = 0; u < kDecodeU; ++u) {
             const bool ok = stb + u < st1;
@@ -1009,15 +1015,18 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
             const uint32_t kB = ok ? static_cast<uint32_t>((stb + u) * 64) : 0u;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) a[u][nt] = buf_load16_nt(rA, ok ? vA[nt] : kOutOfRange, kA);
-            b[u] = buf_load16(rB, ok ? vB : kOutOfRange, kB);
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) b[u][rg] = buf_load16(rB, ok ? vB[rg] : kOutOfRange, kB);
         }
     };
-    auto mma = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU]) {
+    auto mma = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU][RG]) {
 #pragma unroll
         for (int u = 0; u < kDecodeU; ++u)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][nt], b[u], acc[nt], 0, 0, 0);
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[rg][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][nt], b[u][rg], acc[rg][nt], 0, 0, 0);
     };
 
     load(a0, b0, st0);
@@ -1027,62 +1036,68 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
         load(a0, b0, stb + 2 * kDecodeU);
         mma(a1, b1);
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) red[wid][nt][lane] = acc[nt];
-    __syncthreads();
-    if (wid >= NT) return;
-    const int nt = wid;
-    v4i sum = red[0][nt][lane];
-#pragma unroll
-    for (int w = 1; w < kDecodeSplit; ++w) sum += red[w][nt][lane];
-
     // Lane layout of a 16x16 accumulator: register r holds D[o = 4 g + r][s = r16].
-    const int64_t srow = r16;
-    const int64_t ocol = obase + nt * 16 + 4 * g;
-    if constexpr (MODE == GemmOut::Int32) {
-        int32_t* C = static_cast<int32_t*>(Cout);
-        if (srow < s) *reinterpret_cast<v4i*>(C + srow * o + ocol) = sum;
-    } else {
-        uint16_t* C = static_cast<uint16_t*>(Cout);
-        const float inv_x = __builtin_amdgcn_rcpf(srow < s ? c_x[srow] : 1.0f);
-        const v4f cw = *reinterpret_cast<const v4f*>(c_w + ocol);
-        v4f f;
-        if constexpr (MODE == GemmOut::ZeroPoint) {
-            // C' = C_i32 + zp_w (rowsum + (h - |O|) zp_x) + zp_x colsum', exact
-            // in int64 (colsum' = the column's code sum over the non-outlier rows)
-            const int zx = srow < s ? zp.zp_x[srow] : 0;
-            const int64_t zr =
-                srow < s ? static_cast<int64_t>(zp.rowsum_x[srow]) + (h - n_o) * static_cast<int64_t>(zx) : 0;
-            const v4i zw = *reinterpret_cast<const v4i*>(zp.zp_w + ocol);
-            v4i cs = *reinterpret_cast<const v4i*>(zp.colsum_w + ocol);
-            for (int q = 0; q < n_o; ++q) {
-                const int64_t k = idx[q];
-                const int8_t* p = Wq + (k >> 6) * o * 64 + ocol * 64 + (k & 63);
+    auto decode_epilogue = [&](int rg, int nt) {
+        v4i sum = red[0][nt][lane];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) cs[e] -= p[e * 64];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t cp = static_cast<int64_t>(sum[e]) + static_cast<int64_t>(zw[e]) * zr +
-                                   static_cast<int64_t>(zx) * static_cast<int64_t>(cs[e]);
-                f[e] = static_cast<float>(cp) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
-            }
+        for (int w = 1; w < kDecodeSplit; ++w) sum += red[w][nt][lane];
+        const int64_t srow = rg * 16 + r16;
+        const int64_t ocol = obase + nt * 16 + 4 * g;
+        if constexpr (MODE == GemmOut::Int32) {
+            int32_t* C = static_cast<int32_t*>(Cout);
+            if (srow < s) *reinterpret_cast<v4i*>(C + srow * o + ocol) = sum;
         } else {
+            uint16_t* C = static_cast<uint16_t*>(Cout);
+            const float inv_x = __builtin_amdgcn_rcpf(srow < s ? c_x[srow] : 1.0f);
+            const v4f cw = *reinterpret_cast<const v4f*>(c_w + ocol);
+            v4f f;
+            if constexpr (MODE == GemmOut::ZeroPoint) {
+                // C' = C_i32 + zp_w (rowsum + (h - |O|) zp_x) + zp_x colsum', exact
+                // in int64 (colsum' = the column's code sum over the non-outlier rows)
+                const int zx = srow < s ? zp.zp_x[srow] : 0;
+                const int64_t zr =
+                    srow < s ? static_cast<int64_t>(zp.rowsum_x[srow]) + (h - n_o) * static_cast<int64_t>(zx) : 0;
+                const v4i zw = *reinterpret_cast<const v4i*>(zp.zp_w + ocol);
+                v4i cs = *reinterpret_cast<const v4i*>(zp.colsum_w + ocol);
+                for (int q = 0; q < n_o; ++q) {
+                    const int64_t k = idx[q];
+                    const int8_t* p = Wq + (k >> 6) * o * 64 + ocol * 64 + (k & 63);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+                    for (int e = 0; e < 4; ++e) cs[e] -= p[e * 64];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t cp = static_cast<int64_t>(sum[e]) + static_cast<int64_t>(zw[e]) * zr +
+                                       static_cast<int64_t>(zx) * static_cast<int64_t>(cs[e]);
+                    f[e] = static_cast<float>(cp) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+            }
+            // the first slice of row group 0 was fetched before the K loop
+            f = outlier_tile_16x16(f, lane, obase + nt * 16, rg * 16, s, o, X_O, ldo, idx, n_o, W, Wq, c_w,
+                                   rg == 0 ? pre : nullptr);
+            if (bias != nullptr) {
+                f[0] += half_bits_to_float(bias4.x & 0xffffu);
+                f[1] += half_bits_to_float(bias4.x >> 16);
+                f[2] += half_bits_to_float(bias4.y & 0xffffu);
+                f[3] += half_bits_to_float(bias4.y >> 16);
+            }
+            if (srow < s) {
+                const uint32_t lo = pack_half2(f[0], f[1]);
+                const uint32_t hi = pack_half2(f[2], f[3]);
+                *reinterpret_cast<uint2*>(C + srow * o + ocol) = make_uint2(lo, hi);
+            }
         }
-        f = outlier_tile_16x16(f, lane, obase + nt * 16, 0, s, o, X_O, ldo, idx, n_o, W, Wq, c_w, pre);
-        if (bias != nullptr) {
-            f[0] += half_bits_to_float(bias4.x & 0xffffu);
-            f[1] += half_bits_to_float(bias4.x >> 16);
-            f[2] += half_bits_to_float(bias4.y & 0xffffu);
-            f[3] += half_bits_to_float(bias4.y >> 16);
-        }
-        if (srow < s) {
-            const uint32_t lo = pack_half2(f[0], f[1]);
-            const uint32_t hi = pack_half2(f[2], f[3]);
-            *reinterpret_cast<uint2*>(C + srow * o + ocol) = make_uint2(lo, hi);
-        }
+    };
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+        if (rg > 0) __syncthreads();   // every wavefront has read the previous round
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) red[wid][nt][lane] = acc[rg][nt];
+        __syncthreads();
+        if (wid < NT) decode_epilogue(rg, wid);
     }
 }
 
@@ -1356,21 +1371,31 @@ hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, 
                        const int32_t* idx, const int32_t* n_out, const int8_t* Wq, const float* c_w,
                        const uint16_t* W, const uint16_t* bias, int64_t s, int64_t h, int64_t o, void* C,
                        hipStream_t stream, uint32_t* clear, int clear_words, ZpArgs zp) {
+    // Weight streaming for up to 48 rows: 64 output columns per block (one
+    // 16-column tile per wavefront in the epilogue), batches of two K steps:
+    // 7.06 TB/s of weights on the 8 x 12288 x 49152 layer against 6.64 TB/s
+    // with 32 columns and batches of four. More rows share each weight load
+    // as 2 or 3 row groups; every block still reads all of Xq, whose L2
+    // traffic grows with s, so on that layer (forward, us) 17-32 rows take
+    // 102-119 against 155-157 for the tiled product and 33-48 rows 122-140
+    // against 157-161, while 4 row groups (49-64 rows, one wavefront per
+    // SIMD at 272 registers) lost to it (156-175 against 158-163).
+#define I8MM_DECODE(NT, RG)                                                                                       \
+    hipLaunchKernelGGL((k_gemm_decode<MODE, NT, 2, 4, RG>), dim3(static_cast<unsigned>(o / (16 * NT))), dim3(256), \
+                       0, stream, Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp)
     if (s <= 16) {
-        // 64 output columns per block (one 16-column tile per wavefront in the
-        // epilogue), batches of two K steps: 7.06 TB/s of weights on the
-        // 8 x 12288 x 49152 layer against 6.64 TB/s with 32 columns and
-        // batches of four (same 144-register footprint, three blocks per CU).
-        constexpr int NT = 4, U = 2;
-        hipLaunchKernelGGL((k_gemm_decode<MODE, NT, U>), dim3(static_cast<unsigned>(o / (16 * NT))), dim3(256), 0,
-                           stream, Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear,
-                           clear_words, zp);
+        I8MM_DECODE(4, 1);
+    } else if (s <= 32) {
+        I8MM_DECODE(4, 2);
+    } else if (s <= 48) {
+        I8MM_DECODE(4, 3);
     } else {
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
         hipLaunchKernelGGL((k_gemm_prefill<MODE>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
                            Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp,
                            tile_group(h, o), nullptr, nullptr);
     }
+#undef I8MM_DECODE
     return hipGetLastError();
 }
 

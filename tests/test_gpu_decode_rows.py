@@ -1,0 +1,56 @@
+"""The weight-streaming product's row groups (1, 2 or 3 groups of 16 rows of
+X for up to 16, 32 and 48 rows; the tiled product above 48) at each
+boundary, against the oracle: the outlier set, Xq, c_x, X_O and C_i32 bit
+for bit, C within 2e-3 ||C_ref||_inf. The one-call forward, the four-step
+product and the int32 product all dispatch on s the same way."""
+
+import numpy as np
+import pytest
+import torch
+
+import int8_quantized_matmul_amd as i8
+import oracle
+from gpu_util import DEV, H, T, check_C, check_detect, check_rows, say
+from workloads import random_case
+
+pytestmark = pytest.mark.gpu
+
+ROWS = [16, 17, 32, 33, 48, 49]
+
+
+@pytest.mark.parametrize("s", ROWS)
+def test_row_group_boundaries(s):
+    h, o = 4096, 1024
+    inp = random_case(1700 + s, s, h, o, 6, row_frac=0.5)
+    X, W = inp["X"], inp["W"]
+    Xd, Wd = T(X), T(W)
+    say(f"  launch: forward + int8_gemm_i32 + int8_mixed_matmul s={s} h={h} o={o}")
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    ws = i8.forward_workspace(s, h, DEV)
+    C = i8.forward(Xd, Wq, c_w, Wd, 6.0, workspace=ws)
+    v = i8.forward_workspace_views(ws, s, h)
+    Ci = i8.int8_gemm_i32(v["Xq"], Wq)
+    C4 = i8.int8_mixed_matmul(v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, Wd)
+    torch.cuda.synchronize()
+    idx_r = check_detect(X, 6.0, v["mask"], v["idx"], v["n_out"])
+    Xq_r, cx_r, XO_r = check_rows(X, idx_r, v["Xq"], v["c_x"], v["X_O"])
+    Wq_t_r, cw_r = oracle.quantize_colwise_weights(W)
+    Ci_r = oracle.int8_matmul_i32(Xq_r, Wq_t_r)
+    bad = np.argwhere(H(Ci) != Ci_r)
+    assert bad.size == 0, f"C_i32 differs at {bad[:5].tolist()}"
+    check_C(C, oracle.forward(X, W, 6.0)["C"])
+    assert torch.equal(C, C4), "the one-call forward and the four-step product differ"
+
+
+@pytest.mark.parametrize("s", [20, 40])
+def test_row_groups_without_fp16_weights_and_with_bias(s):
+    h, o = 2048, 512
+    inp = random_case(1760 + s, s, h, o, 5, row_frac=0.5)
+    X, W = inp["X"], inp["W"]
+    b = ((np.arange(o) % 7 - 3) * 0.125).astype(np.float16)
+    Xd, Wd = T(X), T(W)
+    say(f"  launch: forward without fp16 W, with bias, s={s}")
+    Wq, c_w = i8.quantize_colwise_weights(Wd)
+    C = i8.forward(Xd, Wq, c_w, None, 6.0, bias=T(b))
+    torch.cuda.synchronize()
+    check_C(C, oracle.forward(X, W, 6.0, fp16_weights=False, bias=b)["C"])
