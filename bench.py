@@ -279,14 +279,27 @@ def run_decode(i8, torch, w, steps, warmup, dev, extras=True, clocks=None):
         three = min(three, timed_ms(torch, steps, lambda: i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C)))
         single = min(single, timed_ms(torch, steps, lambda: i8.forward_decode(X, Wq, c_w, W, w.alpha,
                                                                               workspace=ws, C=C)))
+    # batched decode on the same weights: 32 and 48 rows of X drawn with the
+    # same recipe (the weight-streaming product with 2 and 3 row groups)
+    import dataclasses
+    from workloads import make_inputs as _mk
+    batched = []
+    for sb in (32, 48):
+        Xb = torch.from_numpy(_mk(dataclasses.replace(w, name=f"{w.name}_s{sb}", s=sb), with_W=False)["X"]).to(dev)
+        wsb = i8.forward_workspace(sb, h, dev)
+        Cb = torch.empty((sb, o), dtype=torch.float16, device=dev)
+        tb = timed_ms(torch, steps, lambda: i8.forward(Xb, Wq, c_w, W, w.alpha, workspace=wsb, C=Cb))
+        batched.append({"s": sb, "ms_per_step": round(tb, 5),
+                        "weight_GB_per_s": round((h * o + 4 * o) / (tb * 1e-3) / 1e9, 1)})
+        del Xb, wsb, Cb
     if not extras:
         return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, inputs=inp,
-                    single=single, three=three, clk=clk)
+                    single=single, three=three, clk=clk, batched=batched)
     w8 = variant_ms(i8, torch, steps, X, Wq, c_w, W, w.alpha, ws, C)
     del Wq, c_w
     quant = quantiser_variants(i8, torch, steps, X, W, w.alpha, w8["base"])
     return dict(step_ms=step_ms, gemm_ms=gemm_ms, n_out=n_out, weight_bytes=weight_bytes, w8=w8, quant=quant,
-                inputs=inp, single=single, three=three, clk=clk)
+                inputs=inp, single=single, three=three, clk=clk, batched=batched)
 
 
 def quantiser_variants(i8, torch, steps, X, W, alpha, fused_ms):
@@ -788,6 +801,7 @@ def main(argv=None):
             "clocks": dec["clk"],
             "single_launch": {"ms_per_step": round(dec["single"], 5), "three_launch_ms_per_step": round(dec["three"], 5),
                               "vs_three_launch": round(dec["single"] / dec["three"], 3)},
+            "batched": dec["batched"],
         }
         if not args.no_extras:
             out["decode"].update({
