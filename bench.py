@@ -116,7 +116,8 @@ def table5_set(i8, torch, X, W, Wq, c_w, alpha, n, ws=None):
     """The pages' Table 5 comparison set on one layer (raw matmul time, inputs
     resident): the FP16 GEMM of the vendor library (torch.matmul -> hipBLASLt)
     and the library's own dense fp16 kernel (i8mm_fp16_gemm, weights packed at
-    load time),
+    load time), the vendor library's int8 GEMM with int32 output
+    (torch._int_mm, for scale: no scales, no outliers),
     the int8 product alone ("Int8 without overhead": the same main loop with an
     int32 store, and the fused product with no outlier columns), vector-wise
     quantisation only (forward at alpha = inf: no decomposition) and the full
@@ -141,12 +142,26 @@ def table5_set(i8, torch, X, W, Wq, c_w, alpha, n, ws=None):
     t_i32 = timed_ms(torch, n, lambda: i8.int8_gemm_i32(v["Xq"], Wq, C=Ci))
     t_fused0 = timed_ms(torch, n, lambda: i8.int8_mixed_matmul(v["Xq"], v["c_x"], v["X_O"], v["idx"], zero,
                                                                 Wq, c_w, W, C))
+    # for scale: the vendor library's int8 GEMM (torch._int_mm -> hipBLASLt,
+    # int32 out) on the same codes, its fast layout (weights [o, h], K-major)
+    vendor = {}
+    try:
+        Wt = i8.panels_to_rows(Wq).contiguous()
+        Cv = torch._int_mm(v["Xq"], Wt.t())
+        i8.int8_gemm_i32(v["Xq"], Wq, C=Ci)
+        torch.cuda.synchronize()
+        vendor = {"int8_library_ms": round(timed_ms(torch, n, lambda: torch._int_mm(v["Xq"], Wt.t())), 5),
+                  "int8_library_equals_int8_gemm_i32": bool(torch.equal(Cv, Ci))}
+        del Wt, Cv
+    except Exception as e:   # the op missing or refusing the shape
+        vendor = {"int8_library_error": repr(e)[:200]}
     r = lambda t: round(t_fp16 / t, 3)
     return {
         "fp16_library_ms": round(t_fp16, 5),
         "fp16_own_ms": round(t_fp16_own, 5),
         "fp16_own_tflops": round(2.0 * s * h * o / (t_fp16_own * 1e-3) / 1e12, 1),
         "int8_gemm_i32_ms": round(t_i32, 5),
+        **vendor,
         "int8_product_no_outliers_ms": round(t_fused0, 5),
         "vectorwise_only_ms": round(t_vec, 5),
         "llm_int8_ms": round(t_llm, 5),
@@ -268,7 +283,6 @@ def run_decode(i8, torch, w, steps, warmup, dev, extras=True, clocks=None):
         v["Xq"], v["c_x"], v["X_O"], v["idx"], v["n_out"], Wq, c_w, W, C))
     clk = None
     if clocks is not None:
-        clocks.samples.clear()
         clk = clock_window(torch, lambda: i8.forward(X, Wq, c_w, W, w.alpha, workspace=ws, C=C), step_ms, clocks)
     n_out = int(v["n_out"].cpu()[0])
     weight_bytes = h * o + 2 * n_out * o + 4 * o
@@ -604,11 +618,13 @@ class ClockSampler:
         if self.error is not None and not self.samples:
             return {"error": self.error}
         # the table holds each snapshot for a while: keep the distinct ones,
-        # and drop the idle snapshot the window may start with
+        # and drop the first (it may predate the window) and idle ones
         snaps = []
         for smp in self.samples:
             if not snaps or smp != snaps[-1]:
                 snaps.append(smp)
+        if len(snaps) > 1:
+            snaps = snaps[1:]
         busy = [x for x in snaps if x[0] and sum(x[0]) / len(x[0]) > 500.0] or snaps
 
         def med(vals):
@@ -630,6 +646,7 @@ class ClockSampler:
 def clock_window(torch, fn, step_ms, clocks, seconds=1.5):
     """Runs fn back to back for about `seconds` under the clock sampler."""
     n = max(50, int(seconds * 1e3 / max(step_ms, 1e-3)))
+    clocks.samples.clear()   # a window of its own
     with clocks:
         t0 = time.perf_counter()
         done = 0
@@ -641,6 +658,30 @@ def clock_window(torch, fn, step_ms, clocks, seconds=1.5):
             done += k
         el = time.perf_counter() - t0
     return clocks.summary(round(el, 3), n)
+
+
+def mfma_stream_ceiling(i8, torch, dev, clocks, seconds=3.0):
+    """The int8 matrix-core rate the chip sustains under load: one block of
+    four wavefronts per compute unit issuing v_mfma_i32_32x32x32_i8 back to
+    back on register-resident random codes (i8mm_calib_mfma_i8), timed with
+    HIP events, then run back to back for a clock window. The published
+    peak assumes the 2.4 GHz clock; this is what the clock and power limits
+    leave of it, the practical ceiling for the prefill product."""
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 40000
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    codes = torch.randint(-127, 128, (blocks * 65536,), generator=g, dtype=torch.int8, device=dev)
+    out = torch.empty((blocks * 256,), dtype=torch.int32, device=dev)
+    fn = lambda: i8.calib_mfma_i8(codes, iters, out)
+    ops = fn()
+    torch.cuda.synchronize()
+    ms = timed_ms(torch, 4, fn, warmup=1)
+    clk = clock_window(torch, fn, ms, clocks, seconds) if clocks is not None else None
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"kernel": "k_calib_mfma_i8", "blocks": blocks, "mfma_per_wavefront": 32 * iters,
+            "ms_per_launch": round(ms, 4), "TOP/s": round(tops, 1), "frac_of_peak": round(tops / INT8_PEAK_TOPS, 4),
+            "clocks": clk}
 
 
 CONFIG_NAMES = ["tiny", "opt67b_ffn1_prefill", "sweep_o0"] + \
@@ -769,6 +810,10 @@ def main(argv=None):
                                                         / HBM_PEAK_GBS, 2)},
     }
     if not args.no_extras:
+        _log("[bench] sustained int8 MFMA stream (practical ceiling)")
+        ceil = mfma_stream_ceiling(i8, torch, dev, clocks)
+        ceil["product_kernel_over_stream"] = round(gemm_tops / ceil["TOP/s"], 4)
+        out["roofline"]["sustained_mfma_stream"] = ceil
         out.update({
             "step_ms_weights_from_hbm": {"ms": round(pre["cold_ms"], 5), "weight_copies_rotated": pre["copies"]},
             "table5_comparison": pre["table5"],

@@ -499,6 +499,24 @@ i8mm_status i8mm_forward_noalloc(const uint16_t* X, int64_t s, int64_t h, int64_
  */
 void i8mm_test_fail_product_launches(int count);
 
+/*
+ * Measurement calibration, not part of the method: the int8 matrix-core
+ * rate the chip sustains under load, for the roofline of the products
+ * (whose published int8 peak assumes the full 2.4 GHz clock). Enqueues one
+ * launch of `blocks` blocks of four wavefronts; each wavefront issues
+ * 32 * iters v_mfma_i32_32x32x32_i8 (65536 integer operations each) on
+ * operands held in registers, with no memory traffic inside its loop, so the
+ * launch performs blocks * 4 * 32 * iters * 65536 operations.
+ *   codes  device, blocks * 65536 bytes: the int8 operands (random codes make
+ *          the matrix cores switch as they do on real data); read once.
+ *   out    device, blocks * 256 int32: an XOR of each thread's accumulators
+ *          (keeps the work from being optimised away; no meaning otherwise).
+ * Errors: I8MM_EINVAL for null or unaligned pointers, blocks outside
+ * [1, 2^20] or iters outside [1, 2^24]; I8MM_EDEVICE, I8MM_ELAUNCH as above.
+ */
+i8mm_status i8mm_calib_mfma_i8(const int8_t* codes, int64_t blocks, int64_t iters, int32_t* out,
+                               hipStream_t stream);
+
 /* Library version string (static storage). */
 const char* i8mm_version(void);
 

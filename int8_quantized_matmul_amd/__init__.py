@@ -574,3 +574,17 @@ def forward_noalloc(X: torch.Tensor, Wq: torch.Tensor, c_w: torch.Tensor, W: Opt
         _dev(C, "C", torch.float16, (s, o)), _stream(X))
     _check(st, "forward_noalloc")
     return C
+
+
+def calib_mfma_i8(codes: torch.Tensor, iters: int, out: torch.Tensor) -> int:
+    """Measurement calibration (not the method): enqueues a stream of int8
+    MFMAs on register-resident operands, len(out) / 256 blocks of four
+    wavefronts, 32 * iters MFMAs per wavefront. codes: int8, 65536 per block;
+    out: int32, 256 per block. Returns the integer operations performed."""
+    blocks = out.numel() // 256
+    if blocks < 1 or out.numel() != blocks * 256:
+        raise ValueError("out must hold a positive multiple of 256 int32")
+    st = _lib.i8mm_calib_mfma_i8(_dev(codes, "codes", torch.int8, (blocks * 65536,)), blocks, iters,
+                                 _dev(out, "out", torch.int32, (blocks * 256,)), _stream(codes))
+    _check(st, "calib_mfma_i8")
+    return blocks * 4 * 32 * iters * 65536

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "i8mm_forward_decode": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     "i8mm_forward_inline_quant": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p, c_p]),
     "i8mm_forward_noalloc": (c_int, [c_p, c_i64, c_i64, c_i64, c_f, c_p, c_p, c_p, c_p, c_p, c_p]),
+    "i8mm_calib_mfma_i8": (c_int, [c_p, c_i64, c_i64, c_p, c_p]),
     "i8mm_test_fail_product_launches": (None, [c_int]),
     "i8mm_version": (ctypes.c_char_p, []),
     "i8mm_status_string": (ctypes.c_char_p, [c_int]),

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libi8mm.so")
-SOURCES = ["quant_kernels.hip", "variant_kernels.hip", "gemm_kernels.hip", "api.cpp"]
+SOURCES = ["quant_kernels.hip", "variant_kernels.hip", "gemm_kernels.hip", "calib_kernels.hip", "api.cpp"]
 
 # -ffp-contract=off and correctly rounded fp32 division keep the scales and
 # int8 codes bit-defined; packed fp32 instructions are disabled for device

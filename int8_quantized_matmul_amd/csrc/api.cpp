@@ -540,6 +540,14 @@ i8mm_status i8mm_forward_zeropoint(const uint16_t* X, int64_t s, int64_t h, int6
     return forward_status(e, acc, stream);
 }
 
+i8mm_status i8mm_calib_mfma_i8(const int8_t* codes, int64_t blocks, int64_t iters, int32_t* out,
+                               hipStream_t stream) {
+    if (!codes || !out || !aligned16(codes) || !aligned16(out)) return I8MM_EINVAL;
+    if (blocks < 1 || blocks > (int64_t(1) << 20) || iters < 1 || iters > (int64_t(1) << 24)) return I8MM_EINVAL;
+    if (i8mm_status d = check_device()) return d;
+    return launched(i8mm::launch_calib_mfma_i8(codes, blocks, iters, out, stream));
+}
+
 void i8mm_test_fail_product_launches(int count) {
     g_fail_products.store(count > 0 ? count : 0, std::memory_order_relaxed);
 }

@@ -120,4 +120,10 @@ hipError_t launch_outlier_matmul(const uint16_t* X_O, int64_t ldo,
                                  const uint16_t* W, int64_t s, int64_t o,
                                  float* C_O, hipStream_t stream);
 
+// Calibration stream of int8 MFMAs (k_calib_mfma_i8): `blocks` blocks of
+// four wavefronts, 32 iters MFMAs per wavefront; codes holds 256 bytes per
+// thread, out one int32 per thread.
+hipError_t launch_calib_mfma_i8(const int8_t* codes, int64_t blocks, int64_t iters, int32_t* out,
+                                hipStream_t stream);
+
 }  // namespace i8mm

@@ -177,3 +177,15 @@ def test_variant_entry_points_reject():
     assert lib.i8mm_zeropoint_matmul(*args, None, None, 4, 64, 64, P, None) == -1
     assert lib.i8mm_zeropoint_matmul(*args, P, MIS, 4, 64, 64, P, None) == -1
     assert lib.i8mm_zeropoint_matmul(*args, P, None, 4, 65536, 32768, P, None) == -1
+
+
+def test_calibration_rejects():
+    """The MFMA calibration validates its pointers and counts before any
+    device call."""
+    lib = _lib()
+    assert lib.i8mm_calib_mfma_i8(None, 1, 1, P, None) == -1
+    assert lib.i8mm_calib_mfma_i8(P, 1, 1, MIS, None) == -1
+    assert lib.i8mm_calib_mfma_i8(P, 0, 1, P, None) == -1
+    assert lib.i8mm_calib_mfma_i8(P, (1 << 20) + 1, 1, P, None) == -1
+    assert lib.i8mm_calib_mfma_i8(P, 1, 0, P, None) == -1
+    assert lib.i8mm_calib_mfma_i8(P, 1, (1 << 24) + 1, P, None) == -1
