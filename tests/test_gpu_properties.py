@@ -1,5 +1,5 @@
 """Property-based GPU parity over small random shapes: s in [1, 64] (the
-weight-streaming product for s <= 16, the LDS-tiled one above, the few-rows
+weight-streaming products for s <= 48, the LDS-tiled one above, the few-rows
 prologue of the one-call forward), h and o in 64 * [1, 8], random outlier
 columns and row fractions, an element exactly at alpha, all-zero rows.
 Every entry point is compared with the oracle (bit-exact intermediates,
