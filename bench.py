@@ -718,6 +718,9 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (5 times) and exit; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
+    ap.add_argument("--calibration", action="store_true",
+                    help="only run the sustained int8 MFMA stream (the prefill product's practical ceiling) "
+                         "and print it as one JSON line")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -730,6 +733,10 @@ def main(argv=None):
     from workloads import CONFIGS, get_config
 
     dev = torch.device("cuda:0")
+    if args.calibration:
+        print(json.dumps({"sustained_mfma_stream": mfma_stream_ceiling(i8, torch, dev, ClockSampler(torch)),
+                          "peak_TOPS": INT8_PEAK_TOPS}), flush=True)
+        return 0
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.ones(n // 4, dtype=torch.int32, device=dev)
