@@ -459,8 +459,8 @@ i8mm_status i8mm_forward_decode(const uint16_t* X, int64_t s, int64_t h, int64_t
  * and errors as for i8mm_forward; the workspace's Xq region is not
  * written. s < I8MM_INLINE_QUANT_MIN_ROWS gives I8MM_EINVAL: with fewer
  * rows the forward's prologue is the few-row pair of kernels, which makes
- * the codes in the same pass as the row constants, and up to 48 rows the
- * product streams its weights with no operand staging to fold them into.
+ * the codes in the same pass as the row constants, and the product is one
+ * of the weight-streaming kernels, not the tiled one this variant changes.
  */
 i8mm_status i8mm_forward_inline_quant(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
                                       const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,

@@ -17,16 +17,20 @@
 // decode epilogue stores them as 8-byte fp16 quads, the prefill epilogue
 // regroups them through LDS into full 256-byte rows.
 //
-// Two main loops share the epilogue structure:
-//  * k_gemm_prefill: 256x256 output tile per 256-thread block, K step 128
-//    (two panels), both operands double buffered in LDS through
+// Three main loops share the epilogue structure:
+//  * k_gemm_prefill (s > 64): 256x256 output tile per 256-thread block, K
+//    step 128 (two panels), both operands double buffered in LDS through
 //    direct-to-LDS buffer loads, v_mfma_i32_32x32x32_i8, 2x2 waves of
 //    128x128.
-//  * k_gemm_decode (s <= 48): weight streaming. Four wavefronts per 16*NT
+//  * k_gemm_decode (s <= 16): weight streaming. Four wavefronts per 16*NT
 //    output columns (64) split K and read their panels of Wq straight from
 //    HBM into the MFMA operand registers with non-temporal loads
-//    (v_mfma_i32_16x16x64_i8, one to three row groups of 16 rows of X,
-//    rows beyond s read as zero), two register batches in flight.
+//    (v_mfma_i32_16x16x64_i8, rows beyond s read as zero), two register
+//    batches in flight.
+//  * k_gemm_skinny (17 <= s <= 64): weight streaming with the columns split
+//    between the wavefronts of a block, each over all of K with a ring of
+//    weight steps in registers, and X's codes (two to four row groups of
+//    16) staged once per block in LDS.
 // The fused epilogue converts the int32 accumulator to fp32, multiplies by
 // 1/c_x_i * 1/c_w_j (S is never materialised), then accumulates the fp16
 // outlier product on top with fp16 MFMA (fp32 accumulate), adds the
@@ -943,14 +947,76 @@ __device__ __forceinline__ v4f outlier_tile_16x16(v4f f, int lane, int64_t ocol0
 }
 
 
+// The fused epilogue of one 16 x 16 output tile of the weight-streaming
+// products (rows srow0 .. + 15, columns ocol0 .. + 15) from its exact int32
+// sum. Lane layout of a 16x16 accumulator: register r holds
+// D[o = 4 g + r][s = r16]. bias4 is the layer bias of the lane's 4 columns
+// (fetched by the caller ahead of time); first, if not null, holds the
+// tile's first outlier slice, also fetched ahead of time.
+template <GemmOut MODE>
+__device__ __forceinline__ void decode_tile_out(v4i sum, int lane, int64_t srow0, int64_t ocol0, int64_t s, int64_t h,
+                                                int64_t o, const float* __restrict__ c_x,
+                                                const float* __restrict__ c_w, const uint16_t* __restrict__ X_O,
+                                                int64_t ldo, const int32_t* __restrict__ idx, int n_o,
+                                                const uint16_t* __restrict__ W, const int8_t* __restrict__ Wq,
+                                                bool has_bias, uint2 bias4, void* __restrict__ Cout, const ZpArgs& zp,
+                                                const v8h* first) {
+    const int r16 = lane & 15, g = lane >> 4;
+    const int64_t srow = srow0 + r16;
+    const int64_t ocol = ocol0 + 4 * g;
+    if constexpr (MODE == GemmOut::Int32) {
+        int32_t* C = static_cast<int32_t*>(Cout);
+        if (srow < s) *reinterpret_cast<v4i*>(C + srow * o + ocol) = sum;
+    } else {
+        uint16_t* C = static_cast<uint16_t*>(Cout);
+        const float inv_x = __builtin_amdgcn_rcpf(srow < s ? c_x[srow] : 1.0f);
+        const v4f cw = *reinterpret_cast<const v4f*>(c_w + ocol);
+        v4f f;
+        if constexpr (MODE == GemmOut::ZeroPoint) {
+            // C' = C_i32 + zp_w (rowsum + (h - |O|) zp_x) + zp_x colsum', exact
+            // in int64 (colsum' = the column's code sum over the non-outlier rows)
+            const int zx = srow < s ? zp.zp_x[srow] : 0;
+            const int64_t zr =
+                srow < s ? static_cast<int64_t>(zp.rowsum_x[srow]) + (h - n_o) * static_cast<int64_t>(zx) : 0;
+            const v4i zw = *reinterpret_cast<const v4i*>(zp.zp_w + ocol);
+            v4i cs = *reinterpret_cast<const v4i*>(zp.colsum_w + ocol);
+            for (int q = 0; q < n_o; ++q) {
+                const int64_t k = idx[q];
+                const int8_t* p = Wq + (k >> 6) * o * 64 + ocol * 64 + (k & 63);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cs[e] -= p[e * 64];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t cp = static_cast<int64_t>(sum[e]) + static_cast<int64_t>(zw[e]) * zr +
+                                   static_cast<int64_t>(zx) * static_cast<int64_t>(cs[e]);
+                f[e] = static_cast<float>(cp) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
+        }
+        f = outlier_tile_16x16(f, lane, ocol0, srow0, s, o, X_O, ldo, idx, n_o, W, Wq, c_w, first);
+        if (has_bias) {
+            f[0] += half_bits_to_float(bias4.x & 0xffffu);
+            f[1] += half_bits_to_float(bias4.x >> 16);
+            f[2] += half_bits_to_float(bias4.y & 0xffffu);
+            f[3] += half_bits_to_float(bias4.y >> 16);
+        }
+        if (srow < s) {
+            const uint32_t lo = pack_half2(f[0], f[1]);
+            const uint32_t hi = pack_half2(f[2], f[3]);
+            *reinterpret_cast<uint2*>(C + srow * o + ocol) = make_uint2(lo, hi);
+        }
+    }
+}
+
 // Decode: block = kDecodeSplit (4) wavefronts on the same 16*NT output
 // columns, each streaming its share of K from HBM with two register batches
 // of kDecodeU K steps in flight (range-checked loads: steps past a wave's
 // range read as zero), then an exact int32 reduction of the partial tiles
-// through LDS. RG row groups of 16 (up to 16 RG rows of X) share every
-// weight load: each step multiplies the NT weight operands by RG operands
-// of X, and the reduction and the epilogue run once per row group.
-template <GemmOut MODE, int NT, int kDecodeU = 4, int kDecodeSplit = 4, int RG = 1>
+// through LDS. Up to 16 rows of X (one operand of the 16 x 16 x 64 MFMA).
+template <GemmOut MODE, int NT, int kDecodeU = 4, int kDecodeSplit = 4>
 __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
                                                      int64_t s, int64_t h, int64_t o,
                                                      const float* __restrict__ c_x, const float* __restrict__ c_w,
@@ -973,11 +1039,10 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(Wq + obase * 64, static_cast<uint32_t>(h * o - obase * 64));
     // Xq rows 0 .. s - 1; lanes of rows >= s fall past the range and read zero.
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(Xq, static_cast<uint32_t>(s * h));
-    uint32_t vA[NT], vB[RG];
+    uint32_t vA[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) vA[nt] = static_cast<uint32_t>((nt * 16 + r16) * 64 + g * 16);
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) vB[rg] = static_cast<uint32_t>((rg * 16 + r16) * h + g * 16);
+    const uint32_t vB = static_cast<uint32_t>(r16 * h + g * 16);
 
     // Wavefronts that finish an output tile fetch the first slice of its
     // outlier operands now, so the loads complete under the K loop.
@@ -997,17 +1062,15 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     const int64_t st0 = wid * per < nsteps ? wid * per : nsteps;
     const int64_t st1 = st0 + per < nsteps ? st0 + per : nsteps;
 
-    v4i acc[RG][NT];
+    v4i acc[NT];
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[rg][nt] = v4i{0, 0, 0, 0};
-    v4i a0[kDecodeU][NT], b0[kDecodeU][RG], a1[kDecodeU][NT], b1[kDecodeU][RG];
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = v4i{0, 0, 0, 0};
+    v4i a0[kDecodeU][NT], b0[kDecodeU], a1[kDecodeU][NT], b1[kDecodeU];
 
     // Steps past the wave's range get an out-of-range lane offset and a zero
     // scalar offset, so no sum of the two can wrap back into the range; rows
     // of X past s lie past the end of rB through their lane offset.
-    auto load = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU][RG], int64_t stb) {
+    auto load = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU], int64_t stb) {
 #pragma unroll
         for (int u = 0; u < kDecodeU; ++u) {
             const bool ok = stb + u < st1;
@@ -1015,18 +1078,15 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
             const uint32_t kB = ok ? static_cast<uint32_t>((stb + u) * 64) : 0u;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) a[u][nt] = buf_load16_nt(rA, ok ? vA[nt] : kOutOfRange, kA);
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg) b[u][rg] = buf_load16(rB, ok ? vB[rg] : kOutOfRange, kB);
+            b[u] = buf_load16(rB, ok ? vB : kOutOfRange, kB);
         }
     };
-    auto mma = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU][RG]) {
+    auto mma = [&](v4i (&a)[kDecodeU][NT], v4i (&b)[kDecodeU]) {
 #pragma unroll
         for (int u = 0; u < kDecodeU; ++u)
 #pragma unroll
-            for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    acc[rg][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][nt], b[u][rg], acc[rg][nt], 0, 0, 0);
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][nt], b[u], acc[nt], 0, 0, 0);
     };
 
     load(a0, b0, st0);
@@ -1036,69 +1096,153 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
         load(a0, b0, stb + 2 * kDecodeU);
         mma(a1, b1);
     }
-    // Lane layout of a 16x16 accumulator: register r holds D[o = 4 g + r][s = r16].
-    auto decode_epilogue = [&](int rg, int nt) {
-        v4i sum = red[0][nt][lane];
 #pragma unroll
-        for (int w = 1; w < kDecodeSplit; ++w) sum += red[w][nt][lane];
-        const int64_t srow = rg * 16 + r16;
-        const int64_t ocol = obase + nt * 16 + 4 * g;
-        if constexpr (MODE == GemmOut::Int32) {
-            int32_t* C = static_cast<int32_t*>(Cout);
-            if (srow < s) *reinterpret_cast<v4i*>(C + srow * o + ocol) = sum;
-        } else {
-            uint16_t* C = static_cast<uint16_t*>(Cout);
-            const float inv_x = __builtin_amdgcn_rcpf(srow < s ? c_x[srow] : 1.0f);
-            const v4f cw = *reinterpret_cast<const v4f*>(c_w + ocol);
-            v4f f;
-            if constexpr (MODE == GemmOut::ZeroPoint) {
-                // C' = C_i32 + zp_w (rowsum + (h - |O|) zp_x) + zp_x colsum', exact
-                // in int64 (colsum' = the column's code sum over the non-outlier rows)
-                const int zx = srow < s ? zp.zp_x[srow] : 0;
-                const int64_t zr =
-                    srow < s ? static_cast<int64_t>(zp.rowsum_x[srow]) + (h - n_o) * static_cast<int64_t>(zx) : 0;
-                const v4i zw = *reinterpret_cast<const v4i*>(zp.zp_w + ocol);
-                v4i cs = *reinterpret_cast<const v4i*>(zp.colsum_w + ocol);
-                for (int q = 0; q < n_o; ++q) {
-                    const int64_t k = idx[q];
-                    const int8_t* p = Wq + (k >> 6) * o * 64 + ocol * 64 + (k & 63);
+    for (int nt = 0; nt < NT; ++nt) red[wid][nt][lane] = acc[nt];
+    __syncthreads();
+    if (wid < NT) {
+        v4i sum = red[0][wid][lane];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) cs[e] -= p[e * 64];
-                }
+        for (int w = 1; w < kDecodeSplit; ++w) sum += red[w][wid][lane];
+        // the first outlier slice was fetched before the K loop
+        decode_tile_out<MODE>(sum, lane, 0, obase + wid * 16, s, h, o, c_x, c_w, X_O, ldo, idx, n_o, W, Wq,
+                              bias != nullptr, bias4, Cout, zp, pre);
+    }
+}
+
+// Weight streaming for 17..64 rows with the codes of X shared through LDS:
+// each of the four wavefronts of a block owns 16 NT adjacent output columns
+// and streams their weights over the whole of K, kRing K steps ahead in
+// registers; the block stages X's codes (RG row groups of 16) in LDS chunks
+// of kSkinnyChunk K steps, double-buffered by direct-to-LDS loads, and every
+// wavefront reads them from there. A block thus fetches X once (not once
+// per wavefront) and needs no reduction; its wavefronts meet once per chunk.
+// Columns are always whole 16-column tiles (16 NT divides 64, which divides
+// o); wavefronts past o stage X and wait with the others but read no
+// weights and write nothing.
+// Measured on 12288 x 49152 (forward, us; the K-split kernel with RG row
+// groups and, past 48 rows, the tiled product in brackets): 17 rows 101.0
+// (102.2), 32 rows 106.7 (119.4), 48 rows 124.3 (139.5), 49 rows 129.0
+// (161.8), 64 rows 144.6 (163.4), with NT = 1. NT = 2, rings of 12 or 16
+// steps, 8-step chunks, 8 wavefronts per block, three LDS stages and X
+// staged through registers all measured the same or slower. A timing-only
+// copy without the staging of X ran 64 rows in 110 us: X's share grows with
+// s and is not explained by its L2 bytes (halving them changed nothing).
+constexpr int kSkinnyChunk = 4;
+
+template <GemmOut MODE, int NT, int RG>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
+                                                     int64_t s, int64_t h, int64_t o,
+                                                     const float* __restrict__ c_x, const float* __restrict__ c_w,
+                                                     const uint16_t* __restrict__ X_O, int64_t ldo,
+                                                     const int32_t* __restrict__ idx,
+                                                     const int32_t* __restrict__ n_out,
+                                                     const uint16_t* __restrict__ W,
+                                                     const uint16_t* __restrict__ bias, void* __restrict__ Cout,
+                                                     uint32_t* __restrict__ clear, int clear_words, ZpArgs zp) {
+    constexpr int kRing = 2 * kSkinnyChunk;   // weight steps in flight
+    // xs[buffer][step of the chunk][row group]: one 16 x 64 operand, lane-ordered
+    __shared__ v4i xs[2][kSkinnyChunk][RG][64];
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int r16 = lane & 15, g = lane >> 4;
+    const int64_t wcol = (static_cast<int64_t>(blockIdx.x) * 4 + wid) * 16 * NT;
+    const bool live = wcol < o;
+    const int64_t nsteps = h / 64;
+
+    // this wavefront's weight columns: panel p of them starts p o 64 bytes
+    // past the resource base (a step's uniform offset); a wavefront past o
+    // gets an empty resource
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(live ? Wq + wcol * 64 : Wq, live ? static_cast<uint32_t>(h * o - wcol * 64) : 0u);
+    uint32_t vA[NT];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t cp = static_cast<int64_t>(sum[e]) + static_cast<int64_t>(zw[e]) * zr +
-                                       static_cast<int64_t>(zx) * static_cast<int64_t>(cs[e]);
-                    f[e] = static_cast<float>(cp) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
-                }
-            } else {
+    for (int nt = 0; nt < NT; ++nt) vA[nt] = static_cast<uint32_t>((nt * 16 + r16) * 64 + g * 16);
+    auto load_w = [&](v4i (&a)[NT], int64_t st) {
+        const bool ok = st < nsteps;
+        const uint32_t k = ok ? static_cast<uint32_t>(st * o * 64) : 0u;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) f[e] = static_cast<float>(sum[e]) * (inv_x * __builtin_amdgcn_rcpf(cw[e]));
-            }
-            // the first slice of row group 0 was fetched before the K loop
-            f = outlier_tile_16x16(f, lane, obase + nt * 16, rg * 16, s, o, X_O, ldo, idx, n_o, W, Wq, c_w,
-                                   rg == 0 ? pre : nullptr);
-            if (bias != nullptr) {
-                f[0] += half_bits_to_float(bias4.x & 0xffffu);
-                f[1] += half_bits_to_float(bias4.x >> 16);
-                f[2] += half_bits_to_float(bias4.y & 0xffffu);
-                f[3] += half_bits_to_float(bias4.y >> 16);
-            }
-            if (srow < s) {
-                const uint32_t lo = pack_half2(f[0], f[1]);
-                const uint32_t hi = pack_half2(f[2], f[3]);
-                *reinterpret_cast<uint2*>(C + srow * o + ocol) = make_uint2(lo, hi);
-            }
+        for (int nt = 0; nt < NT; ++nt) a[nt] = buf_load16_nt(rA, ok ? vA[nt] : kOutOfRange, k);
+    };
+    // X's codes: rows 0 .. s - 1 (lanes of rows >= s fall past the range and
+    // read zero; so do steps past K). Wavefront w stages operands
+    // b = w + 4 i (i < RG) of each chunk: step b / RG, row group b % RG.
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(Xq, static_cast<uint32_t>(s * h));
+    auto stage_x = [&](int64_t chunk, int buf) {
+#pragma unroll
+        for (int i = 0; i < RG; ++i) {
+            const int b = wid + 4 * i, j = b / RG, rg = b % RG;
+            const int64_t st = chunk * kSkinnyChunk + j;
+            const uint32_t off = st < nsteps ? static_cast<uint32_t>((rg * 16 + r16) * h + st * 64 + g * 16) : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(&xs[buf][j][rg][0]), 16, off, 0, 0, 0);
         }
     };
+
+    int n_o = 0;
+    uint2 bias4[NT];
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        if (rg > 0) __syncthreads();   // every wavefront has read the previous round
+    for (int nt = 0; nt < NT; ++nt) bias4[nt] = make_uint2(0u, 0u);
+    if constexpr (MODE == GemmOut::Mixed || MODE == GemmOut::ZeroPoint) {
+        n_o = __builtin_amdgcn_readfirstlane(n_out[0]);
+        if (live && bias != nullptr)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) red[wid][nt][lane] = acc[rg][nt];
-        __syncthreads();
-        if (wid < NT) decode_epilogue(rg, wid);
+            for (int nt = 0; nt < NT; ++nt) bias4[nt] = *reinterpret_cast<const uint2*>(bias + wcol + nt * 16 + 4 * g);
     }
+
+    v4i acc[RG][NT];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[rg][nt] = v4i{0, 0, 0, 0};
+    v4i wr[kRing][NT];
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) load_w(wr[i], i);
+    stage_x(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): chunk 0 (and the first weights) in place
+    __syncthreads();
+
+    // One chunk from buffer `buf`, whose weights sit in ring slots slot0 ..
+    // slot0 + kSkinnyChunk - 1; the next chunk is staged into the other
+    // buffer first, and each slot is refilled kRing steps ahead once used.
+    auto chunk_step = [&](int64_t c, int buf, int slot0) __attribute__((always_inline)) {
+        stage_x(c + 1, buf ^ 1);
+        asm volatile("" ::: "memory");   // the weight loads below stay after the staging
+#pragma unroll
+        for (int j = 0; j < kSkinnyChunk; ++j) {
+            v4i b[RG];
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) b[rg] = xs[buf][j][rg][lane];
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[rg][nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wr[slot0 + j][nt], b[rg], acc[rg][nt], 0, 0, 0);
+            load_w(wr[slot0 + j], c * kSkinnyChunk + j + kRing);
+        }
+        // The barrier's fence does not cover direct-to-LDS loads: wait for
+        // this wavefront's staging of chunk c + 1, which is older than the
+        // kSkinnyChunk NT weight loads issued after it (loads return in order).
+        __builtin_amdgcn_s_waitcnt(0x0f70 | (kSkinnyChunk * NT));
+        __syncthreads();
+    };
+    const int64_t nchunks = (nsteps + kSkinnyChunk - 1) / kSkinnyChunk;
+    for (int64_t c = 0; c < nchunks; c += 2) {
+        chunk_step(c, 0, 0);
+        chunk_step(c + 1, 1, kSkinnyChunk);   // past K when nchunks is odd: zeros
+    }
+    // the last staging (past K) still writes zeros into LDS: let it land
+    // before the block can end
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+
+    if (!live) return;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+        if (rg * 16 < s)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                decode_tile_out<MODE>(acc[rg][nt], lane, rg * 16, wcol + nt * 16, s, h, o, c_x, c_w, X_O, ldo, idx,
+                                      n_o, W, Wq, bias != nullptr, bias4[nt], Cout, zp, nullptr);
 }
 
 // ------------------------------------------------------------------ single-launch decode forward
@@ -1371,31 +1515,35 @@ hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, 
                        const int32_t* idx, const int32_t* n_out, const int8_t* Wq, const float* c_w,
                        const uint16_t* W, const uint16_t* bias, int64_t s, int64_t h, int64_t o, void* C,
                        hipStream_t stream, uint32_t* clear, int clear_words, ZpArgs zp) {
-    // Weight streaming for up to 48 rows: 64 output columns per block (one
-    // 16-column tile per wavefront in the epilogue), batches of two K steps:
-    // 7.06 TB/s of weights on the 8 x 12288 x 49152 layer against 6.64 TB/s
-    // with 32 columns and batches of four. More rows share each weight load
-    // as 2 or 3 row groups; every block still reads all of Xq, whose L2
-    // traffic grows with s, so on that layer (forward, us) 17-32 rows take
-    // 102-119 against 155-157 for the tiled product and 33-48 rows 122-140
-    // against 157-161, while 4 row groups (49-64 rows, one wavefront per
-    // SIMD at 272 registers) lost to it (156-175 against 158-163).
-#define I8MM_DECODE(NT, RG)                                                                                       \
-    hipLaunchKernelGGL((k_gemm_decode<MODE, NT, 2, 4, RG>), dim3(static_cast<unsigned>(o / (16 * NT))), dim3(256), \
-                       0, stream, Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp)
+    // Weight streaming. Up to 16 rows: the K-split kernel, 64 output columns
+    // per block (one 16-column tile per wavefront in the epilogue), batches
+    // of two K steps: 7.06 TB/s of weights on the 8 x 12288 x 49152 layer
+    // against 6.64 TB/s with 32 columns and batches of four. 17-64 rows: the
+    // column-split kernel with X in LDS (k_gemm_skinny), 2, 3 or 4 row
+    // groups of 16; on that layer (forward) 101-145 us, where the K-split
+    // kernel with 2-4 row groups took 102-175 us and the tiled product
+    // 155-163 us.
     if (s <= 16) {
-        I8MM_DECODE(4, 1);
-    } else if (s <= 32) {
-        I8MM_DECODE(4, 2);
-    } else if (s <= 48) {
-        I8MM_DECODE(4, 3);
+        hipLaunchKernelGGL((k_gemm_decode<MODE, 4, 2, 4>), dim3(static_cast<unsigned>(o / 64)), dim3(256), 0, stream,
+                           Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp);
+    } else if (s <= 64) {
+#define I8MM_SKINNY(RG)                                                                                            \
+    hipLaunchKernelGGL((k_gemm_skinny<MODE, 1, RG>), dim3(static_cast<unsigned>(o / 64)), dim3(256), 0, stream, Xq, \
+                       Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp)
+        if (s <= 32) {
+            I8MM_SKINNY(2);
+        } else if (s <= 48) {
+            I8MM_SKINNY(3);
+        } else {
+            I8MM_SKINNY(4);
+        }
+#undef I8MM_SKINNY
     } else {
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);
         hipLaunchKernelGGL((k_gemm_prefill<MODE>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream,
                            Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp,
                            tile_group(h, o), nullptr, nullptr);
     }
-#undef I8MM_DECODE
     return hipGetLastError();
 }
 

@@ -1,8 +1,12 @@
-"""The weight-streaming product's row groups (1, 2 or 3 groups of 16 rows of
-X for up to 16, 32 and 48 rows; the tiled product above 48) at each
-boundary, against the oracle: the outlier set, Xq, c_x, X_O and C_i32 bit
-for bit, C within 2e-3 ||C_ref||_inf. The one-call forward, the four-step
-product and the int32 product all dispatch on s the same way."""
+"""The products at each row-count boundary, against the oracle: the K-split
+weight-streaming kernel up to 16 rows, the column-split one with X's codes
+in LDS for 17-64 rows (2, 3 or 4 row groups of 16), the tiled product
+above 64. Checked bit for bit: the outlier set, Xq, c_x, X_O and C_i32; C
+within 2e-3 ||C_ref||_inf. The one-call forward, the four-step product and
+the int32 product all dispatch on s the same way. The column-split kernel
+stages K in chunks of four 64-wide steps, two chunks per loop: the uneven
+shapes give an odd number of chunks, a last chunk with one to three steps,
+a single step, and column counts that are not a multiple of 256."""
 
 import numpy as np
 import pytest
@@ -15,13 +19,12 @@ from workloads import random_case
 
 pytestmark = pytest.mark.gpu
 
-ROWS = [16, 17, 32, 33, 48, 49]
+ROWS = [16, 17, 32, 33, 48, 49, 64, 65]
+UNEVEN = [(40, 4160, 192, 5), (24, 64, 64, 1), (64, 448, 320, 3), (17, 192, 128, 2), (56, 1216, 576, 9)]
 
 
-@pytest.mark.parametrize("s", ROWS)
-def test_row_group_boundaries(s):
-    h, o = 4096, 1024
-    inp = random_case(1700 + s, s, h, o, 6, row_frac=0.5)
+def _check_shape(seed, s, h, o, nout):
+    inp = random_case(seed, s, h, o, nout, row_frac=0.5)
     X, W = inp["X"], inp["W"]
     Xd, Wd = T(X), T(W)
     say(f"  launch: forward + int8_gemm_i32 + int8_mixed_matmul s={s} h={h} o={o}")
@@ -42,7 +45,17 @@ def test_row_group_boundaries(s):
     assert torch.equal(C, C4), "the one-call forward and the four-step product differ"
 
 
-@pytest.mark.parametrize("s", [20, 40])
+@pytest.mark.parametrize("s", ROWS)
+def test_row_group_boundaries(s):
+    _check_shape(1700 + s, s, 4096, 1024, 6)
+
+
+@pytest.mark.parametrize("s,h,o,nout", UNEVEN, ids=[f"s{c[0]}h{c[1]}o{c[2]}" for c in UNEVEN])
+def test_uneven_k_and_columns(s, h, o, nout):
+    _check_shape(1800 + s + h, s, h, o, nout)
+
+
+@pytest.mark.parametrize("s", [20, 40, 60])
 def test_row_groups_without_fp16_weights_and_with_bias(s):
     h, o = 2048, 512
     inp = random_case(1760 + s, s, h, o, 5, row_frac=0.5)

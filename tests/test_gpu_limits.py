@@ -1,7 +1,8 @@
 """Parity at the size limits: the largest weight extent the products accept
 (h * o just below 2^31: Wq and the fp16 weight rows are read through 32-bit
-buffer offsets), on the weight-streaming (s <= 16) and the tiled (s > 16)
-product, through the one-call forward the benchmark times; and tall inputs
+buffer offsets), on the two weight-streaming products (s <= 16, 17..64)
+and the tiled one (s > 64), through the one-call forward the benchmark
+times; and tall inputs
 (up to 2^18 rows).
 
 Every code of the converted weights, every c_w and every element of C_i32 is
@@ -61,7 +62,7 @@ def max_extent_weights():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("s", [16, 300])
+@pytest.mark.parametrize("s", [16, 40, 300])
 def test_largest_weight_extent(max_extent_weights, s):
     W, Wd, Wq, c_w, Wq_t_r, cw_r = max_extent_weights
     h, o = W.shape

@@ -202,8 +202,8 @@ def test_forward_paths_match_separate_calls(s, h, o, nout, alpha):
 
 def test_forward_workspace_reuse_across_shapes():
     """One workspace, shapes alternating between the two prologue paths
-    (few rows: slabs of 128 columns with 16 and 48 rows; many rows:
-    detection then rows)."""
+    (few rows: slabs of 128 columns, one and four groups of 16 rows; many
+    rows: detection then rows)."""
     big = i8.forward_workspace(1100, 640, DEV)
     for (s, h, o, nout) in [(1100, 640, 256, 5), (8, 640, 256, 3), (40, 640, 256, 4), (600, 640, 320, 9),
                             (8, 640, 256, 3), (40, 640, 256, 4)]:

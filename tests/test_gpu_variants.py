@@ -22,7 +22,8 @@ pytestmark = pytest.mark.gpu
 
 # (seed, s, h, o, n_outliers, alpha)
 SHAPES = [(0, 8, 1024, 512, 3, 6.0), (1, 300, 1088, 448, 5, 6.0), (2, 17, 192, 320, 2, 6.0),
-          (3, 40, 512, 256, 0, float("inf")), (4, 260, 640, 576, 100, 6.0), (5, 5, 12288, 128, 7, 6.0)]
+          (3, 40, 512, 256, 0, float("inf")), (4, 260, 640, 576, 100, 6.0), (5, 5, 12288, 128, 7, 6.0),
+          (6, 64, 704, 192, 4, 6.0)]
 IDS = [f"s{c[1]}h{c[2]}n{c[4]}a{c[5]}" for c in SHAPES]
 
 
