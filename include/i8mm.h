@@ -330,7 +330,7 @@ i8mm_status i8mm_zeropoint_matmul(const int8_t* Xq, const float* nd_x, const int
 
 /* Bytes at the start of the forward workspace that hold the cross-block
  * accumulator of the detection (the outlier mask being ORed together, or,
- * for inputs of at most 64 rows, the per-row maxima). */
+ * for inputs of at most 8 rows, the per-row maxima). */
 #define I8MM_FORWARD_ACC_BYTES 16640
 
 /*
@@ -442,7 +442,7 @@ i8mm_status i8mm_forward_decode(const uint16_t* X, int64_t s, int64_t h, int64_t
                                 void* workspace, uint16_t* C, hipStream_t stream);
 
 /* Smallest row count of i8mm_forward_inline_quant. */
-#define I8MM_INLINE_QUANT_MIN_ROWS 65
+#define I8MM_INLINE_QUANT_MIN_ROWS 129
 
 /*
  * i8mm_forward with the row quantisation folded into the product: the
@@ -458,9 +458,8 @@ i8mm_status i8mm_forward_decode(const uint16_t* X, int64_t s, int64_t h, int64_t
  * bit (the same codes, made by the same rounding). Arguments, workspace
  * and errors as for i8mm_forward; the workspace's Xq region is not
  * written. s < I8MM_INLINE_QUANT_MIN_ROWS gives I8MM_EINVAL: with fewer
- * rows the forward's prologue is the few-row pair of kernels, which makes
- * the codes in the same pass as the row constants, and the product is one
- * of the weight-streaming kernels, not the tiled one this variant changes.
+ * rows the forward's product is one of the weight-streaming kernels, not
+ * the tiled one this variant changes.
  */
 i8mm_status i8mm_forward_inline_quant(const uint16_t* X, int64_t s, int64_t h, int64_t o, float alpha,
                                       const int8_t* Wq, const float* c_w, const uint16_t* W, const uint16_t* bias,

@@ -18,7 +18,7 @@
 // regroups them through LDS into full 256-byte rows.
 //
 // Three main loops share the epilogue structure:
-//  * k_gemm_prefill (s > 64): 256x256 output tile per 256-thread block, K
+//  * k_gemm_prefill (s > 128): 256x256 output tile per 256-thread block, K
 //    step 128 (two panels), both operands double buffered in LDS through
 //    direct-to-LDS buffer loads, v_mfma_i32_32x32x32_i8, 2x2 waves of
 //    128x128.
@@ -27,15 +27,17 @@
 //    HBM into the MFMA operand registers with non-temporal loads
 //    (v_mfma_i32_16x16x64_i8, rows beyond s read as zero), two register
 //    batches in flight.
-//  * k_gemm_skinny (17 <= s <= 64): weight streaming with the columns split
-//    between the wavefronts of a block, each over all of K with a ring of
-//    weight steps in registers, and X's codes (two to four row groups of
-//    16) staged once per block in LDS.
+//  * k_gemm_skinny (17 <= s <= 128): weight streaming with the columns split
+//    between the wavefronts of a block (one block per CU where the columns
+//    allow), each over all of K with a ring of weight steps in registers,
+//    and X's codes (two to eight row groups of 16) staged once per block
+//    in LDS.
 // The fused epilogue converts the int32 accumulator to fp32, multiplies by
 // 1/c_x_i * 1/c_w_j (S is never materialised), then accumulates the fp16
 // outlier product on top with fp16 MFMA (fp32 accumulate), adds the
 // optional layer bias and rounds once to fp16.
 
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -1109,28 +1111,32 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     }
 }
 
-// Weight streaming for 17..64 rows with the codes of X shared through LDS:
-// each of the four wavefronts of a block owns 16 NT adjacent output columns
-// and streams their weights over the whole of K, kRing K steps ahead in
-// registers; the block stages X's codes (RG row groups of 16) in LDS chunks
-// of kSkinnyChunk K steps, double-buffered by direct-to-LDS loads, and every
-// wavefront reads them from there. A block thus fetches X once (not once
-// per wavefront) and needs no reduction; its wavefronts meet once per chunk.
-// Columns are always whole 16-column tiles (16 NT divides 64, which divides
-// o); wavefronts past o stage X and wait with the others but read no
-// weights and write nothing.
-// Measured on 12288 x 49152 (forward, us; the K-split kernel with RG row
-// groups and, past 48 rows, the tiled product in brackets): 17 rows 101.0
-// (102.2), 32 rows 106.7 (119.4), 48 rows 124.3 (139.5), 49 rows 129.0
-// (161.8), 64 rows 144.6 (163.4), with NT = 1. NT = 2, rings of 12 or 16
-// steps, 8-step chunks, 8 wavefronts per block, three LDS stages and X
-// staged through registers all measured the same or slower. A timing-only
-// copy without the staging of X ran 64 rows in 110 us: X's share grows with
-// s and is not explained by its L2 bytes (halving them changed nothing).
+// Weight streaming for 17..128 rows with the codes of X shared through LDS:
+// each of the kWaves wavefronts of a block owns 16 NT adjacent output
+// columns and streams their weights over the whole of K, kRing K steps
+// ahead in registers; the block stages X's codes (RG row groups of 16) in
+// LDS chunks of kSkinnyChunk K steps, double-buffered by direct-to-LDS
+// loads, and every wavefront reads them from there. A block thus fetches X
+// once (not once per wavefront) and needs no reduction; its wavefronts meet
+// once per chunk. The launch sizes blocks to one per CU where the columns
+// allow: a CU's texture address unit serves both the weight stream and the
+// staging of X (16 bytes per lane each), so every extra block per CU
+// re-staging X slows the weight stream. Columns are always whole 16-column
+// tiles (16 NT divides 64, which divides o); wavefronts past o stage X and
+// wait with the others but read no weights and write nothing.
+// Measured on 12288 x 49152 (forward with the slab prologue, us): 12
+// wavefronts (one block per CU)
+// 99.7 / 101.6 / 104.7 / 107.5 / 110.3 for 17 / 32 / 48 / 49 / 64 rows;
+// 4 wavefronts (three blocks per CU) 101.5 / 107.1 / 124.4 / 128.8 / 144.7;
+// the K-split kernel with row groups 102.8 / 119.1 / 139.5 and the tiled
+// product 162-163 past 48 rows; 106.6 / 116.8 / 131.4 for 65 / 96 / 128
+// rows against 155.2 / 160.0 / 164.9 for the tiled product. NT = 2, longer
+// rings or chunks, three LDS stages and X staged through registers
+// measured the same or slower.
 constexpr int kSkinnyChunk = 4;
 
-template <GemmOut MODE, int NT, int RG>
-__global__ __launch_bounds__(256) void k_gemm_skinny(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
+template <GemmOut MODE, int NT, int RG, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void k_gemm_skinny(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq,
                                                      int64_t s, int64_t h, int64_t o,
                                                      const float* __restrict__ c_x, const float* __restrict__ c_w,
                                                      const uint16_t* __restrict__ X_O, int64_t ldo,
@@ -1143,11 +1149,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const int8_t* __restrict__ 
     // xs[buffer][step of the chunk][row group]: one 16 x 64 operand, lane-ordered
     __shared__ v4i xs[2][kSkinnyChunk][RG][64];
     if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < clear_words; i += 256) clear[i] = 0u;
+        for (int i = threadIdx.x; i < clear_words; i += 64 * kWaves) clear[i] = 0u;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int r16 = lane & 15, g = lane >> 4;
-    const int64_t wcol = (static_cast<int64_t>(blockIdx.x) * 4 + wid) * 16 * NT;
+    const int64_t wcol = (static_cast<int64_t>(blockIdx.x) * kWaves + wid) * 16 * NT;
     const bool live = wcol < o;
     const int64_t nsteps = h / 64;
 
@@ -1167,12 +1173,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const int8_t* __restrict__ 
     };
     // X's codes: rows 0 .. s - 1 (lanes of rows >= s fall past the range and
     // read zero; so do steps past K). Wavefront w stages operands
-    // b = w + 4 i (i < RG) of each chunk: step b / RG, row group b % RG.
+    // b = w, w + kWaves, ... of each chunk: step b / RG, row group b % RG.
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(Xq, static_cast<uint32_t>(s * h));
     auto stage_x = [&](int64_t chunk, int buf) {
-#pragma unroll
-        for (int i = 0; i < RG; ++i) {
-            const int b = wid + 4 * i, j = b / RG, rg = b % RG;
+        for (int b = wid; b < kSkinnyChunk * RG; b += kWaves) {
+            const int j = b / RG, rg = b % RG;
             const int64_t st = chunk * kSkinnyChunk + j;
             const uint32_t off = st < nsteps ? static_cast<uint32_t>((rg * 16 + r16) * h + st * 64 + g * 16) : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, LDS_PTR(&xs[buf][j][rg][0]), 16, off, 0, 0, 0);
@@ -1507,6 +1512,24 @@ __global__ __launch_bounds__(256) void k_outlier_only(const uint16_t* __restrict
 // Cache, else 8. On 4096 x 12288 x 36864 (453 MB of weights) 4 took the
 // product from 1554 to 1494 us; on 4096 x 8192 x 28672 (235 MB) 8 is 2 %
 // faster than 4.
+// Compute units of the current device (read once per device).
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 constexpr int64_t kMallBytes = int64_t(256) << 20;
 uint32_t tile_group(int64_t hb, int64_t o) { return hb * o > kMallBytes ? 4u : 8u; }
 
@@ -1518,25 +1541,45 @@ hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, 
     // Weight streaming. Up to 16 rows: the K-split kernel, 64 output columns
     // per block (one 16-column tile per wavefront in the epilogue), batches
     // of two K steps: 7.06 TB/s of weights on the 8 x 12288 x 49152 layer
-    // against 6.64 TB/s with 32 columns and batches of four. 17-64 rows: the
-    // column-split kernel with X in LDS (k_gemm_skinny), 2, 3 or 4 row
-    // groups of 16; on that layer (forward) 101-145 us, where the K-split
-    // kernel with 2-4 row groups took 102-175 us and the tiled product
-    // 155-163 us.
+    // against 6.64 TB/s with 32 columns and batches of four. 17-128 rows:
+    // the column-split kernel with X in LDS (k_gemm_skinny), 2, 3, 4, 6 or 8
+    // row groups of 16; on that layer (forward) 96-103 us for 17-64 rows
+    // and 107-136 us for 65-128, where the tiled product takes 155-165 us.
     if (s <= 16) {
         hipLaunchKernelGGL((k_gemm_decode<MODE, 4, 2, 4>), dim3(static_cast<unsigned>(o / 64)), dim3(256), 0, stream,
                            Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp);
-    } else if (s <= 64) {
-#define I8MM_SKINNY(RG)                                                                                            \
-    hipLaunchKernelGGL((k_gemm_skinny<MODE, 1, RG>), dim3(static_cast<unsigned>(o / 64)), dim3(256), 0, stream, Xq, \
-                       Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp)
-        if (s <= 32) {
-            I8MM_SKINNY(2);
-        } else if (s <= 48) {
-            I8MM_SKINNY(3);
+    } else if (s <= 128) {
+        // one block per CU where the 16-column tiles allow: the fewest
+        // wavefronts per block (4, 8, 12 or 16) whose blocks fit the CUs
+        const int64_t tiles = o / 16;
+        const int64_t per_cu = (tiles + cu_count() - 1) / cu_count();
+        const int waves = per_cu <= 4 ? 4 : per_cu <= 8 ? 8 : per_cu <= 12 ? 12 : 16;
+        const dim3 grid(static_cast<unsigned>((tiles + waves - 1) / waves)), block(static_cast<unsigned>(64 * waves));
+#define I8MM_SKINNY(RG, WV)                                                                                        \
+    hipLaunchKernelGGL((k_gemm_skinny<MODE, 1, RG, WV>), grid, block, 0, stream, Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, \
+                       idx, n_out, W, bias, C, clear, clear_words, zp)
+#define I8MM_SKINNY_RG(WV)          \
+    if (s <= 32) {                  \
+        I8MM_SKINNY(2, WV);         \
+    } else if (s <= 48) {           \
+        I8MM_SKINNY(3, WV);         \
+    } else if (s <= 64) {           \
+        I8MM_SKINNY(4, WV);         \
+    } else if (s <= 96) {           \
+        I8MM_SKINNY(6, WV);         \
+    } else {                        \
+        I8MM_SKINNY(8, WV);         \
+    }
+        if (waves == 4) {
+            I8MM_SKINNY_RG(4)
+        } else if (waves == 8) {
+            I8MM_SKINNY_RG(8)
+        } else if (waves == 12) {
+            I8MM_SKINNY_RG(12)
         } else {
-            I8MM_SKINNY(4);
+            I8MM_SKINNY_RG(16)
         }
+#undef I8MM_SKINNY_RG
 #undef I8MM_SKINNY
     } else {
         const int64_t tiles = ((s + kTS - 1) / kTS) * ((o + kTO - 1) / kTO);

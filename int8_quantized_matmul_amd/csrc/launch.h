@@ -22,9 +22,9 @@ hipError_t launch_quantize_rows(const uint16_t* X, int64_t s, int64_t h,
 
 // Forward path: detection + index list + row quantisation in two launches.
 // Cross-block state (the mask accumulator, or the row maxima for inputs of
-// at most 64 rows) goes to `acc`, which must be zero on entry;
+// at most 8 rows) goes to `acc`, which must be zero on entry;
 // *clear_words is how many of its words the product launch must clear
-// again (see launch_int8_gemm). For s > 64, Xq may be null: the codes are
+// again (see launch_int8_gemm). For s > 8, Xq may be null: the codes are
 // then not written (launch_int8_gemm_inline_quant makes them).
 hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, float alpha, uint32_t* acc,
                                    uint32_t* mask, int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x,

@@ -253,16 +253,20 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Forward path for few rows (s <= 16 RG): blocks of 256 threads on
-// 128-column slabs, thread t on the 8-column chunk t % 16 of rows
-// t / 16 + 16 g, g < RG. A block of k_small_detect sees every row of its
+// Forward path for few rows (the one-call forward takes it for s <= 8, the
+// kernels hold up to 16 RG rows): blocks of 256 threads on 128-column
+// slabs, thread t on the 8-column chunk t % 16 of rows t / 16 + 16 g,
+// g < RG. A block of k_small_detect sees every row of its
 // slab, so it writes the slab's mask words itself and folds the per-row
 // maxima over its non-outlier columns into `rowmax` with an integer
 // atomicMax on the float bits (non-negative floats order like their bit
 // patterns); k_small_quant then quantises with the finished row maxima.
 // rowmax must be zero beforehand.
 constexpr int kSlabCols = 128;
-constexpr int kSmallRowsMax = 64;
+// Up to 8 rows the slab pair and detection + row pass take the same time
+// on 12288 columns (~94 us per decode forward); from 16 rows on, detection
+// + row pass is 2.6-7.4 us faster per forward (16-64 rows).
+constexpr int kSmallRowsMax = 8;
 
 template <int RG>
 __global__ __launch_bounds__(256) void k_small_detect(const uint16_t* __restrict__ X, int s, int h, Threshold th,
@@ -667,9 +671,7 @@ hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, floa
     hipLaunchKernelGGL(k_small_detect<RG>, grid, block, 0, stream, X, si, hi, th, mask, acc);              \
     hipLaunchKernelGGL(k_small_quant<RG>, grid, block, 0, stream, X, si, hi, mask, acc, idx, n_out, Xq, c_x, \
                        X_O, ldo)
-        if (s <= 16) { I8MM_SMALL(1); }
-        else if (s <= 32) { I8MM_SMALL(2); }
-        else { I8MM_SMALL(4); }
+        I8MM_SMALL(1);
 #undef I8MM_SMALL
         return hipGetLastError();
     }

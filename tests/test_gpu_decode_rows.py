@@ -1,7 +1,7 @@
 """The products at each row-count boundary, against the oracle: the K-split
 weight-streaming kernel up to 16 rows, the column-split one with X's codes
-in LDS for 17-64 rows (2, 3 or 4 row groups of 16), the tiled product
-above 64. Checked bit for bit: the outlier set, Xq, c_x, X_O and C_i32; C
+in LDS for 17-128 rows (2, 3, 4, 6 or 8 row groups of 16), the tiled
+product above 128. Checked bit for bit: the outlier set, Xq, c_x, X_O and C_i32; C
 within 2e-3 ||C_ref||_inf. The one-call forward, the four-step product and
 the int32 product all dispatch on s the same way. The column-split kernel
 stages K in chunks of four 64-wide steps, two chunks per loop: the uneven
@@ -19,8 +19,9 @@ from workloads import random_case
 
 pytestmark = pytest.mark.gpu
 
-ROWS = [16, 17, 32, 33, 48, 49, 64, 65]
-UNEVEN = [(40, 4160, 192, 5), (24, 64, 64, 1), (64, 448, 320, 3), (17, 192, 128, 2), (56, 1216, 576, 9)]
+ROWS = [16, 17, 32, 33, 48, 49, 64, 65, 96, 97, 128, 129]
+UNEVEN = [(40, 4160, 192, 5), (24, 64, 64, 1), (64, 448, 320, 3), (17, 192, 128, 2), (56, 1216, 576, 9),
+          (100, 704, 192, 4), (128, 64, 3136, 2)]
 
 
 def _check_shape(seed, s, h, o, nout):
@@ -55,7 +56,7 @@ def test_uneven_k_and_columns(s, h, o, nout):
     _check_shape(1800 + s + h, s, h, o, nout)
 
 
-@pytest.mark.parametrize("s", [20, 40, 60])
+@pytest.mark.parametrize("s", [20, 40, 60, 90, 120])
 def test_row_groups_without_fp16_weights_and_with_bias(s):
     h, o = 2048, 512
     inp = random_case(1760 + s, s, h, o, 5, row_frac=0.5)

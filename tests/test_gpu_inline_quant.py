@@ -22,10 +22,10 @@ from workloads import get_config, make_inputs, planted_on_row_subset, random_cas
 pytestmark = pytest.mark.gpu
 
 # (seed, s, h, o, planted outlier columns, alpha)
-SHAPES = [(1, 65, 256, 512, 2, 6.0), (2, 300, 640, 576, 5, 6.0), (3, 513, 384, 768, 40, 6.0),
-          (4, 257, 1088, 832, 3, 6.0), (5, 128, 192, 320, 1, 6.0), (6, 96, 4096, 256, 7, 6.0),
-          (7, 200, 512, 256, 0, 6.0), (8, 80, 256, 128, 3, 0.0), (9, 150, 512, 384, 6, float("inf")),
-          (10, 65, 133120, 256, 4, 6.0)]
+SHAPES = [(1, 129, 256, 512, 2, 6.0), (2, 300, 640, 576, 5, 6.0), (3, 513, 384, 768, 40, 6.0),
+          (4, 257, 1088, 832, 3, 6.0), (5, 160, 192, 320, 1, 6.0), (6, 130, 4096, 256, 7, 6.0),
+          (7, 200, 512, 256, 0, 6.0), (8, 144, 256, 128, 3, 0.0), (9, 150, 512, 384, 6, float("inf")),
+          (10, 129, 133120, 256, 4, 6.0)]
 
 
 def _run(X, W, alpha, fp16_weights=True, bias=None):

@@ -1,7 +1,7 @@
 """Parity at the size limits: the largest weight extent the products accept
 (h * o just below 2^31: Wq and the fp16 weight rows are read through 32-bit
 buffer offsets), on the two weight-streaming products (s <= 16, 17..64)
-and the tiled one (s > 64), through the one-call forward the benchmark
+and the tiled one (s > 128), through the one-call forward the benchmark
 times; and tall inputs
 (up to 2^18 rows).
 

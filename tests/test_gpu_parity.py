@@ -160,9 +160,11 @@ def test_forward_matches_separate_calls_and_is_deterministic():
     assert torch.equal(v["Xq"], g["Xq"]) and torch.equal(v["c_x"], g["c_x"])
 
 
-# Forward paths: s <= 64 runs the slab kernels (row groups of 16: s <= 16, 32,
-# 64), larger s the accumulator path with one wavefront per row, the row held
-# in registers for h <= 16384 (chunks per lane 2 .. 32) and re-read above.
+# Forward paths: s <= 8 runs the slab kernels (one row group of 16), larger s
+# the accumulator path (detection, then one to four wavefronts per row, the
+# row held in registers for h <= 32768 and re-read above); the products: the
+# K-split weight stream up to 16 rows, the column-split one up to 128 rows,
+# the tiled one above.
 # (70, 768) once overran a former single-block path's 16-row tables.
 FWD = [(70, 768, 640, 6, 6.0), (16, 8192, 256, 7, 6.0), (17, 8192, 256, 7, 6.0), (33, 1024, 256, 7, 6.0),
        (64, 2048, 256, 7, 6.0), (65, 2048, 256, 7, 6.0), (300, 640, 576, 5, 6.0),

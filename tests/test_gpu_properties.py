@@ -1,6 +1,6 @@
-"""Property-based GPU parity over small random shapes: s in [1, 80] (the
-weight-streaming products for s <= 64, the LDS-tiled one above, the few-rows
-prologue of the one-call forward up to 64 rows), h and o in 64 * [1, 8], random outlier
+"""Property-based GPU parity over small random shapes: s in [1, 160] (the
+weight-streaming products for s <= 128, the LDS-tiled one above, the
+few-rows prologue of the one-call forward up to 8 rows), h and o in 64 * [1, 8], random outlier
 columns and row fractions, an element exactly at alpha, all-zero rows.
 Every entry point is compared with the oracle (bit-exact intermediates,
 C within 2e-3 ||C_ref||_inf), and the one-call forward with the separate
@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 @st.composite
 def cases(draw):
-    s = draw(st.integers(1, 80))
+    s = draw(st.integers(1, 160))
     h = 64 * draw(st.integers(1, 8))
     o = 64 * draw(st.integers(1, 8))
     nout = draw(st.integers(0, min(8, h)))

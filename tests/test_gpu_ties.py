@@ -103,10 +103,13 @@ def test_row_quantiser_ties(s, h, label):
     assert Xq_r[1 % s, NEAR_MISS_COL] == 127     # the near miss sets its row's constant
 
 
-# (s, h): the few-row forward (detection and row quantisation by slabs of
-# 128 columns, rows in groups of 16: RG = 1, 2, 4) and one many-row forward.
-FORWARD_SHAPES = [(8, 256, "RG1"), (16, 12288, "RG1 wide"), (24, 1024, "RG2"), (48, 4096, "RG4"),
-                  (64, 12288, "RG4 wide"), (300, 2048, "detect + rows")]
+# (s, h): the few-row forward (s <= 8: detection and row quantisation by
+# slabs of 128 columns in one row group of 16) and detection + row pass
+# beside each product: the K-split (s <= 16) and column-split (s <= 128)
+# weight streams and the tiled product.
+FORWARD_SHAPES = [(8, 256, "slabs"), (8, 12288, "slabs wide"), (16, 12288, "rows K-split"),
+                  (24, 1024, "rows column-split"), (48, 4096, "rows column-split 3"),
+                  (64, 12288, "rows column-split 4 wide"), (300, 2048, "rows tiled")]
 
 
 @pytest.mark.parametrize("s,h,label", FORWARD_SHAPES, ids=[c[2] for c in FORWARD_SHAPES])

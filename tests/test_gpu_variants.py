@@ -212,7 +212,7 @@ def test_one_call_forwards_share_a_workspace():
     shapes and both prologue paths (the accumulator must come back to zero
     after each)."""
     seq = [("zeropoint", 300, 640, 320), ("vector", 8, 1024, 256), ("tensor", 40, 512, 192),
-           ("inline", 100, 1024, 256), ("zeropoint", 5, 1024, 128), ("decode", 12, 640, 192),
+           ("inline", 150, 1024, 256), ("zeropoint", 5, 1024, 128), ("decode", 12, 640, 192),
            ("vector", 260, 640, 576), ("tensor", 3, 192, 64), ("inline", 300, 192, 320),
            ("zeropoint", 17, 192, 320)]
     ws = i8.forward_workspace(300, 1024, DEV, zeropoint=True)
