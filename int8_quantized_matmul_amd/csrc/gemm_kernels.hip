@@ -22,15 +22,16 @@
 //    step 128 (two panels), both operands double buffered in LDS through
 //    direct-to-LDS buffer loads, v_mfma_i32_32x32x32_i8, 2x2 waves of
 //    128x128.
-//  * k_gemm_decode (s <= 16): weight streaming. Four wavefronts per 16*NT
+//  * k_gemm_decode (s <= 16, narrow or evenly filling layers): weight
+//    streaming. Four wavefronts per 16*NT
 //    output columns (64) split K and read their panels of Wq straight from
 //    HBM into the MFMA operand registers with non-temporal loads
 //    (v_mfma_i32_16x16x64_i8, rows beyond s read as zero), two register
 //    batches in flight.
-//  * k_gemm_skinny (17 <= s <= 128): weight streaming with the columns split
+//  * k_gemm_skinny (s <= 128 otherwise): weight streaming with the columns split
 //    between the wavefronts of a block (one block per CU where the columns
 //    allow), each over all of K with a ring of weight steps in registers,
-//    and X's codes (two to eight row groups of 16) staged once per block
+//    and X's codes (one to eight row groups of 16) staged once per block
 //    in LDS.
 // The fused epilogue converts the int32 accumulator to fp32, multiplies by
 // 1/c_x_i * 1/c_w_j (S is never materialised), then accumulates the fp16
@@ -1538,28 +1539,38 @@ hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, 
                        const int32_t* idx, const int32_t* n_out, const int8_t* Wq, const float* c_w,
                        const uint16_t* W, const uint16_t* bias, int64_t s, int64_t h, int64_t o, void* C,
                        hipStream_t stream, uint32_t* clear, int clear_words, ZpArgs zp) {
-    // Weight streaming. Up to 16 rows: the K-split kernel, 64 output columns
-    // per block (one 16-column tile per wavefront in the epilogue), batches
-    // of two K steps: 7.06 TB/s of weights on the 8 x 12288 x 49152 layer
-    // against 6.64 TB/s with 32 columns and batches of four. 17-128 rows:
-    // the column-split kernel with X in LDS (k_gemm_skinny), 2, 3, 4, 6 or 8
+    // Weight streaming. The K-split kernel: 64 output columns per block (one
+    // 16-column tile per wavefront in the epilogue), batches of two K steps:
+    // 7.06 TB/s of weights on the 8 x 12288 x 49152 layer against 6.64 TB/s
+    // with 32 columns and batches of four. Up to 128 rows otherwise: the
+    // column-split kernel with X in LDS (k_gemm_skinny), 1, 2, 3, 4, 6 or 8
     // row groups of 16; on that layer (forward) 96-103 us for 17-64 rows
     // and 107-136 us for 65-128, where the tiled product takes 155-165 us.
-    if (s <= 16) {
+    // Up to 16 rows the K-split kernel keeps narrow layers (fewer than four
+    // 16-column tiles per CU: its K split keeps more loads in flight) and
+    // layers whose 64-column blocks fill the CUs evenly three at a time;
+    // other layers take the column-split kernel, which places one block on
+    // each CU (forward, 1-16 rows, 12288-deep layers: 76.6-78.5 us against
+    // 85.2-94.3 on 36864 columns, 60.8-61.6 against 62.3-68.5 on 28672,
+    // 37.5-39.9 against 40.7-41.5 on 16384; equal on 49152).
+    const int cus = cu_count();
+    if (s <= 16 && (o / 16 < 4 * cus || (o / 64) % (3 * cus) == 0)) {
         hipLaunchKernelGGL((k_gemm_decode<MODE, 4, 2, 4>), dim3(static_cast<unsigned>(o / 64)), dim3(256), 0, stream,
                            Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, idx, n_out, W, bias, C, clear, clear_words, zp);
     } else if (s <= 128) {
         // one block per CU where the 16-column tiles allow: the fewest
         // wavefronts per block (4, 8, 12 or 16) whose blocks fit the CUs
         const int64_t tiles = o / 16;
-        const int64_t per_cu = (tiles + cu_count() - 1) / cu_count();
+        const int64_t per_cu = (tiles + cus - 1) / cus;
         const int waves = per_cu <= 4 ? 4 : per_cu <= 8 ? 8 : per_cu <= 12 ? 12 : 16;
         const dim3 grid(static_cast<unsigned>((tiles + waves - 1) / waves)), block(static_cast<unsigned>(64 * waves));
 #define I8MM_SKINNY(RG, WV)                                                                                        \
     hipLaunchKernelGGL((k_gemm_skinny<MODE, 1, RG, WV>), grid, block, 0, stream, Xq, Wq, s, h, o, c_x, c_w, X_O, ldo, \
                        idx, n_out, W, bias, C, clear, clear_words, zp)
 #define I8MM_SKINNY_RG(WV)          \
-    if (s <= 32) {                  \
+    if (s <= 16) {                  \
+        I8MM_SKINNY(1, WV);         \
+    } else if (s <= 32) {           \
         I8MM_SKINNY(2, WV);         \
     } else if (s <= 48) {           \
         I8MM_SKINNY(3, WV);         \

@@ -1,7 +1,8 @@
 """The products at each row-count boundary, against the oracle: the K-split
-weight-streaming kernel up to 16 rows, the column-split one with X's codes
-in LDS for 17-128 rows (2, 3, 4, 6 or 8 row groups of 16), the tiled
-product above 128. Checked bit for bit: the outlier set, Xq, c_x, X_O and C_i32; C
+weight-streaming kernel up to 16 rows (narrow layers, and layers its blocks
+fill evenly), the column-split one with X's codes in LDS otherwise up to
+128 rows (1, 2, 3, 4, 6 or 8 row groups of 16), the tiled product above
+128. Checked bit for bit: the outlier set, Xq, c_x, X_O and C_i32; C
 within 2e-3 ||C_ref||_inf. The one-call forward, the four-step product and
 the int32 product all dispatch on s the same way. The column-split kernel
 stages K in chunks of four 64-wide steps, two chunks per loop: the uneven
@@ -22,6 +23,10 @@ pytestmark = pytest.mark.gpu
 ROWS = [16, 17, 32, 33, 48, 49, 64, 65, 96, 97, 128, 129]
 UNEVEN = [(40, 4160, 192, 5), (24, 64, 64, 1), (64, 448, 320, 3), (17, 192, 128, 2), (56, 1216, 576, 9),
           (100, 704, 192, 4), (128, 64, 3136, 2)]
+# Few rows on wide layers that the K-split kernel would not fill evenly: the
+# forward picks the column-split kernel with one row group from the column
+# count (on 256 CUs); the test checks parity only.
+WIDE_FEW = [(1, 256, 36864, 2), (8, 320, 28672, 3), (16, 192, 16384, 1), (9, 128, 17408, 4)]
 
 
 def _check_shape(seed, s, h, o, nout):
@@ -54,6 +59,11 @@ def test_row_group_boundaries(s):
 @pytest.mark.parametrize("s,h,o,nout", UNEVEN, ids=[f"s{c[0]}h{c[1]}o{c[2]}" for c in UNEVEN])
 def test_uneven_k_and_columns(s, h, o, nout):
     _check_shape(1800 + s + h, s, h, o, nout)
+
+
+@pytest.mark.parametrize("s,h,o,nout", WIDE_FEW, ids=[f"s{c[0]}h{c[1]}o{c[2]}" for c in WIDE_FEW])
+def test_few_rows_on_wide_layers(s, h, o, nout):
+    _check_shape(1900 + s + h, s, h, o, nout)
 
 
 @pytest.mark.parametrize("s", [20, 40, 60, 90, 120])
