@@ -1112,28 +1112,26 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     }
 }
 
-// Weight streaming for 17..128 rows with the codes of X shared through LDS:
-// each of the kWaves wavefronts of a block owns 16 NT adjacent output
-// columns and streams their weights over the whole of K, kRing K steps
-// ahead in registers; the block stages X's codes (RG row groups of 16) in
-// LDS chunks of kSkinnyChunk K steps, double-buffered by direct-to-LDS
-// loads, and every wavefront reads them from there. A block thus fetches X
-// once (not once per wavefront) and needs no reduction; its wavefronts meet
-// once per chunk. The launch sizes blocks to one per CU where the columns
-// allow: a CU's texture address unit serves both the weight stream and the
-// staging of X (16 bytes per lane each), so every extra block per CU
-// re-staging X slows the weight stream. Columns are always whole 16-column
-// tiles (16 NT divides 64, which divides o); wavefronts past o stage X and
-// wait with the others but read no weights and write nothing.
-// Measured on 12288 x 49152 (forward with the slab prologue, us): 12
-// wavefronts (one block per CU)
-// 99.7 / 101.6 / 104.7 / 107.5 / 110.3 for 17 / 32 / 48 / 49 / 64 rows;
-// 4 wavefronts (three blocks per CU) 101.5 / 107.1 / 124.4 / 128.8 / 144.7;
-// the K-split kernel with row groups 102.8 / 119.1 / 139.5 and the tiled
-// product 162-163 past 48 rows; 106.6 / 116.8 / 131.4 for 65 / 96 / 128
-// rows against 155.2 / 160.0 / 164.9 for the tiled product. NT = 2, longer
-// rings or chunks, three LDS stages and X staged through registers
-// measured the same or slower.
+// Weight streaming for up to 128 rows with the codes of X shared through
+// LDS (the forward routes 17..128 rows here, and 1..16 rows on layers that
+// the K-split kernel cannot spread evenly over the CUs): each of the kWaves
+// wavefronts of a block owns 16 NT adjacent output columns and streams
+// their weights over the whole of K, kRing K steps ahead in registers; the
+// block stages X's codes (RG row groups of 16) in LDS chunks of
+// kSkinnyChunk K steps, double-buffered by direct-to-LDS loads, and every
+// wavefront reads them from there. A block thus fetches X once (not once
+// per wavefront) and needs no reduction; its wavefronts meet once per
+// chunk. The launch sizes blocks to one per CU where the columns allow: a
+// CU's texture address unit serves both the weight stream and the staging
+// of X (16 bytes per lane each), so every extra block per CU re-staging X
+// slows the weight stream. Columns are always whole 16-column tiles (16 NT
+// divides 64, which divides o); wavefronts past o stage X and wait with the
+// others but read no weights and write nothing.
+// Measured on 12288 x 49152 (forward, us): 96.4 / 97.1 / 99.0 / 103.2 /
+// 106.9 / 117.5 / 135.9 for 17 / 32 / 48 / 64 / 65 / 96 / 128 rows, where
+// the tiled product takes 155-165; with three 4-wavefront blocks per CU
+// instead of one, 64 rows took 144.7. NT = 2, longer rings or chunks, three
+// LDS stages and X staged through registers measured the same or slower.
 constexpr int kSkinnyChunk = 4;
 
 template <GemmOut MODE, int NT, int RG, int kWaves>
@@ -1147,6 +1145,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_gemm_skinny(const int8_t* __res
                                                      const uint16_t* __restrict__ bias, void* __restrict__ Cout,
                                                      uint32_t* __restrict__ clear, int clear_words, ZpArgs zp) {
     constexpr int kRing = 2 * kSkinnyChunk;   // weight steps in flight
+    static_assert(kSkinnyChunk * NT < 16, "the wait below encodes the count in 4 bits");
     // xs[buffer][step of the chunk][row group]: one 16 x 64 operand, lane-ordered
     __shared__ v4i xs[2][kSkinnyChunk][RG][64];
     if (blockIdx.x == 0)
