@@ -343,8 +343,9 @@ size_t i8mm_forward_workspace_bytes(int64_t s, int64_t h);
 /*
  * The whole per-forward path for one linear layer ([DIGEST] "The Full
  * LLM.int8() Algorithm", Steps 1-5): detect, quantise rows and gather,
- * decomposed product, in three kernel launches. Weights must already
- * be converted by i8mm_quantize_colwise_weights.
+ * decomposed product, in three kernel launches (two when s <= 8 and X
+ * holds at most 24 KiB: detection and quantisation then share one).
+ * Weights must already be converted by i8mm_quantize_colwise_weights.
  *
  * workspace: caller-owned device buffer of i8mm_forward_workspace_bytes(s, h)
  * bytes, 256-byte aligned. Its first I8MM_FORWARD_ACC_BYTES bytes (the

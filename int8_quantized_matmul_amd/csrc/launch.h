@@ -20,9 +20,11 @@ hipError_t launch_quantize_rows(const uint16_t* X, int64_t s, int64_t h,
                                 int8_t* Xq, float* c_x, uint16_t* X_O, int64_t ldo,
                                 hipStream_t stream);
 
-// Forward path: detection + index list + row quantisation in two launches.
-// Cross-block state (the mask accumulator, or the row maxima for inputs of
-// at most 8 rows) goes to `acc`, which must be zero on entry;
+// Forward path: detection + index list + row quantisation in two launches,
+// or in one for at most 8 rows and at most 24 KiB of X (no cross-block
+// state; *clear_words is then 0). Cross-block state (the mask accumulator,
+// or the row maxima for other inputs of at most 8 rows) goes to `acc`,
+// which must be zero on entry;
 // *clear_words is how many of its words the product launch must clear
 // again (see launch_int8_gemm). For s > 8, Xq may be null: the codes are
 // then not written (launch_int8_gemm_inline_quant makes them).

@@ -253,8 +253,9 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Forward path for few rows (the one-call forward takes it for s <= 8, the
-// kernels hold up to 16 RG rows): blocks of 256 threads on 128-column
+// Forward path for few rows (the one-call forward takes it for s <= 8 when
+// X is larger than kOneLaunchBytes, the kernels hold up to 16 RG rows):
+// blocks of 256 threads on 128-column
 // slabs, thread t on the 8-column chunk t % 16 of rows t / 16 + 16 g,
 // g < RG. A block of k_small_detect sees every row of its
 // slab, so it writes the slab's mask words itself and folds the per-row
@@ -267,6 +268,14 @@ constexpr int kSlabCols = 128;
 // on 12288 columns (~94 us per decode forward); from 16 rows on, detection
 // + row pass is 2.6-7.4 us faster per forward (16-64 rows).
 constexpr int kSmallRowsMax = 8;
+// Up to 8 rows and this many bytes of X, the one-launch prologue
+// (k_small_prologue) replaces the slab pair. Measured per forward: 1-8 rows
+// on 256 x 512, 10.4-12.4 us against 13.1-14.1; 1-2 rows on 4096 x 16384,
+// 17.0-17.2 against 18.0-18.1; one row on 12288 x 49152, 93.2 against 95.5.
+// With more of X each block's scan costs more than the second launch (8
+// rows on 12288 x 49152: 95.2 against 94.7), and from 9 rows on it lost on
+// every width measured (256-12288 columns).
+constexpr int64_t kOneLaunchBytes = 24576;
 
 template <int RG>
 __global__ __launch_bounds__(256) void k_small_detect(const uint16_t* __restrict__ X, int s, int h, Threshold th,
@@ -399,6 +408,152 @@ __global__ __launch_bounds__(256) void k_small_quant(const uint16_t* __restrict_
         if (t == 0) n_out[0] = total;
         const int pad = ((total + 31) & ~31) - total;
         for (int e = t; e < s * pad; e += 256) X_O[(e / pad) * ldo + total + e % pad] = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward prologue for few rows and small X in one launch: outlier columns,
+// row-wise absmax scales over the other columns, codes and the outlier
+// gather ([DIGEST] "The Full LLM.int8() Algorithm", Steps 1, 2 and 4; [TM]
+// "Absmax INT8 quantization from first principles"). Every block of
+// 1024 threads scans all of X (at most R rows): a thread takes 8-column
+// chunks with all their rows, so it knows a chunk's outlier flags at once
+// and folds the rows' maxima over the non-outlier columns in the same pass.
+// The block thus holds the whole mask and the finished row maxima without
+// waiting for any other block, and quantises the rows of its own 128-column
+// slab as k_small_quant does. Blocks start their scans at staggered chunks,
+// so that the blocks sharing an L2 fetch different lines of X first. Max
+// and OR do not depend on the order, so the results equal the two-launch
+// pair's bit for bit. Each block reads all of X, so this pays only while X
+// is small (see kOneLaunchBytes).
+template <int R>
+__global__ __launch_bounds__(1024) void k_small_prologue(const uint16_t* __restrict__ X, int s, int h, Threshold th,
+                                                         uint32_t* __restrict__ mask, int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ n_out, int8_t* __restrict__ Xq,
+                                                         float* __restrict__ c_x, uint16_t* __restrict__ X_O,
+                                                         int64_t ldo) {
+    constexpr int kSlabChunks = kSlabCols / 8;   // 8-column chunks per slab row
+    static_assert(R >= 1 && R <= 16 && 16 * kSlabChunks <= 1024, "launch shape");
+    extern __shared__ uint32_t smask[];   // h / 32 words
+    __shared__ uint32_t pmax[16][R];
+    __shared__ int part[2][16];
+    __shared__ float rscale[R];
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    const int nw = h / 32, nch = h / 8;
+    const __amdgpu_buffer_rsrc_t rX = range_rsrc(X, static_cast<uint32_t>(2 * static_cast<int64_t>(s) * h));
+
+    // This block's slab first, so that its loads are in flight during the scan.
+    const int sc = t % kSlabChunks, sr = t / kSlabChunks;
+    const int scol = static_cast<int>(blockIdx.x) * kSlabChunks * 8 + sc * 8;
+    const bool sok = t < 16 * kSlabChunks && sr < s && scol < h;
+    const uint4 sv = load_chunk_rsrc(rX, sok ? static_cast<uint32_t>(2 * (sr * h + scol)) : 0x80000000u);
+
+    // The scan. Four aligned lanes hold the four chunks of one mask word
+    // (the start is a multiple of 4 chunks, and so is h / 8).
+    const int start = static_cast<int>((static_cast<int64_t>(blockIdx.x) * (nch / 4)) / gridDim.x) * 4;
+    uint32_t m2[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) m2[r] = 0u;
+    for (int base = 0; base < nch; base += 1024) {
+        const bool ok = base + t < nch;
+        int c = start + base + t;
+        if (c >= nch) c -= nch;
+        uint4 v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            v[r] = load_chunk_rsrc(rX, ok ? static_cast<uint32_t>(2 * (r * h + c * 8)) : 0x80000000u);
+        uint4 d = detect_init();
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r < s) detect_fold(d, v[r], th.thr2);
+        const uint32_t flags = ok ? detect_flags(d, th.span) : 0u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) m2[r] = chunk_absmax_fold(chunk_clear(v[r], flags), m2[r]);
+        uint32_t word = flags << ((c & 3) * 8);
+        word |= __shfl_xor(word, 1, kWave);
+        word |= __shfl_xor(word, 2, kWave);
+        if (ok && (lane & 3) == 0) smask[c >> 2] = word;
+    }
+    // The rows' reductions are independent: each level's shuffles issue
+    // together (one LDS round trip per level, not one per row and level).
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        uint32_t o2[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) o2[r] = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m2[r]), off, kWave));
+#pragma unroll
+        for (int r = 0; r < R; ++r) m2[r] = pk_max_u16(m2[r], o2[r]);
+    }
+    if (lane == 0)
+#pragma unroll
+        for (int r = 0; r < R; ++r) pmax[wid][r] = m2[r];
+    __syncthreads();
+
+    // Outlier columns before this slab and in total; row scales.
+    const int w0 = static_cast<int>(blockIdx.x) * (kSlabChunks / 4);
+    int before = 0, total = 0;
+    for (int w = t; w < nw; w += 1024) {
+        const int p = __popc(smask[w]);
+        total += p;
+        before += w < w0 ? p : 0;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        before += __shfl_xor(before, off, kWave);
+        total += __shfl_xor(total, off, kWave);
+    }
+    if (lane == 0) {
+        part[0][wid] = before;
+        part[1][wid] = total;
+    }
+    if (t < R) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) m = pk_max_u16(m, pmax[w][t]);
+        rscale[t] = absmax_scale(absmax_value(m));
+    }
+    __syncthreads();
+    before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        before += part[0][w];
+        total += part[1][w];
+    }
+
+    // Rank of the chunk's first outlier column: the slab's words below it,
+    // then the bits below it in its own word.
+    const int q = sc >> 2;
+    int rank = before;
+    uint32_t word = 0u;
+    for (int j = 0; j <= q; ++j) {
+        word = w0 + j < nw ? smask[w0 + j] : 0u;
+        if (j < q) rank += __popc(word);
+    }
+    rank += __popc(word & ((1u << ((sc & 3) * 8)) - 1u));
+    const uint32_t bits = (word >> ((sc & 3) * 8)) & 0xffu;
+    if (sok) {
+        if (bits) {
+            int k = rank;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if ((bits >> e) & 1u) X_O[sr * ldo + k++] = static_cast<uint16_t>(word_of(sv, e >> 1) >> ((e & 1) * 16));
+        }
+        *reinterpret_cast<uint2*>(Xq + static_cast<int64_t>(sr) * h + scol) =
+            chunk_quantize(chunk_clear(sv, bits), rscale[sr]);
+    }
+    if (t < 16 * kSlabChunks && sr == 0 && scol < h && bits) {
+        int k = rank;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((bits >> e) & 1u) idx[k++] = scol + e;
+    }
+    if (t < kSlabChunks / 4 && w0 + t < nw) mask[w0 + t] = smask[w0 + t];
+    if (blockIdx.x == 0) {
+        if (t < s) c_x[t] = rscale[t];
+        if (t == 0) n_out[0] = total;
+        const int pad = ((total + 31) & ~31) - total;
+        for (int e = t; e < s * pad; e += 1024) X_O[(e / pad) * ldo + total + e % pad] = 0;
     }
 }
 
@@ -661,6 +816,27 @@ hipError_t launch_quantize_rows(const uint16_t* X, int64_t s, int64_t h,
 hipError_t launch_forward_prologue(const uint16_t* X, int64_t s, int64_t h, float alpha, uint32_t* acc,
                                    uint32_t* mask, int32_t* idx, int32_t* n_out, int8_t* Xq, float* c_x,
                                    uint16_t* X_O, int64_t ldo, hipStream_t stream, int* clear_words) {
+    if (s <= kSmallRowsMax && 2 * s * h <= kOneLaunchBytes) {
+        // no accumulator: every block finds the mask and the row maxima itself
+        *clear_words = 0;
+        const dim3 grid(static_cast<unsigned>((h + kSlabCols - 1) / kSlabCols)), block(1024);
+        const size_t lds = static_cast<size_t>(h / 32) * sizeof(uint32_t);
+        const int si = static_cast<int>(s), hi = static_cast<int>(h);
+        const Threshold th = make_threshold(alpha);
+#define I8MM_ONE(R)                                                                                          \
+    hipLaunchKernelGGL(k_small_prologue<R>, grid, block, lds, stream, X, si, hi, th, mask, idx, n_out, Xq, c_x, \
+                       X_O, ldo)
+        if (s <= 1)
+            I8MM_ONE(1);
+        else if (s <= 2)
+            I8MM_ONE(2);
+        else if (s <= 4)
+            I8MM_ONE(4);
+        else
+            I8MM_ONE(8);
+#undef I8MM_ONE
+        return hipGetLastError();
+    }
     if (s <= kSmallRowsMax) {
         // acc[0 .. s) holds the row maxima.
         *clear_words = static_cast<int>(s);

@@ -103,11 +103,11 @@ def test_row_quantiser_ties(s, h, label):
     assert Xq_r[1 % s, NEAR_MISS_COL] == 127     # the near miss sets its row's constant
 
 
-# (s, h): the few-row forward (s <= 8: detection and row quantisation by
-# slabs of 128 columns in one row group of 16) and detection + row pass
-# beside each product: the K-split (s <= 16) and column-split (s <= 128)
-# weight streams and the tiled product.
-FORWARD_SHAPES = [(8, 256, "slabs"), (8, 12288, "slabs wide"), (16, 12288, "rows K-split"),
+# (s, h): the few-row forward (s <= 8: in one launch up to 24 KiB of X,
+# else detection and row quantisation by slabs of 128 columns in one row
+# group of 16) and detection + row pass beside each product: the K-split
+# (s <= 16) and column-split (s <= 128) weight streams and the tiled product.
+FORWARD_SHAPES = [(8, 256, "one launch"), (8, 2048, "slabs"), (8, 12288, "slabs wide"), (16, 12288, "rows K-split"),
                   (24, 1024, "rows column-split"), (48, 4096, "rows column-split 3"),
                   (64, 12288, "rows column-split 4 wide"), (300, 2048, "rows tiled")]
 
@@ -203,14 +203,13 @@ def test_weight_conversion_ties(h, o):
     assert np.array_equal(H(cs_w), Wz_r.astype(np.int64).sum(axis=1)), "colsum_w differs"
 
 
-@pytest.mark.parametrize("s,path", [(4, "detect"), (100, "detect"), (8, "forward, few rows"),
-                                    (100, "forward, many rows")])
-def test_detection_with_nan(s, path):
+@pytest.mark.parametrize("s,h,path", [(4, 256, "detect"), (100, 256, "detect"), (8, 256, "forward, one launch"),
+                                      (8, 2048, "forward, slab pair"), (100, 256, "forward, many rows")])
+def test_detection_with_nan(s, h, path):
     """A column is in O when one of its elements reaches alpha ([DIGEST] "The
     Full LLM.int8() Algorithm", Step 1), also when it holds a NaN as well;
     a NaN alone does not reach alpha. Only the outlier set is defined for
     such inputs, so only the mask, the index list and |O| are compared."""
-    h = 256
     X = tie_matrix(s, h, outliers=False, near_miss=False)
     X[0, 3] = np.nan
     X[s - 1, 3] = 10.0                 # NaN and an outlier: in O

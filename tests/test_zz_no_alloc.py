@@ -31,8 +31,9 @@ def _noalloc(lib, Xd, Wq, c_w, Wd, alpha, C):
 
 
 @pytest.mark.parametrize("shapes", [[(2048, 4096, 1024, 6), (300, 1024, 512, 5)],
-                                    [(64, 8192, 768, 7), (8, 2048, 256, 3)]],
-                         ids=["prefill then smaller", "few rows then decode"])
+                                    [(64, 8192, 768, 7), (8, 2048, 256, 3)],
+                                    [(8, 1024, 256, 3), (2, 512, 128, 2)]],
+                         ids=["prefill then smaller", "few rows then decode", "one-launch prologue twice"])
 def test_noalloc_matches_workspace_forward(shapes):
     lib = _native.load()
     for k, (s, h, o, nout) in enumerate(shapes):
@@ -67,13 +68,14 @@ def test_noalloc_rejects_shapes_beyond_the_scratch():
 
 
 def test_noalloc_graph_replays():
-    """The use the entry point exists for: two allocation-free forwards (a
-    prefill and a decode shape) captured in one HIP graph (torch's CUDA-graph
+    """The use the entry point exists for: three allocation-free forwards (a
+    prefill shape and two decode shapes, one per few-row prologue route)
+    captured in one HIP graph (torch's CUDA-graph
     API over the library's stream-ordered launches) and replayed four times.
     Between replays, eager work runs: a fill of the outputs, and an eager
     allocation-free forward on other inputs that rewrites the shared scratch.
     Every replay must reproduce the workspace forward's C bit for bit."""
-    cases = [(300, 1024, 512, 5), (8, 2048, 256, 3)]
+    cases = [(300, 1024, 512, 5), (8, 2048, 256, 3), (4, 1024, 256, 3)]
     data = []
     for k, (s, h, o, nout) in enumerate(cases):
         inp = random_case(760 + k, s, h, o, nout, row_frac=0.5)
@@ -97,7 +99,7 @@ def test_noalloc_graph_replays():
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
-    say("  capture: two forward_noalloc calls")
+    say("  capture: three forward_noalloc calls")
     with torch.cuda.graph(g):
         for Xd, Wd, Wq, c_w, _, C in data:
             i8.forward_noalloc(Xd, Wq, c_w, Wd, 6.0, C=C)
