@@ -330,7 +330,8 @@ i8mm_status i8mm_zeropoint_matmul(const int8_t* Xq, const float* nd_x, const int
 
 /* Bytes at the start of the forward workspace that hold the cross-block
  * accumulator of the detection (the outlier mask being ORed together, or,
- * for inputs of at most 8 rows, the per-row maxima). */
+ * for inputs of at most 8 rows and more than 24 KiB, the per-row maxima;
+ * smaller inputs of at most 8 rows leave it untouched). */
 #define I8MM_FORWARD_ACC_BYTES 16640
 
 /*
