@@ -17,7 +17,7 @@ expansion decode layer (X [8, 12288], W [12288, 49152]) against 8 TB/s HBM;
 prefill and the nine outlier-density sweep points), each with its own CPU
 oracle baseline; `cpu_baseline` times the CPU oracle on host cores on a
 bounded sample of the headline layer; `clocks` are the GPU clocks and socket
-power read from the driver's metrics table over a clock window of the same
+power read from the GPU's metrics table (amdsmi) over a clock window of the same
 step (the table is refreshed every few hundred ms).
 """
 
@@ -552,7 +552,7 @@ def cpu_baseline(w, inputs, budget_s, host, rows=None, reps=3):
 
 class ClockSampler:
     """Samples the GPU's graphics clock (per XCD), memory clock and socket
-    power from the driver's metrics table (amdsmi) in a background thread.
+    power from the GPU's metrics table (amdsmi) in a background thread.
     The table is refreshed by the power-management firmware only every few
     hundred ms, so the sampler is run over a clock window of >= 1 s of the
     same step back to back, and the distinct snapshots are reported.
@@ -580,7 +580,7 @@ class ClockSampler:
             self._amdsmi = amdsmi
             if self.handle is None:
                 self.error = "no GPU handle"
-        except Exception as e:  # amdsmi missing or the driver's table unreadable
+        except Exception as e:  # amdsmi missing or the metrics table unreadable
             self.error = repr(e)
 
     def read(self):
