@@ -100,8 +100,9 @@ constexpr uint32_t kOutOfRangeW = 0xfffff000u;
 // panels streamed through its 4 MiB L2 per round (an order with rows
 // fastest made each round re-fetch every row panel of Xq). Over the whole
 // product the weights are fetched (row tiles / (32 / group)) times and Xq
-// (weight tiles / group) times, so the launch takes a smaller group (5)
-// when the int8 weights exceed the 256 MiB Infinity Cache and 8 otherwise.
+// (weight tiles / group) times, so the launch takes group 4 when the int8
+// weights exceed the 256 MiB Infinity Cache (fewer passes over them) and 8
+// otherwise.
 // Block and tile indices are 32-bit (as the grid is), which keeps the index
 // arithmetic short ahead of the first loads.
 __device__ __forceinline__ void grouped_tile(uint32_t b, uint32_t nb, uint32_t n_ts, uint32_t n_to, uint32_t group,
@@ -1540,16 +1541,14 @@ __global__ __launch_bounds__(256) void k_outlier_only(const uint16_t* __restrict
     if (srow < s) *reinterpret_cast<v4f*>(C_O + srow * o + ocol) = f;
 }
 
-// Weight tiles per group of the grouped tile order (grouped_tile): 5 when
+// Weight tiles per group of the grouped tile order (grouped_tile): 4 when
 // the weight operand (hb reduction bytes per column) exceeds the Infinity
-// Cache, else 8. Interleaved A/B of the product kernel on three GPUs,
-// groups 3 / 4 / 5 / 8 in us: 4096 x 12288 x 36864 (453 MB of weights)
-// 1486-1498 / 1498-1510 / 1481-1497 / 1546-1568; 4096 x 8192 x 28672
-// (235 MB) 780-785 / 793-795 / 777 / 774-778; 2048 x 4096 x 16384 flat
-// within 1 %. FETCH_SIZE on the first layer grows with the group count's
-// distance from a rectangle of the ~32 tiles an XCD runs at once: 2.74 GB
-// per launch with 4, 3.13 GB with 5, 3.73 GB with 3; most of the growth is
-// Xq (50 MB), re-read from the Infinity Cache.
+// Cache, else 8. Interleaved A/B of the product kernel, groups 4 / 5 / 8
+// in us: 4096 x 12288 x 36864 (453 MB of weights) 1464-1468 / 1468-1471 /
+// 1500-1506; 4096 x 8192 x 28672 (235 MB) 778-785 / 777-778 / 770-773;
+// 2048 x 4096 x 16384 flat within 1 %. (Before the weights-first load
+// order, 5 was 0.8-1.3 % faster than 4 on the first layer; now they tie,
+// and 4 fetches less: the weights twice and Xq 36 times per launch.)
 // Compute units of the current device (read once per device).
 int cu_count() {
     static std::atomic<int> cached[64];
@@ -1569,7 +1568,7 @@ int cu_count() {
 }
 
 constexpr int64_t kMallBytes = int64_t(256) << 20;
-uint32_t tile_group(int64_t hb, int64_t o) { return hb * o > kMallBytes ? 5u : 8u; }
+uint32_t tile_group(int64_t hb, int64_t o) { return hb * o > kMallBytes ? 4u : 8u; }
 
 template <GemmOut MODE>
 hipError_t launch_mode(const int8_t* Xq, const float* c_x, const uint16_t* X_O, int64_t ldo,
