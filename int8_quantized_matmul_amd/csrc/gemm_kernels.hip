@@ -570,6 +570,19 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
             if (i & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
         }
     };
+    // The sub-step after the barrier, which carries the eight weight loads:
+    // each one a MFMA earlier (after MFMAs 0, 2, .., 14), the first right
+    // behind the first MFMA. Interleaved A/B on two GPUs: -0.6 to -0.8 %
+    // product time on all three prefill layers; the same shift in every
+    // sub-step was slower on 4096 x 12288 x 36864.
+    auto sched_sub_first = [&]() {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+            if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+            if (!(i & 1)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+    };
     // Stage kt from (Ac, Bc); stage kt + 1 sits in (An, Bn), of which the
     // activation loads are still to go out (its weight loads left with the
     // previous stage's last sub-step). Software pipeline across the
@@ -602,7 +615,7 @@ void k_gemm_prefill(const int8_t* __restrict__ Xq, const int8_t* __restrict__ Wq
         frags(An, Bn, 0, fa[0], fb[0]);
         load_a(kt + 2, Ac, 0, 8);
         mma(fa[1], fb[1]);
-        sched_sub();
+        sched_sub_first();
     };
     // QX: the same stage, with the fp16 rows of stage kt + 1 loaded in
     // sub-steps 0 and 1 and quantised into Bn in sub-steps 2 and 3 (Bn was
